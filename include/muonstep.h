@@ -1,0 +1,133 @@
+/*
+ * muonstep.h -- C ABI of the MI355X (gfx950) Muon optimizer step and weight EMA.
+ *
+ * What is computed (pages cited by title and section):
+ *   - "Record: L_ParallelResiduals_UNetSkips_DepthRecur_Muon_ 1.0901" (PR #1893),
+ *     "Architecture and training stack": Muon on the matrix parameters with
+ *     momentum 0.99 and matrix LR 0.022; weight EMA with decay 0.9965.
+ *   - "Record: Combined 3-Layer Recurrence + Parallel Residuals + Polar Express +
+ *     Brotli" (PR #1396), "Techniques Combined": MuonEq-R row normalisation before
+ *     the Newton-Schulz iteration, a per-step NS coefficient schedule, WD 0.105.
+ *   - "Record: Improved Parallel Residuals + Systems Optimization" (PR #1584),
+ *     "Summary": one fused Muon step and one batched EMA over all parameters,
+ *     with the optimizer's arithmetic unchanged.
+ *
+ * The pages do not print the equations; the library implements the plain
+ * reading of Muon, per matrix W (rows x cols, row-major, PyTorch out x in):
+ *   M' = mu*M + G;  U = G + mu*M' (nesterov) or U = M' (otherwise)
+ *   U_i <- U_i / (||U_i||_2 + 1e-7) for every stored row i     (if row_norm)
+ *   X0 = U / (||U||_F + 1e-7);  X0 <- X0^T if rows > cols
+ *   for k < ns_steps, (a,b,c) = coeffs[k]:  A = X X^T;  X <- a X + (b A + c A A) X
+ *   O = X (transposed back);  s = sqrt(max(1, rows/cols))
+ *   W' = (1 - lr*wd) W - lr*s*O
+ * and the EMA  E' = d*E + (1 - d)*P  over any list of fp32 tensors.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers to contiguous fp32 data on the
+ *     current HIP device.  The library never allocates, frees or synchronises
+ *     on these calls; all work is enqueued on `stream` (a hipStream_t; NULL is
+ *     the null stream) and runs asynchronously.  Faults inside kernels surface
+ *     at the caller's next synchronisation.
+ *   - Host arrays (the tensor list, the coefficient table, the EMA lists) are
+ *     read during the call only; the caller keeps ownership.
+ *   - Every argument is validated on the host before anything is enqueued, so a
+ *     call that returns an error has no side effect and needs no GPU.
+ *   - Return value 0 on success, otherwise one of the MUON_ERR_* codes; the
+ *     message of the last error on the calling thread is muon_last_error().
+ *   - Results are deterministic: fixed reduction orders, no atomics.
+ *   - Calls that share a workspace must not overlap in time.
+ */
+#ifndef MUONSTEP_H
+#define MUONSTEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MUON_OK 0
+#define MUON_ERR_INVALID_ARG (-1)   /* null pointer, bad size, non-finite scalar */
+#define MUON_ERR_UNSUPPORTED (-2)   /* shape beyond the limits, aliasing buffers */
+#define MUON_ERR_WORKSPACE (-3)     /* workspace missing or smaller than required */
+#define MUON_ERR_HIP (-4)           /* a HIP runtime call or kernel launch failed */
+
+#define MUON_MAX_NS_STEPS 16        /* rows of the coefficient table, at most */
+#define MUON_MAX_SHORT_SIDE 8192    /* min(rows, cols) of a Muon matrix, at most */
+#define MUON_MAX_LONG_SIDE 65536    /* max(rows, cols) of a Muon matrix, at most */
+#define MUON_MAX_TENSORS 4096       /* tensors per call, at most */
+
+#define MUON_NS_BF16 0              /* NS products on bf16 MFMA, fp32 accumulation */
+#define MUON_NS_FP32 1              /* NS products on fp32 MFMA */
+
+/* One Muon matrix.  param and momentum are updated in place; grad is read only.
+ * update_out is optional (NULL to skip): when set, the orthogonalised update O
+ * (rows x cols, fp32, before the lr and shape scaling) is written there.  The
+ * four buffers must not overlap. */
+typedef struct muon_tensor_t {
+    float* param;
+    const float* grad;
+    float* momentum;
+    float* update_out;
+    int32_t rows;
+    int32_t cols;
+} muon_tensor_t;
+
+/* Bytes of device workspace muon_step needs for this list of matrices and this
+ * NS precision.  Depends only on the shapes.  Returns 0 if the arguments are
+ * invalid (see muon_last_error()). */
+size_t muon_workspace_size(const muon_tensor_t* tensors, int32_t n, int32_t ns_precision);
+
+/* One Muon step on n matrices (the equations above).
+ *   tensors       host array of n descriptors, 1 <= n <= MUON_MAX_TENSORS; the
+ *                 library groups them by shape itself.
+ *   lr, momentum, weight_decay   finite scalars (momentum is mu).
+ *   nesterov, row_norm           0 or 1.
+ *   ns_steps      0 <= ns_steps <= MUON_MAX_NS_STEPS; 0 gives O = X0.
+ *   ns_coeffs     host array of ns_steps rows (a_k, b_k, c_k), row-major,
+ *                 finite; may be NULL only when ns_steps == 0.
+ *   ns_precision  MUON_NS_BF16 or MUON_NS_FP32.
+ *   workspace     device buffer of at least muon_workspace_size(...) bytes,
+ *                 256-byte aligned; its contents on entry do not matter.
+ *   stream        hipStream_t to enqueue on.
+ * NaN or Inf inside the tensors is not checked and propagates. */
+int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
+              int32_t nesterov, float weight_decay, int32_t row_norm, int32_t ns_steps,
+              const float* ns_coeffs, int32_t ns_precision, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/* Weight EMA over n fp32 tensors: ema[i][j] = decay*ema[i][j] + (1-decay)*params[i][j]
+ * for j < numel[i].
+ *   ema, params   host arrays of n device pointers; ema[i] is updated in place,
+ *                 params[i] is read only and must not overlap any ema[j].
+ *   numel         host array of n element counts, each >= 0 (0 is skipped).
+ *   decay         finite, 0 <= decay <= 1.
+ *   1 <= n <= MUON_MAX_TENSORS. */
+int ema_update(float* const* ema, const float* const* params, const int64_t* numel, int32_t n,
+               float decay, void* stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* muon_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int muon_version(void);
+
+/* Kernel timing hook for measurement tools.  When enabled (non-zero), every
+ * kernel the library launches is bracketed by HIP events on its stream and its
+ * duration is added to a per-kernel-name total once the caller calls
+ * muon_profile_read (which synchronises on the recorded events).  Disabled by
+ * default; enabling adds two event records per launch. */
+int muon_profile_enable(int32_t enable);
+
+/* Copy the per-kernel totals since the last reset into host arrays of length
+ * cap: names (each at most 47 characters plus NUL, 48 bytes per entry),
+ * launch counts and summed milliseconds.  Returns the number of kernels (which
+ * may exceed cap), or a negative MUON_ERR_* code.  reset != 0 clears the totals. */
+int muon_profile_read(char* names, int64_t* counts, double* total_ms, int32_t cap, int32_t reset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUONSTEP_H */

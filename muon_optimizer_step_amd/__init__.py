@@ -1,0 +1,14 @@
+"""MI355X (gfx950) Muon optimizer step and weight EMA.
+
+Thin Python binding over the C ABI of libmuonstep.so (include/muonstep.h):
+it only turns torch tensors into device pointers plus the current HIP stream.
+Every step of the computation runs in the library's HIP kernels.
+"""
+
+from ._lib import (  # noqa: F401
+    MUON_NS_BF16, MUON_NS_FP32, MuonError, LIB_PATH, load,
+)
+from .api import (  # noqa: F401
+    muon_step, ema_update, workspace_size, profile_enable, profile_read, version,
+    PreparedMuonStep, PreparedEma,
+)

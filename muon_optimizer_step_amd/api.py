@@ -1,0 +1,216 @@
+"""torch-facing binding: argument marshalling onto the C ABI, nothing else."""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, Optional, Sequence, Tuple
+
+from . import _lib
+
+_workspaces: Dict[Tuple[int, int], "object"] = {}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check_tensor(t, name: str, ndim: Optional[int] = None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
+
+
+def _stream_handle(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def workspace_size(shapes: Sequence[Tuple[int, int]], ns_precision: int = _lib.MUON_NS_BF16) -> int:
+    """Bytes of workspace muon_step needs for these (rows, cols) shapes."""
+    table = _lib.tensor_table((0, 0, 0, 0, int(r), int(c)) for r, c in shapes)
+    n = _lib.load().muon_workspace_size(table, len(shapes), int(ns_precision))
+    if n == 0:
+        raise _lib.MuonError(_lib.MUON_ERR_INVALID_ARG, _lib.load().muon_last_error().decode())
+    return int(n)
+
+
+def _workspace_for(nbytes: int, device):
+    torch = _torch()
+    key = (device.index if device.index is not None else torch.cuda.current_device(), nbytes)
+    ws = _workspaces.get(key)
+    if ws is None:
+        _workspaces.clear()
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def muon_step(params, grads, moms, *, lr: float, momentum: float, weight_decay: float,
+              coeffs, nesterov: bool = True, row_norm: bool = True,
+              ns_precision: int = _lib.MUON_NS_BF16, update_outs=None, workspace=None, stream=None) -> None:
+    """One Muon step over lists of 2-D fp32 tensors (params and moms updated in place).
+
+    coeffs: ns_steps rows of (a, b, c); update_outs: optional list of tensors
+    (or None entries) that receive the orthogonalised update O.
+    """
+    lib = _lib.load()
+    n = len(params)
+    if len(grads) != n or len(moms) != n:
+        raise ValueError("params, grads and moms must have the same length")
+    outs = update_outs if update_outs is not None else [None] * n
+    entries = []
+    for i, (p, g, m, o) in enumerate(zip(params, grads, moms, outs)):
+        _check_tensor(p, f"params[{i}]", 2)
+        _check_tensor(g, f"grads[{i}]", 2)
+        _check_tensor(m, f"moms[{i}]", 2)
+        if g.shape != p.shape or m.shape != p.shape:
+            raise ValueError(f"tensor {i}: shapes differ {tuple(p.shape)} {tuple(g.shape)} {tuple(m.shape)}")
+        if o is not None:
+            _check_tensor(o, f"update_outs[{i}]", 2)
+            if o.shape != p.shape:
+                raise ValueError(f"update_outs[{i}] shape {tuple(o.shape)} != {tuple(p.shape)}")
+        entries.append((p.data_ptr(), g.data_ptr(), m.data_ptr(), o.data_ptr() if o is not None else 0,
+                        p.shape[0], p.shape[1]))
+    table = _lib.tensor_table(entries)
+    carr, steps = _lib.coeff_array(coeffs)
+    device = params[0].device if n else None
+    if workspace is None:
+        need = lib.muon_workspace_size(table, n, int(ns_precision))
+        if need == 0:
+            raise _lib.MuonError(_lib.MUON_ERR_INVALID_ARG, lib.muon_last_error().decode())
+        workspace = _workspace_for(int(need), device)
+    rc = lib.muon_step(table, n, float(lr), float(momentum), int(bool(nesterov)), float(weight_decay),
+                       int(bool(row_norm)), steps, carr if steps else None, int(ns_precision),
+                       ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+                       _stream_handle(stream, device))
+    _lib.check(rc)
+
+
+def ema_update(emas, params, decay: float, stream=None) -> None:
+    """emas[i] = decay * emas[i] + (1 - decay) * params[i] for fp32 tensors of any shape."""
+    lib = _lib.load()
+    n = len(emas)
+    if len(params) != n:
+        raise ValueError("emas and params must have the same length")
+    e_ptrs = (ctypes.c_void_p * max(1, n))()
+    p_ptrs = (ctypes.c_void_p * max(1, n))()
+    numel = (ctypes.c_int64 * max(1, n))()
+    for i, (e, p) in enumerate(zip(emas, params)):
+        _check_tensor(e, f"emas[{i}]")
+        _check_tensor(p, f"params[{i}]")
+        if e.numel() != p.numel():
+            raise ValueError(f"tensor {i}: {e.numel()} != {p.numel()} elements")
+        e_ptrs[i] = e.data_ptr()
+        p_ptrs[i] = p.data_ptr()
+        numel[i] = e.numel()
+    device = emas[0].device if n else None
+    rc = lib.ema_update(e_ptrs, p_ptrs, numel, n, float(decay), _stream_handle(stream, device))
+    _lib.check(rc)
+
+
+def profile_enable(enable: bool = True) -> None:
+    _lib.check(_lib.load().muon_profile_enable(int(bool(enable))))
+
+
+def profile_read(reset: bool = True) -> Dict[str, Tuple[int, float]]:
+    """{kernel name: (launches, total ms)} since the last reset (synchronises on the events)."""
+    lib = _lib.load()
+    cap = 64
+    names = ctypes.create_string_buffer(48 * cap)
+    counts = (ctypes.c_int64 * cap)()
+    ms = (ctypes.c_double * cap)()
+    total = lib.muon_profile_read(names, counts, ms, cap, int(bool(reset)))
+    if total < 0:
+        _lib.check(total)
+    out = {}
+    for i in range(min(total, cap)):
+        nm = names.raw[48 * i: 48 * (i + 1)].split(b"\0", 1)[0].decode()
+        out[nm] = (int(counts[i]), float(ms[i]))
+    return out
+
+
+def version() -> int:
+    return int(_lib.load().muon_version())
+
+
+class PreparedMuonStep:
+    """muon_step with the tensor table marshalled once (same tensors every call).
+
+    Only the scalars may change between calls; the tensors, their shapes and the
+    workspace are fixed at construction.
+    """
+
+    def __init__(self, params, grads, moms, *, ns_precision: int = _lib.MUON_NS_BF16, update_outs=None,
+                 workspace=None):
+        self._keep = (list(params), list(grads), list(moms), update_outs, workspace)
+        outs = update_outs if update_outs is not None else [None] * len(params)
+        entries = []
+        for i, (p, g, m, o) in enumerate(zip(params, grads, moms, outs)):
+            for t, nm in ((p, "params"), (g, "grads"), (m, "moms")):
+                _check_tensor(t, f"{nm}[{i}]", 2)
+                if t.shape != p.shape:
+                    raise ValueError(f"tensor {i}: shape mismatch")
+            if o is not None:
+                _check_tensor(o, f"update_outs[{i}]", 2)
+            entries.append((p.data_ptr(), g.data_ptr(), m.data_ptr(), o.data_ptr() if o is not None else 0,
+                            p.shape[0], p.shape[1]))
+        self.n = len(entries)
+        self.table = _lib.tensor_table(entries)
+        self.ns_precision = int(ns_precision)
+        self.device = params[0].device
+        lib = _lib.load()
+        need = lib.muon_workspace_size(self.table, self.n, self.ns_precision)
+        if need == 0:
+            raise _lib.MuonError(_lib.MUON_ERR_INVALID_ARG, lib.muon_last_error().decode())
+        if workspace is None:
+            workspace = _torch().empty(int(need), dtype=_torch().uint8, device=self.device)
+        self.workspace = workspace
+        self._ws_ptr = ctypes.c_void_p(workspace.data_ptr())
+        self._ws_bytes = workspace.numel() * workspace.element_size()
+        self._coeffs = None
+
+    def __call__(self, *, lr, momentum, weight_decay, coeffs, nesterov=True, row_norm=True, stream=None):
+        if self._coeffs is None or self._coeffs[0] != coeffs:
+            key = [tuple(float(v) for v in row) for row in coeffs]
+            self._coeffs = (coeffs, _lib.coeff_array(key))
+        carr, steps = self._coeffs[1]
+        rc = _lib.load().muon_step(self.table, self.n, float(lr), float(momentum), int(bool(nesterov)),
+                                   float(weight_decay), int(bool(row_norm)), steps, carr if steps else None,
+                                   self.ns_precision, self._ws_ptr, self._ws_bytes,
+                                   _stream_handle(stream, self.device))
+        _lib.check(rc)
+
+
+class PreparedEma:
+    """ema_update with the tensor lists marshalled once."""
+
+    def __init__(self, emas, params):
+        self._keep = (list(emas), list(params))
+        n = len(emas)
+        self.n = n
+        self.e = (ctypes.c_void_p * max(1, n))()
+        self.p = (ctypes.c_void_p * max(1, n))()
+        self.numel = (ctypes.c_int64 * max(1, n))()
+        for i, (e, p) in enumerate(zip(emas, params)):
+            _check_tensor(e, f"emas[{i}]")
+            _check_tensor(p, f"params[{i}]")
+            if e.numel() != p.numel():
+                raise ValueError(f"tensor {i}: element counts differ")
+            self.e[i], self.p[i], self.numel[i] = e.data_ptr(), p.data_ptr(), e.numel()
+        self.device = emas[0].device
+
+    def __call__(self, decay: float, stream=None):
+        rc = _lib.load().ema_update(self.e, self.p, self.numel, self.n, float(decay),
+                                    _stream_handle(stream, self.device))
+        _lib.check(rc)

@@ -1,0 +1,521 @@
+// Host side of the Muon step library: argument validation, shape grouping,
+// workspace layout and the launch sequence behind the C ABI in muonstep.h.
+//
+// One muon_step enqueues, on the caller's stream:
+//   prep  (per-row momentum, MuonEq-R row norm, NS input X0 short side first)
+//   frob  (per-matrix Frobenius scale from the per-row sums)
+//   for each NS iteration: ns_gram, ns_square, ns_update (all shape groups
+//   batched in one launch per phase)
+//   apply (decoupled weight decay + shape-scaled update)
+// ema_update enqueues one multi-tensor EMA launch per table chunk.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "../../include/muonstep.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace muon {
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ------------------------------------------------------------- profiling
+struct PendingEvent {
+    std::string name;
+    hipEvent_t start, stop;
+};
+struct ProfileTotal {
+    int64_t count = 0;
+    double ms = 0.0;
+};
+std::mutex g_prof_mu;
+bool g_prof_enabled = false;
+std::vector<PendingEvent> g_pending;
+std::vector<hipEvent_t> g_event_pool;
+std::vector<std::pair<std::string, ProfileTotal>> g_totals;
+
+hipEvent_t take_event() {
+    if (!g_event_pool.empty()) {
+        hipEvent_t e = g_event_pool.back();
+        g_event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Runs `launch` (which returns the launch's hipError_t) bracketed by events
+// when profiling is on.
+template <typename F>
+hipError_t timed_launch(const char* name, hipStream_t s, F launch) {
+    bool prof;
+    {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        prof = g_prof_enabled;
+    }
+    if (!prof) return launch();
+    hipEvent_t e0, e1;
+    {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        e0 = take_event();
+        e1 = take_event();
+    }
+    if (!e0 || !e1) return hipErrorOutOfMemory;
+    hipError_t err = hipEventRecord(e0, s);
+    if (err != hipSuccess) return err;
+    err = launch();
+    if (err != hipSuccess) return err;
+    err = hipEventRecord(e1, s);
+    if (err != hipSuccess) return err;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_pending.push_back({name, e0, e1});
+    return hipSuccess;
+}
+
+// ------------------------------------------------------------- planning
+struct Group {
+    int m, n;        // short side, long side
+    int M, N;        // padded
+    int count = 0;
+    size_t x_off[2], xl_off[2], ah_off, al_off, b_off;
+    int scale_begin = 0;  // index of slot 0 in the scale array
+};
+
+struct Plan {
+    std::vector<Group> groups;
+    std::vector<int> group_of, slot_of;
+    std::vector<size_t> rowsq_off;  // in floats
+    size_t rowsq_base = 0;          // byte offset of the rowsq array
+    size_t scale_base = 0;          // byte offset of the per-matrix scale array
+    size_t bytes = 0;
+};
+
+int transposed_rb(int cols) {
+    // stored rows per workgroup when X0 is the transpose: rb * (cols + 1) floats <= 16384
+    int rb = 64;
+    while (rb > 1 && (size_t)rb * (cols + 1) > 16384) rb >>= 1;
+    return rb;
+}
+
+void make_plan(const muon_tensor_t* t, int n, int precision, Plan& p) {
+    std::map<std::pair<int, int>, int> index;
+    p.group_of.resize(n);
+    p.slot_of.resize(n);
+    p.rowsq_off.resize(n);
+    size_t rowsq_total = 0;
+    for (int i = 0; i < n; ++i) {
+        const int m = std::min(t[i].rows, t[i].cols), nn = std::max(t[i].rows, t[i].cols);
+        auto key = std::make_pair(m, nn);
+        auto it = index.find(key);
+        int g;
+        if (it == index.end()) {
+            g = (int)p.groups.size();
+            index[key] = g;
+            Group G;
+            G.m = m;
+            G.n = nn;
+            G.M = pad_to_tile(m);
+            G.N = pad_to_tile(nn);
+            p.groups.push_back(G);
+        } else {
+            g = it->second;
+        }
+        p.group_of[i] = g;
+        p.slot_of[i] = p.groups[g].count++;
+        p.rowsq_off[i] = rowsq_total;
+        rowsq_total += (size_t)t[i].rows;
+    }
+    const size_t xe = precision == kNsBf16 ? 2 : 4;  // bytes per element of an X / A / B plane
+    size_t off = 0;
+    for (Group& G : p.groups) {
+        const size_t xplane = align256((size_t)G.count * G.M * G.N * xe);
+        const size_t aplane = align256((size_t)G.count * G.M * G.M * xe);
+        for (int k = 0; k < 2; ++k) { G.x_off[k] = off; off += xplane; }
+        if (precision == kNsBf16) {
+            for (int k = 0; k < 2; ++k) { G.xl_off[k] = off; off += xplane; }
+        } else {
+            G.xl_off[0] = G.x_off[0];
+            G.xl_off[1] = G.x_off[1];
+        }
+        G.ah_off = off; off += aplane;
+        if (precision == kNsBf16) { G.al_off = off; off += aplane; } else { G.al_off = G.ah_off; }
+        G.b_off = off; off += aplane;
+    }
+    int scale_count = 0;
+    for (Group& G : p.groups) { G.scale_begin = scale_count; scale_count += G.count; }
+    p.scale_base = off;
+    off += align256((size_t)scale_count * sizeof(float));
+    p.rowsq_base = off;
+    off += align256(rowsq_total * sizeof(float));
+    p.bytes = off;
+}
+
+// ------------------------------------------------------------- validation
+struct Span {
+    uintptr_t lo, hi;
+    int tensor;
+};
+
+int check_overlaps(std::vector<Span>& spans, const char* what) {
+    std::sort(spans.begin(), spans.end(), [](const Span& a, const Span& b) { return a.lo < b.lo; });
+    for (size_t i = 1; i < spans.size(); ++i) {
+        if (spans[i].lo < spans[i - 1].hi)
+            return fail(MUON_ERR_UNSUPPORTED, "%s: buffers of tensors %d and %d overlap", what,
+                        spans[i - 1].tensor, spans[i].tensor);
+    }
+    return MUON_OK;
+}
+
+int validate_tensors(const muon_tensor_t* t, int32_t n, int32_t precision) {
+    if (!t) return fail(MUON_ERR_INVALID_ARG, "tensors is NULL");
+    if (n <= 0 || n > MUON_MAX_TENSORS) return fail(MUON_ERR_INVALID_ARG, "n = %d outside [1, %d]", n, MUON_MAX_TENSORS);
+    if (precision != MUON_NS_BF16 && precision != MUON_NS_FP32)
+        return fail(MUON_ERR_INVALID_ARG, "ns_precision = %d is neither MUON_NS_BF16 nor MUON_NS_FP32", precision);
+    for (int i = 0; i < n; ++i) {
+        const muon_tensor_t& x = t[i];
+        if (x.rows <= 0 || x.cols <= 0)
+            return fail(MUON_ERR_INVALID_ARG, "tensor %d: rows = %d, cols = %d must be positive", i, x.rows, x.cols);
+        if (std::min(x.rows, x.cols) > MUON_MAX_SHORT_SIDE || std::max(x.rows, x.cols) > MUON_MAX_LONG_SIDE)
+            return fail(MUON_ERR_UNSUPPORTED, "tensor %d: shape %d x %d beyond the limits (short side <= %d, long side <= %d)",
+                        i, x.rows, x.cols, MUON_MAX_SHORT_SIDE, MUON_MAX_LONG_SIDE);
+    }
+    return MUON_OK;
+}
+
+int validate_pointers(const muon_tensor_t* t, int32_t n) {
+    std::vector<Span> spans;
+    spans.reserve(4 * (size_t)n);
+    for (int i = 0; i < n; ++i) {
+        const muon_tensor_t& x = t[i];
+        if (!x.param || !x.grad || !x.momentum)
+            return fail(MUON_ERR_INVALID_ARG, "tensor %d: param, grad and momentum must be non-NULL", i);
+        const size_t bytes = (size_t)x.rows * x.cols * sizeof(float);
+        const void* ptrs[4] = {x.param, x.grad, x.momentum, x.update_out};
+        for (int k = 0; k < 4; ++k) {
+            if (!ptrs[k]) continue;
+            if (reinterpret_cast<uintptr_t>(ptrs[k]) % sizeof(float))
+                return fail(MUON_ERR_INVALID_ARG, "tensor %d: pointer %d is not 4-byte aligned", i, k);
+            const uintptr_t lo = reinterpret_cast<uintptr_t>(ptrs[k]);
+            spans.push_back({lo, lo + bytes, i});
+        }
+    }
+    return check_overlaps(spans, "muon_step");
+}
+
+}  // namespace
+}  // namespace muon
+
+using namespace muon;
+
+extern "C" {
+
+const char* muon_last_error(void) { return g_last_error.c_str(); }
+
+int muon_version(void) { return 10000; }
+
+size_t muon_workspace_size(const muon_tensor_t* tensors, int32_t n, int32_t ns_precision) {
+    if (validate_tensors(tensors, n, ns_precision) != MUON_OK) return 0;
+    Plan p;
+    make_plan(tensors, n, ns_precision, p);
+    return p.bytes;
+}
+
+int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum, int32_t nesterov,
+              float weight_decay, int32_t row_norm, int32_t ns_steps, const float* ns_coeffs,
+              int32_t ns_precision, void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = validate_tensors(tensors, n, ns_precision);
+    if (rc) return rc;
+    if (!std::isfinite(lr) || !std::isfinite(momentum) || !std::isfinite(weight_decay))
+        return fail(MUON_ERR_INVALID_ARG, "lr, momentum and weight_decay must be finite");
+    if ((nesterov != 0 && nesterov != 1) || (row_norm != 0 && row_norm != 1))
+        return fail(MUON_ERR_INVALID_ARG, "nesterov and row_norm must be 0 or 1");
+    if (ns_steps < 0 || ns_steps > MUON_MAX_NS_STEPS)
+        return fail(MUON_ERR_INVALID_ARG, "ns_steps = %d outside [0, %d]", ns_steps, MUON_MAX_NS_STEPS);
+    if (ns_steps > 0 && !ns_coeffs) return fail(MUON_ERR_INVALID_ARG, "ns_coeffs is NULL with ns_steps = %d", ns_steps);
+    for (int k = 0; k < 3 * ns_steps; ++k)
+        if (!std::isfinite(ns_coeffs[k])) return fail(MUON_ERR_INVALID_ARG, "ns_coeffs[%d] is not finite", k);
+    rc = validate_pointers(tensors, n);
+    if (rc) return rc;
+    Plan p;
+    make_plan(tensors, n, ns_precision, p);
+    if (!workspace) return fail(MUON_ERR_WORKSPACE, "workspace is NULL (needs %zu bytes)", p.bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+        return fail(MUON_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (workspace_bytes < p.bytes)
+        return fail(MUON_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, p.bytes);
+    {
+        // the workspace must not overlap any tensor
+        const uintptr_t wlo = reinterpret_cast<uintptr_t>(workspace), whi = wlo + p.bytes;
+        for (int i = 0; i < n; ++i) {
+            const muon_tensor_t& x = tensors[i];
+            const size_t bytes = (size_t)x.rows * x.cols * sizeof(float);
+            const void* ptrs[4] = {x.param, x.grad, x.momentum, x.update_out};
+            for (int k = 0; k < 4; ++k) {
+                if (!ptrs[k]) continue;
+                const uintptr_t lo = reinterpret_cast<uintptr_t>(ptrs[k]);
+                if (lo < whi && wlo < lo + bytes)
+                    return fail(MUON_ERR_UNSUPPORTED, "tensor %d overlaps the workspace", i);
+            }
+        }
+    }
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    float* rowsq = reinterpret_cast<float*>(ws + p.rowsq_base);
+    const int prec = ns_precision;
+    hipError_t err;
+
+    // ---- prep: momentum, row norm, X0 (short side first, zero padded)
+    for (int c0 = 0; c0 < n; c0 += kPrepChunk) {
+        PrepArgs a;
+        memset(&a, 0, sizeof(a));
+        a.mu = momentum;
+        a.nesterov = nesterov;
+        a.row_norm = row_norm;
+        int blocks = 0;
+        size_t lds = 0;
+        for (int i = c0; i < std::min(n, c0 + kPrepChunk); ++i) {
+            const muon_tensor_t& x = tensors[i];
+            const Group& G = p.groups[p.group_of[i]];
+            PrepTensor& T = a.t[a.n++];
+            T.grad = x.grad;
+            T.mom = x.momentum;
+            const size_t xe = prec == kNsBf16 ? 2 : 4;
+            const size_t slot_off = (size_t)p.slot_of[i] * G.M * G.N * xe;
+            T.xh = ws + G.x_off[0] + slot_off;
+            T.xl = ws + G.xl_off[0] + slot_off;
+            T.rowsq = rowsq + p.rowsq_off[i];
+            T.rows = x.rows;
+            T.cols = x.cols;
+            T.transposed = x.rows > x.cols;
+            T.m_pad = G.M;
+            T.n_pad = G.N;
+            T.vec = (x.cols % 4 == 0) && (reinterpret_cast<uintptr_t>(x.grad) % 16 == 0) &&
+                    (reinterpret_cast<uintptr_t>(x.momentum) % 16 == 0);
+            T.block_begin = blocks;
+            if (T.transposed) {
+                T.rb = transposed_rb(x.cols);
+                blocks += G.N / T.rb;
+                lds = std::max(lds, (size_t)T.rb * (x.cols + 1) * sizeof(float));
+            } else {
+                T.rb = kRowsPerWaveBlock;
+                blocks += G.M / kRowsPerWaveBlock;
+            }
+        }
+        err = timed_launch("prep", s, [&] { return launch_prep(a, prec, blocks, lds, s); });
+        if (err != hipSuccess) return fail(MUON_ERR_HIP, "prep launch failed: %s", hipGetErrorString(err));
+    }
+
+    // ---- Frobenius scales
+    for (int c0 = 0; c0 < n; c0 += kFrobChunk) {
+        FrobArgs a;
+        memset(&a, 0, sizeof(a));
+        a.rowsq = rowsq;
+        a.scale = reinterpret_cast<float*>(ws + p.scale_base);
+        for (int i = c0; i < std::min(n, c0 + kFrobChunk); ++i) {
+            const Group& G = p.groups[p.group_of[i]];
+            a.rowsq_off[a.n] = (int)p.rowsq_off[i];
+            a.rows[a.n] = tensors[i].rows;
+            a.scale_idx[a.n] = G.scale_begin + p.slot_of[i];
+            ++a.n;
+        }
+        err = timed_launch("frob", s, [&] { return launch_frob(a, s); });
+        if (err != hipSuccess) return fail(MUON_ERR_HIP, "frob launch failed: %s", hipGetErrorString(err));
+    }
+
+    // ---- Newton-Schulz iterations
+    const int ngroups = (int)p.groups.size();
+    for (int k = 0; k < ns_steps; ++k) {
+        for (int phase = kGram; phase <= kUpdate; ++phase) {
+            for (int g0 = 0; g0 < ngroups; g0 += kMaxGroups) {
+                NsArgs a;
+                memset(&a, 0, sizeof(a));
+                a.src = k & 1;
+                a.first = (k == 0);
+                a.a = ns_coeffs[3 * k + 0];
+                a.b = ns_coeffs[3 * k + 1];
+                a.c = ns_coeffs[3 * k + 2];
+                int jobs = 0;
+                for (int g = g0; g < std::min(ngroups, g0 + kMaxGroups); ++g) {
+                    const Group& G = p.groups[g];
+                    NsGroup& D = a.g[a.ngroups++];
+                    for (int b = 0; b < 2; ++b) {
+                        D.x[b] = ws + G.x_off[b];
+                        D.xl[b] = ws + G.xl_off[b];
+                    }
+                    D.a_hi = ws + G.ah_off;
+                    D.a_lo = ws + G.al_off;
+                    D.b = ws + G.b_off;
+                    D.scale = reinterpret_cast<const float*>(ws + p.scale_base) + G.scale_begin;
+                    D.count = G.count;
+                    D.M = G.M;
+                    D.N = G.N;
+                    D.job_begin = jobs;
+                    const int tm = G.M / kTile, tn = G.N / kTile;
+                    jobs += G.count * (phase == kUpdate ? tm * tn : tm * (tm + 1) / 2);
+                }
+                a.total_jobs = jobs;
+                err = timed_launch(ns_kernel_name(phase, prec), s, [&] { return launch_ns(a, phase, prec, s); });
+                if (err != hipSuccess)
+                    return fail(MUON_ERR_HIP, "%s launch failed: %s", ns_kernel_name(phase, prec), hipGetErrorString(err));
+            }
+        }
+    }
+
+    // ---- apply: W' = (1 - lr wd) W - lr s O
+    const int final_buf = ns_steps & 1;
+    for (int c0 = 0; c0 < n; c0 += kPrepChunk) {
+        ApplyArgs a;
+        memset(&a, 0, sizeof(a));
+        a.keep = 1.0f - lr * weight_decay;
+        a.use_scale = ns_steps == 0;
+        int blocks = 0;
+        size_t lds = 0;
+        for (int i = c0; i < std::min(n, c0 + kPrepChunk); ++i) {
+            const muon_tensor_t& x = tensors[i];
+            const Group& G = p.groups[p.group_of[i]];
+            ApplyTensor& T = a.t[a.n++];
+            T.param = x.param;
+            T.out = x.update_out;
+            const size_t xe = prec == kNsBf16 ? 2 : 4;
+            const size_t slot_off = (size_t)p.slot_of[i] * G.M * G.N * xe;
+            T.xh = ws + G.x_off[final_buf] + slot_off;
+            T.xl = ws + G.xl_off[final_buf] + slot_off;
+            T.scale = reinterpret_cast<const float*>(ws + p.scale_base) + G.scale_begin + p.slot_of[i];
+            T.lr_s = lr * (float)std::sqrt(std::max(1.0, (double)x.rows / (double)x.cols));
+            T.rows = x.rows;
+            T.cols = x.cols;
+            T.n_pad = G.N;
+            T.transposed = x.rows > x.cols;
+            T.vec = (x.cols % 4 == 0) && (reinterpret_cast<uintptr_t>(x.param) % 16 == 0) &&
+                    (reinterpret_cast<uintptr_t>(x.update_out) % 16 == 0);
+            T.block_begin = blocks;
+            if (T.transposed) {
+                T.rb = transposed_rb(x.cols);
+                blocks += (x.rows + T.rb - 1) / T.rb;
+                lds = std::max(lds, (size_t)T.rb * (x.cols + 1) * sizeof(float));
+            } else {
+                T.rb = kRowsPerWaveBlock;
+                blocks += (x.rows + kRowsPerWaveBlock - 1) / kRowsPerWaveBlock;
+            }
+        }
+        err = timed_launch("apply", s, [&] { return launch_apply(a, prec, blocks, lds, s); });
+        if (err != hipSuccess) return fail(MUON_ERR_HIP, "apply launch failed: %s", hipGetErrorString(err));
+    }
+    return MUON_OK;
+}
+
+int ema_update(float* const* ema, const float* const* params, const int64_t* numel, int32_t n, float decay,
+               void* stream) {
+    if (!ema || !params || !numel) return fail(MUON_ERR_INVALID_ARG, "ema, params and numel must be non-NULL");
+    if (n <= 0 || n > MUON_MAX_TENSORS) return fail(MUON_ERR_INVALID_ARG, "n = %d outside [1, %d]", n, MUON_MAX_TENSORS);
+    if (!std::isfinite(decay) || decay < 0.f || decay > 1.f)
+        return fail(MUON_ERR_INVALID_ARG, "decay must be finite and in [0, 1]");
+    std::vector<Span> spans;
+    for (int i = 0; i < n; ++i) {
+        if (numel[i] < 0) return fail(MUON_ERR_INVALID_ARG, "numel[%d] = %lld is negative", i, (long long)numel[i]);
+        if (numel[i] == 0) continue;
+        if (!ema[i] || !params[i]) return fail(MUON_ERR_INVALID_ARG, "tensor %d: NULL pointer", i);
+        if (reinterpret_cast<uintptr_t>(ema[i]) % 4 || reinterpret_cast<uintptr_t>(params[i]) % 4)
+            return fail(MUON_ERR_INVALID_ARG, "tensor %d: pointer not 4-byte aligned", i);
+        const uintptr_t e = reinterpret_cast<uintptr_t>(ema[i]);
+        const uintptr_t q = reinterpret_cast<uintptr_t>(params[i]);
+        const size_t bytes = (size_t)numel[i] * sizeof(float);
+        spans.push_back({e, e + bytes, i});
+        spans.push_back({q, q + bytes, i});
+    }
+    // no two buffers of the call may overlap
+    int rc = check_overlaps(spans, "ema_update");
+    if (rc) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int i = 0;
+    while (i < n) {
+        EmaArgs a;
+        memset(&a, 0, sizeof(a));
+        a.decay = decay;
+        a.one_minus_decay = 1.0f - decay;
+        int64_t blocks = 0;
+        for (; i < n && a.n < kEmaChunk; ++i) {
+            if (numel[i] == 0) continue;
+            const int64_t nb = (numel[i] + kEmaElemsPerBlock - 1) / kEmaElemsPerBlock;
+            if (blocks + nb > (int64_t)1 << 30) break;
+            EmaTensor& T = a.t[a.n++];
+            T.ema = ema[i];
+            T.param = params[i];
+            T.numel = numel[i];
+            T.block_begin = (int)blocks;
+            T.vec = (reinterpret_cast<uintptr_t>(ema[i]) % 16 == 0) && (reinterpret_cast<uintptr_t>(params[i]) % 16 == 0);
+            blocks += nb;
+        }
+        if (a.n == 0) continue;
+        hipError_t err = timed_launch("ema", s, [&] { return launch_ema(a, (int)blocks, s); });
+        if (err != hipSuccess) return fail(MUON_ERR_HIP, "ema launch failed: %s", hipGetErrorString(err));
+    }
+    return MUON_OK;
+}
+
+int muon_profile_enable(int32_t enable) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_enabled = enable != 0;
+    return MUON_OK;
+}
+
+int muon_profile_read(char* names, int64_t* counts, double* total_ms, int32_t cap, int32_t reset) {
+    std::vector<PendingEvent> pending;
+    {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        pending.swap(g_pending);
+    }
+    for (PendingEvent& e : pending) {
+        hipError_t err = hipEventSynchronize(e.stop);
+        float ms = 0.f;
+        if (err == hipSuccess) err = hipEventElapsedTime(&ms, e.start, e.stop);
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        if (err != hipSuccess) return fail(MUON_ERR_HIP, "profile event: %s", hipGetErrorString(err));
+        auto it = std::find_if(g_totals.begin(), g_totals.end(), [&](const auto& kv) { return kv.first == e.name; });
+        if (it == g_totals.end()) {
+            g_totals.push_back({e.name, ProfileTotal()});
+            it = g_totals.end() - 1;
+        }
+        it->second.count += 1;
+        it->second.ms += ms;
+        g_event_pool.push_back(e.start);
+        g_event_pool.push_back(e.stop);
+    }
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    const int total = (int)g_totals.size();
+    for (int i = 0; i < total && i < cap; ++i) {
+        if (names) {
+            strncpy(names + 48 * i, g_totals[i].first.c_str(), 47);
+            names[48 * i + 47] = '\0';
+        }
+        if (counts) counts[i] = g_totals[i].second.count;
+        if (total_ms) total_ms[i] = g_totals[i].second.ms;
+    }
+    if (reset) g_totals.clear();
+    return total;
+}
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Shared device-side definitions for the gfx950 Muon step kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dispatched round-robin
+constexpr int kTile = 128;        // NS output tile edge; workspace dims are padded to it
+constexpr float kEps = 1e-7f;     // added to the row and Frobenius norms
+
+// Number of elements of the workspace layouts kept per NS precision.
+enum NsPrecision { kNsBf16 = 0, kNsFp32 = 1 };
+
+__host__ __device__ inline int pad_to_tile(int x) { return (x + kTile - 1) / kTile * kTile; }
+
+// fp32 -> bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ inline bf16 to_bf16(float x) { return (bf16)x; }
+__device__ inline float from_bf16(bf16 x) { return (float)x; }
+
+// x == hi + lo to ~16 significant bits: hi = rne(x), lo = rne(x - hi).
+__device__ inline void split_bf16(float x, bf16& hi, bf16& lo) {
+    hi = to_bf16(x);
+    lo = to_bf16(x - from_bf16(hi));
+}
+
+__device__ inline uint32_t bf16_bits(bf16 x) { return (uint32_t)__builtin_bit_cast(uint16_t, x); }
+__device__ inline bf16 bits_bf16(uint32_t b) { return __builtin_bit_cast(bf16, (uint16_t)b); }
+
+__device__ inline float wave_sum(float v) {
+    // Butterfly over the 64 lanes; every lane ends with the same total and the
+    // order of additions is fixed, so results are reproducible.
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// Remap blockIdx so that consecutive job indices land on the same XCD (blocks
+// are dispatched round-robin over the XCDs).  grid must be a multiple of kXcds.
+__device__ inline int xcd_job_index() {
+    const int b = blockIdx.x;
+    const int per_xcd = gridDim.x / kXcds;
+    return (b % kXcds) * per_xcd + b / kXcds;
+}
+
+}  // namespace muon

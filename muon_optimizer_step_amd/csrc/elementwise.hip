@@ -1,0 +1,318 @@
+// Streaming kernels of the Muon step: momentum / row-norm / NS-input preparation
+// (prep), the per-matrix Frobenius scale (frob), the weight update (apply) and
+// the multi-tensor weight EMA (ema).  All are HBM-bound: coalesced fp32 streams,
+// float4 where the pointers allow, wavefront-shuffle reductions in a fixed
+// order.
+//
+// Method: "Record: L_ParallelResiduals_UNetSkips_DepthRecur_Muon_ 1.0901"
+// (PR #1893), "Architecture and training stack" (Muon with momentum, weight
+// EMA); "Record: Combined 3-Layer Recurrence + Parallel Residuals + Polar
+// Express + Brotli" (PR #1396), "Techniques Combined" (MuonEq-R row norm before
+// NS, WD 0.105); "Record: Improved Parallel Residuals + Systems Optimization"
+// (PR #1584), "Summary" (batched EMA over all parameters).
+#include "common.h"
+#include "kernels.h"
+
+namespace muon {
+
+namespace {
+
+template <typename Tab>
+__device__ inline int find_tensor(const Tab* t, int n, int blk) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (t[mid].block_begin <= blk) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Momentum: M' = mu*M + G;  U = G + mu*M' (Nesterov) or M'.
+__device__ inline float momentum_u(float g, float m, float mu, int nesterov, float& m_new) {
+    m_new = fmaf(mu, m, g);
+    return nesterov ? fmaf(mu, m_new, g) : m_new;
+}
+
+template <int PREC>
+__device__ inline void store_x(void* xh, void* xl, size_t idx, float v) {
+    if (PREC == kNsBf16) {
+        bf16 h, l;
+        split_bf16(v, h, l);
+        static_cast<bf16*>(xh)[idx] = h;
+        static_cast<bf16*>(xl)[idx] = l;
+    } else {
+        static_cast<float*>(xh)[idx] = v;
+    }
+}
+
+template <int PREC>
+__device__ inline float load_x(const void* xh, const void* xl, size_t idx) {
+    if (PREC == kNsBf16) {
+        return from_bf16(static_cast<const bf16*>(xh)[idx]) + from_bf16(static_cast<const bf16*>(xl)[idx]);
+    } else {
+        return static_cast<const float*>(xh)[idx];
+    }
+}
+
+// One stored row, one wavefront.  Pass 1 reduces sum(U^2) (no writes); pass 2
+// recomputes U, writes M', and hands r = U/(|U|+eps) (or U) to `emit`.
+// Returns sum(r^2) on every lane.
+template <typename Emit>
+__device__ inline float process_row(const float* __restrict__ g, float* __restrict__ m, int cols, int vec,
+                                    float mu, int nesterov, int row_norm, int lane, Emit emit) {
+    float ss = 0.f;
+    if (vec) {
+        const float4* g4 = reinterpret_cast<const float4*>(g);
+        const float4* m4 = reinterpret_cast<const float4*>(m);
+        for (int j = lane; j < cols / 4; j += kWave) {
+            const float4 gv = g4[j], mv = m4[j];
+            float t;
+            const float u0 = momentum_u(gv.x, mv.x, mu, nesterov, t);
+            const float u1 = momentum_u(gv.y, mv.y, mu, nesterov, t);
+            const float u2 = momentum_u(gv.z, mv.z, mu, nesterov, t);
+            const float u3 = momentum_u(gv.w, mv.w, mu, nesterov, t);
+            ss = fmaf(u0, u0, ss); ss = fmaf(u1, u1, ss); ss = fmaf(u2, u2, ss); ss = fmaf(u3, u3, ss);
+        }
+    } else {
+        for (int j = lane; j < cols; j += kWave) {
+            float t;
+            const float u = momentum_u(g[j], m[j], mu, nesterov, t);
+            ss = fmaf(u, u, ss);
+        }
+    }
+    ss = wave_sum(ss);
+    const float denom = sqrtf(ss) + kEps;
+    float rs = 0.f;
+    if (vec) {
+        const float4* g4 = reinterpret_cast<const float4*>(g);
+        float4* m4 = reinterpret_cast<float4*>(m);
+        for (int j = lane; j < cols / 4; j += kWave) {
+            const float4 gv = g4[j], mv = m4[j];
+            float4 mn;
+            float4 u;
+            u.x = momentum_u(gv.x, mv.x, mu, nesterov, mn.x);
+            u.y = momentum_u(gv.y, mv.y, mu, nesterov, mn.y);
+            u.z = momentum_u(gv.z, mv.z, mu, nesterov, mn.z);
+            u.w = momentum_u(gv.w, mv.w, mu, nesterov, mn.w);
+            m4[j] = mn;
+            if (row_norm) { u.x /= denom; u.y /= denom; u.z /= denom; u.w /= denom; }
+            rs = fmaf(u.x, u.x, rs); rs = fmaf(u.y, u.y, rs); rs = fmaf(u.z, u.z, rs); rs = fmaf(u.w, u.w, rs);
+            emit(4 * j + 0, u.x); emit(4 * j + 1, u.y); emit(4 * j + 2, u.z); emit(4 * j + 3, u.w);
+        }
+    } else {
+        for (int j = lane; j < cols; j += kWave) {
+            float mn;
+            float u = momentum_u(g[j], m[j], mu, nesterov, mn);
+            m[j] = mn;
+            if (row_norm) u /= denom;
+            rs = fmaf(u, u, rs);
+            emit(j, u);
+        }
+    }
+    return wave_sum(rs);
+}
+
+template <int PREC>
+__global__ __launch_bounds__(256) void prep_kernel(const PrepArgs a) {
+    extern __shared__ float lds_rows[];
+    const int ti = find_tensor(a.t, a.n, blockIdx.x);
+    const PrepTensor& T = a.t[ti];
+    const int blk = blockIdx.x - T.block_begin;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const size_t ld = (size_t)T.n_pad;
+
+    if (!T.transposed) {
+        // X0 row i is stored row i; rows in [rows, m_pad) and cols in [cols, n_pad) are zero.
+        const int row = blk * kRowsPerWaveBlock + wave;
+        if (row >= T.m_pad) return;
+        const size_t xrow = (size_t)row * ld;
+        if (row < T.rows) {
+            const float* g = T.grad + (size_t)row * T.cols;
+            float* m = T.mom + (size_t)row * T.cols;
+            const float rs = process_row(g, m, T.cols, T.vec, a.mu, a.nesterov, a.row_norm, lane,
+                                         [&](int j, float r) { store_x<PREC>(T.xh, T.xl, xrow + j, r); });
+            if (lane == 0) T.rowsq[row] = rs;
+            for (int j = T.cols + lane; j < T.n_pad; j += kWave) store_x<PREC>(T.xh, T.xl, xrow + j, 0.f);
+        } else {
+            for (int j = lane; j < T.n_pad; j += kWave) store_x<PREC>(T.xh, T.xl, xrow + j, 0.f);
+        }
+        return;
+    }
+
+    // Transposed: X0[j][i] = r[i][j].  The workgroup owns stored rows
+    // [blk*rb, blk*rb + rb), stages r in LDS, then writes X0 columns
+    // [blk*rb, blk*rb + rb) for every X0 row j in [0, m_pad).
+    const int rb = T.rb;
+    const int pitch = T.cols + 1;
+    const int row0 = blk * rb;
+    for (int rr = wave; rr < rb; rr += 4) {
+        const int row = row0 + rr;
+        float* dst = lds_rows + (size_t)rr * pitch;
+        if (row < T.rows) {
+            const float* g = T.grad + (size_t)row * T.cols;
+            float* m = T.mom + (size_t)row * T.cols;
+            const float rs = process_row(g, m, T.cols, T.vec, a.mu, a.nesterov, a.row_norm, lane,
+                                         [&](int j, float r) { dst[j] = r; });
+            if (lane == 0) T.rowsq[row] = rs;
+        } else {
+            for (int j = lane; j < T.cols; j += kWave) dst[j] = 0.f;
+        }
+    }
+    __syncthreads();
+    const int items = T.m_pad * rb;
+    for (int it = threadIdx.x; it < items; it += blockDim.x) {
+        const int j = it / rb;
+        const int rr = it - j * rb;
+        const float v = (j < T.cols) ? lds_rows[(size_t)rr * pitch + j] : 0.f;
+        store_x<PREC>(T.xh, T.xl, (size_t)j * ld + row0 + rr, v);
+    }
+}
+
+// One workgroup per matrix: scale = 1 / (sqrt(sum of the row sums) + eps),
+// summed in a fixed order.
+__global__ __launch_bounds__(256) void frob_kernel(const FrobArgs a) {
+    __shared__ float part[256];
+    const int i = blockIdx.x;
+    const float* rs = a.rowsq + a.rowsq_off[i];
+    float s = 0.f;
+    for (int r = threadIdx.x; r < a.rows[i]; r += blockDim.x) s += rs[r];
+    part[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) a.scale[a.scale_idx[i]] = 1.0f / (sqrtf(part[0]) + kEps);
+}
+
+// W' = keep*W - lr_s*O with O = fac*X (fac = Frobenius scale when no NS step ran).
+template <int PREC>
+__global__ __launch_bounds__(256) void apply_kernel(const ApplyArgs a) {
+    extern __shared__ float lds_o[];
+    const int ti = find_tensor(a.t, a.n, blockIdx.x);
+    const ApplyTensor& T = a.t[ti];
+    const int blk = blockIdx.x - T.block_begin;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const float fac = a.use_scale ? *T.scale : 1.0f;
+    const float keep = a.keep;
+    const float lr_s = T.lr_s;
+    const size_t ld = (size_t)T.n_pad;
+
+    if (!T.transposed) {
+        const int row = blk * kRowsPerWaveBlock + wave;
+        if (row >= T.rows) return;
+        float* w = T.param + (size_t)row * T.cols;
+        float* out = T.out ? T.out + (size_t)row * T.cols : nullptr;
+        const size_t xrow = (size_t)row * ld;
+        if (T.vec) {
+            float4* w4 = reinterpret_cast<float4*>(w);
+            float4* o4 = reinterpret_cast<float4*>(out);
+            for (int j = lane; j < T.cols / 4; j += kWave) {
+                float4 o;
+                o.x = fac * load_x<PREC>(T.xh, T.xl, xrow + 4 * j + 0);
+                o.y = fac * load_x<PREC>(T.xh, T.xl, xrow + 4 * j + 1);
+                o.z = fac * load_x<PREC>(T.xh, T.xl, xrow + 4 * j + 2);
+                o.w = fac * load_x<PREC>(T.xh, T.xl, xrow + 4 * j + 3);
+                float4 wv = w4[j];
+                wv.x = fmaf(-lr_s, o.x, keep * wv.x);
+                wv.y = fmaf(-lr_s, o.y, keep * wv.y);
+                wv.z = fmaf(-lr_s, o.z, keep * wv.z);
+                wv.w = fmaf(-lr_s, o.w, keep * wv.w);
+                w4[j] = wv;
+                if (o4) o4[j] = o;
+            }
+        } else {
+            for (int j = lane; j < T.cols; j += kWave) {
+                const float o = fac * load_x<PREC>(T.xh, T.xl, xrow + j);
+                w[j] = fmaf(-lr_s, o, keep * w[j]);
+                if (out) out[j] = o;
+            }
+        }
+        return;
+    }
+
+    // Transposed: O[i][j] = X[j][i].  Stage X columns [row0, row0+rb) in LDS.
+    const int rb = T.rb;
+    const int pitch = T.cols + 1;
+    const int row0 = blk * rb;
+    const int items = T.cols * rb;
+    for (int it = threadIdx.x; it < items; it += blockDim.x) {
+        const int j = it / rb;
+        const int rr = it - j * rb;
+        lds_o[(size_t)rr * pitch + j] = (row0 + rr < T.rows) ? fac * load_x<PREC>(T.xh, T.xl, (size_t)j * ld + row0 + rr) : 0.f;
+    }
+    __syncthreads();
+    for (int rr = wave; rr < rb; rr += 4) {
+        const int row = row0 + rr;
+        if (row >= T.rows) break;
+        float* w = T.param + (size_t)row * T.cols;
+        float* out = T.out ? T.out + (size_t)row * T.cols : nullptr;
+        const float* o = lds_o + (size_t)rr * pitch;
+        for (int j = lane; j < T.cols; j += kWave) {
+            w[j] = fmaf(-lr_s, o[j], keep * w[j]);
+            if (out) out[j] = o[j];
+        }
+    }
+}
+
+// E' = d*E + (1-d)*P over a chunk of kEmaElemsPerBlock elements of one tensor.
+__global__ __launch_bounds__(kEmaThreads) void ema_kernel(const EmaArgs a) {
+    const int ti = find_tensor(a.t, a.n, blockIdx.x);
+    const EmaTensor& T = a.t[ti];
+    const int64_t base = (int64_t)(blockIdx.x - T.block_begin) * kEmaElemsPerBlock;
+    const int64_t end = min(base + (int64_t)kEmaElemsPerBlock, T.numel);
+    const float d = a.decay, omd = a.one_minus_decay;
+    if (T.vec && end - base == kEmaElemsPerBlock) {
+        floatx4* e4 = reinterpret_cast<floatx4*>(T.ema + base);
+        const floatx4* p4 = reinterpret_cast<const floatx4*>(T.param + base);
+        floatx4 ev[4], pv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            ev[k] = __builtin_nontemporal_load(e4 + threadIdx.x + k * kEmaThreads);
+            pv[k] = __builtin_nontemporal_load(p4 + threadIdx.x + k * kEmaThreads);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            floatx4 r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = fmaf(d, ev[k][e], omd * pv[k][e]);
+            __builtin_nontemporal_store(r, e4 + threadIdx.x + k * kEmaThreads);
+        }
+        return;
+    }
+    for (int64_t i = base + threadIdx.x; i < end; i += kEmaThreads) {
+        T.ema[i] = fmaf(d, T.ema[i], omd * T.param[i]);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prep(const PrepArgs& a, int precision, int blocks, size_t lds_bytes, hipStream_t s) {
+    if (precision == kNsBf16)
+        prep_kernel<kNsBf16><<<blocks, 256, lds_bytes, s>>>(a);
+    else
+        prep_kernel<kNsFp32><<<blocks, 256, lds_bytes, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_frob(const FrobArgs& a, hipStream_t s) {
+    frob_kernel<<<a.n, 256, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_apply(const ApplyArgs& a, int precision, int blocks, size_t lds_bytes, hipStream_t s) {
+    if (precision == kNsBf16)
+        apply_kernel<kNsBf16><<<blocks, 256, lds_bytes, s>>>(a);
+    else
+        apply_kernel<kNsFp32><<<blocks, 256, lds_bytes, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_ema(const EmaArgs& a, int blocks, hipStream_t s) {
+    ema_kernel<<<blocks, kEmaThreads, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace muon

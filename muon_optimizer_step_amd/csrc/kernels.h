@@ -1,0 +1,129 @@
+// Kernel argument blocks and launchers of the Muon step library (host + device).
+//
+// Every multi-tensor kernel takes its tensor table by value as a kernel
+// argument (no device-side table, no upload); tables are chunked on the host so
+// that each argument block stays under 4 KiB.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+constexpr int kMaxGroups = 12;    // NS shape groups per NS launch
+constexpr int kPrepChunk = 40;    // tensors per prep / apply launch
+constexpr int kFrobChunk = 256;   // matrices per Frobenius-scale launch
+constexpr int kEmaChunk = 112;    // tensors per EMA launch
+constexpr int kRowsPerWaveBlock = 4;  // stored rows per workgroup when no transpose is needed
+
+// ---------------------------------------------------------------- prep (K1)
+// Momentum update, optional row normalisation, per-row sum of squares, and the
+// NS input written short-side-first into the zero-padded workspace planes.
+struct PrepTensor {
+    const float* grad;
+    float* mom;
+    void* xh;        // bf16: hi plane of X0; fp32: the X0 plane.  [M_pad][N_pad]
+    void* xl;        // bf16: lo plane of X0; fp32: unused
+    float* rowsq;    // one float per stored row
+    int rows, cols;  // stored shape
+    int m_pad, n_pad;
+    int transposed;  // rows > cols: X0 = U^T
+    int rb;          // stored rows per workgroup
+    int block_begin; // first workgroup of this tensor
+    int vec;         // grad/mom 16-byte aligned and cols % 4 == 0
+};
+struct PrepArgs {
+    PrepTensor t[kPrepChunk];
+    int n;
+    float mu;
+    int nesterov;
+    int row_norm;
+};
+
+// ------------------------------------------------------- Frobenius scale
+struct FrobArgs {
+    const float* rowsq;          // base of the per-row sums
+    float* scale;                // base of the per-matrix scales
+    int rowsq_off[kFrobChunk];
+    int rows[kFrobChunk];
+    int scale_idx[kFrobChunk];
+    int n;
+};
+
+// ------------------------------------------------------------- NS phases
+struct NsGroup {
+    void* x[2];      // bf16: hi planes (ping-pong); fp32: X planes.  [count][M][N]
+    void* xl[2];     // bf16: lo planes; fp32: unused
+    void* a_hi;      // bf16: hi of A; fp32: A.  [count][M][M]
+    void* a_lo;      // bf16: lo of A; fp32: unused
+    void* b;         // bf16: B rounded; fp32: B.  [count][M][M]
+    const float* scale;  // [count] Frobenius scale of X0
+    int count, M, N;     // padded, multiples of 128
+    int job_begin;
+};
+struct NsArgs {
+    NsGroup g[kMaxGroups];
+    int ngroups;
+    int total_jobs;
+    int src;         // ping-pong plane holding the current X
+    int first;       // iteration 0: fold the Frobenius scale in
+    float a, b, c;
+};
+
+enum NsPhase { kGram = 0, kSquare = 1, kUpdate = 2 };
+
+// ------------------------------------------------------------- apply (K3)
+struct ApplyTensor {
+    float* param;
+    float* out;          // optional copy of O (stored layout)
+    const void* xh;      // final X: bf16 hi plane or fp32 plane
+    const void* xl;      // bf16 lo plane
+    const float* scale;  // Frobenius scale (used when no NS step ran)
+    float lr_s;          // lr * shape scale
+    int rows, cols;
+    int n_pad;           // leading dimension of X
+    int transposed;
+    int rb;
+    int block_begin;
+    int vec;             // param/out 16-byte aligned and cols % 4 == 0
+};
+struct ApplyArgs {
+    ApplyTensor t[kPrepChunk];
+    int n;
+    float keep;          // 1 - lr*wd
+    int use_scale;       // 1 when ns_steps == 0
+};
+
+// ------------------------------------------------------------------ EMA (K4)
+struct EmaTensor {
+    float* ema;
+    const float* param;
+    int64_t numel;
+    int block_begin;
+    int vec;             // both pointers 16-byte aligned
+};
+struct EmaArgs {
+    EmaTensor t[kEmaChunk];
+    int n;
+    float decay;
+    float one_minus_decay;
+};
+constexpr int kEmaThreads = 256;
+constexpr int kEmaElemsPerBlock = kEmaThreads * 4 * 4;  // float4 x 4 per thread
+
+static_assert(sizeof(PrepArgs) <= 4096, "prep kernel arguments exceed 4 KiB");
+static_assert(sizeof(FrobArgs) <= 4096, "frob kernel arguments exceed 4 KiB");
+static_assert(sizeof(NsArgs) <= 4096, "NS kernel arguments exceed 4 KiB");
+static_assert(sizeof(ApplyArgs) <= 4096, "apply kernel arguments exceed 4 KiB");
+static_assert(sizeof(EmaArgs) <= 4096, "EMA kernel arguments exceed 4 KiB");
+
+// Launchers: enqueue on `s`, return hipGetLastError() of the launch.
+hipError_t launch_prep(const PrepArgs& a, int precision, int blocks, size_t lds_bytes, hipStream_t s);
+hipError_t launch_frob(const FrobArgs& a, hipStream_t s);
+hipError_t launch_ns(const NsArgs& a, int phase, int precision, hipStream_t s);
+hipError_t launch_apply(const ApplyArgs& a, int precision, int blocks, size_t lds_bytes, hipStream_t s);
+hipError_t launch_ema(const EmaArgs& a, int blocks, hipStream_t s);
+
+const char* ns_kernel_name(int phase, int precision);
+
+}  // namespace muon

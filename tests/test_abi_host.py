@@ -1,0 +1,182 @@
+"""The C ABI on the host: the library loads, exports what include/muonstep.h
+declares, sizes workspaces, and rejects bad arguments before touching a GPU.
+
+Every call here fails validation (or only sizes a workspace), so no HIP call
+is made and no GPU is needed.
+"""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+from muon_optimizer_step_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muonstep.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([A-Za-z_]\w*)\s*\([^;{]*\)\s*;", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_abi():
+    names = _declared_functions()
+    assert names == sorted(["muon_workspace_size", "muon_step", "ema_update", "muon_last_error",
+                            "muon_version", "muon_profile_enable", "muon_profile_read"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    assert lib.muon_version() == 10000
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    for name in ["MUON_OK", "MUON_ERR_INVALID_ARG", "MUON_ERR_UNSUPPORTED", "MUON_ERR_WORKSPACE", "MUON_ERR_HIP",
+                 "MUON_MAX_NS_STEPS", "MUON_MAX_SHORT_SIDE", "MUON_MAX_LONG_SIDE", "MUON_MAX_TENSORS",
+                 "MUON_NS_BF16", "MUON_NS_FP32"]:
+        m = re.search(rf"#define {name} \(?(-?\d+)\)?", text)
+        assert m, name
+        assert int(m.group(1)) == getattr(_lib, name), name
+    assert ctypes.sizeof(_lib.MuonTensor) == 40
+
+
+# Fake, well-separated device addresses: validation only compares them.
+BASE = 1 << 40
+
+
+def _t(i, rows, cols, out=False):
+    span = 1 << 30
+    p = BASE + 4 * i * span
+    return (p, p + span, p + 2 * span, (p + 3 * span) if out else 0, rows, cols)
+
+
+def _call(entries, lr=0.02, mu=0.95, nesterov=1, wd=0.1, row_norm=1, steps=5, coeffs="std",
+          prec=0, ws=BASE + (1 << 45), ws_bytes=1 << 40, n=None):
+    lib = _lib.load()
+    table = _lib.tensor_table(entries)
+    if coeffs == "std":
+        carr, k = _lib.coeff_array([(3.4445, -4.775, 2.0315)] * max(steps, 0))
+        cptr = carr
+    else:
+        cptr = coeffs
+    rc = lib.muon_step(table, len(entries) if n is None else n, lr, mu, nesterov, wd, row_norm, steps, cptr, prec,
+                       ctypes.c_void_p(ws), ws_bytes, None)
+    return rc, lib.muon_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(n=0), _lib.MUON_ERR_INVALID_ARG, "n = 0"),
+    (dict(n=_lib.MUON_MAX_TENSORS + 1), _lib.MUON_ERR_INVALID_ARG, "outside"),
+    (dict(prec=2), _lib.MUON_ERR_INVALID_ARG, "ns_precision"),
+    (dict(lr=float("nan")), _lib.MUON_ERR_INVALID_ARG, "finite"),
+    (dict(mu=float("inf")), _lib.MUON_ERR_INVALID_ARG, "finite"),
+    (dict(wd=float("-inf")), _lib.MUON_ERR_INVALID_ARG, "finite"),
+    (dict(nesterov=2), _lib.MUON_ERR_INVALID_ARG, "nesterov"),
+    (dict(row_norm=-1), _lib.MUON_ERR_INVALID_ARG, "row_norm"),
+    (dict(steps=-1), _lib.MUON_ERR_INVALID_ARG, "ns_steps"),
+    (dict(steps=_lib.MUON_MAX_NS_STEPS + 1), _lib.MUON_ERR_INVALID_ARG, "ns_steps"),
+    (dict(steps=3, coeffs=None), _lib.MUON_ERR_INVALID_ARG, "ns_coeffs is NULL"),
+    (dict(ws=0), _lib.MUON_ERR_WORKSPACE, "workspace is NULL"),
+    (dict(ws=BASE + (1 << 45) + 16), _lib.MUON_ERR_WORKSPACE, "256-byte"),
+    (dict(ws_bytes=1024), _lib.MUON_ERR_WORKSPACE, "needs"),
+])
+def test_muon_step_rejects_bad_arguments(kw, code, msg):
+    rc, err = _call([_t(0, 64, 32), _t(1, 16, 48)], **kw)
+    assert rc == code and msg in err, (rc, err)
+
+
+def test_muon_step_rejects_non_finite_coefficients():
+    carr, _ = _lib.coeff_array([(3.4445, -4.775, 2.0315), (1.0, float("nan"), 0.0)])
+    rc, err = _call([_t(0, 64, 32)], steps=2, coeffs=carr)
+    assert rc == _lib.MUON_ERR_INVALID_ARG and "ns_coeffs[4]" in err
+
+
+@pytest.mark.parametrize("shape,code", [
+    ((0, 5), _lib.MUON_ERR_INVALID_ARG), ((5, -1), _lib.MUON_ERR_INVALID_ARG),
+    ((_lib.MUON_MAX_SHORT_SIDE + 1, _lib.MUON_MAX_SHORT_SIDE + 1), _lib.MUON_ERR_UNSUPPORTED),
+    ((4, _lib.MUON_MAX_LONG_SIDE + 1), _lib.MUON_ERR_UNSUPPORTED),
+])
+def test_muon_step_rejects_bad_shapes(shape, code):
+    rc, err = _call([_t(0, *shape)])
+    assert rc == code, err
+
+
+def test_muon_step_rejects_null_and_aliased_buffers():
+    p, g, m, o, r, c = _t(0, 64, 64)
+    rc, err = _call([(0, g, m, 0, r, c)])
+    assert rc == _lib.MUON_ERR_INVALID_ARG and "non-NULL" in err
+    rc, err = _call([(p, p, m, 0, r, c)])          # grad aliases param
+    assert rc == _lib.MUON_ERR_UNSUPPORTED and "overlap" in err
+    rc, err = _call([(p, g, m, g + 256, r, c)])    # update_out overlaps grad
+    assert rc == _lib.MUON_ERR_UNSUPPORTED
+    q = _t(1, 64, 64)
+    rc, err = _call([(p, g, m, 0, r, c), (q[0], q[1], m + 4, 0, r, c)])  # two tensors share a buffer
+    assert rc == _lib.MUON_ERR_UNSUPPORTED and "tensors 0 and 1" in err
+    rc, err = _call([(p + 2, g, m, 0, r, c)])      # misaligned
+    assert rc == _lib.MUON_ERR_INVALID_ARG and "aligned" in err
+    rc, err = _call([(p, g, m, 0, r, c)], ws=p - 256)  # workspace overlaps a tensor
+    assert rc == _lib.MUON_ERR_UNSUPPORTED and "workspace" in err
+
+
+def _ws(shapes, prec=0):
+    lib = _lib.load()
+    table = _lib.tensor_table((0, 0, 0, 0, r, c) for r, c in shapes)
+    return lib.muon_workspace_size(table, len(shapes), prec)
+
+
+def test_workspace_size_properties():
+    one = _ws([(512, 512)])
+    # four bf16 planes of X (two ping-pong pairs) and three of the Gram-sized matrices
+    assert one >= 4 * 2 * 512 * 512 + 3 * 2 * 512 * 512
+    assert _ws([(512, 512)], 1) > one                      # fp32 planes are wider
+    # orientation only changes the per-row sums (one float per stored row)
+    assert 0 <= _ws([(2048, 512)]) - _ws([(512, 2048)]) <= 4 * (2048 - 512) + 256
+    assert _ws([(100, 30)]) == _ws([(128, 128)])           # padded to 128 on both sides
+    assert _ws([(512, 512)] * 22) > 21 * one
+    assert _ws([(4, 4)]) % 256 == 0
+    assert _ws([]) == 0 and _ws([(0, 4)]) == 0 and _ws([(4, 4)], 7) == 0
+
+
+def test_ema_rejects_bad_arguments():
+    lib = _lib.load()
+    n = 2
+    e = (ctypes.c_void_p * n)(BASE, BASE + (1 << 30))
+    p = (ctypes.c_void_p * n)(BASE + (2 << 30), BASE + (3 << 30))
+    ne = (ctypes.c_int64 * n)(100, 200)
+
+    def call(e=e, p=p, ne=ne, n=n, decay=0.99):
+        return lib.ema_update(e, p, ne, n, decay, None), lib.muon_last_error().decode()
+
+    assert call(n=0)[0] == _lib.MUON_ERR_INVALID_ARG
+    assert call(decay=1.5)[0] == _lib.MUON_ERR_INVALID_ARG
+    assert call(decay=-0.1)[0] == _lib.MUON_ERR_INVALID_ARG
+    assert call(decay=math.nan)[0] == _lib.MUON_ERR_INVALID_ARG
+    bad = (ctypes.c_int64 * n)(100, -1)
+    assert call(ne=bad)[0] == _lib.MUON_ERR_INVALID_ARG
+    alias = (ctypes.c_void_p * n)(BASE, BASE + 200)   # param 0 overlaps ema 0's tail
+    rc, err = call(p=alias)
+    assert rc == _lib.MUON_ERR_UNSUPPORTED and "overlap" in err
+    nul = (ctypes.c_void_p * n)(BASE, 0)
+    assert call(e=nul)[0] == _lib.MUON_ERR_INVALID_ARG
+    odd = (ctypes.c_void_p * n)(BASE + 2, BASE + (1 << 30))
+    assert call(e=odd)[0] == _lib.MUON_ERR_INVALID_ARG
+
+
+def test_profile_read_without_events():
+    lib = _lib.load()
+    assert lib.muon_profile_enable(0) == 0
+    assert lib.muon_profile_read(None, None, None, 0, 1) == 0

@@ -1,0 +1,161 @@
+"""GPU parity: the HIP library against the float64 oracle on the same seeded inputs.
+
+Layered checks per matrix: the momentum buffer M' (fp32, 1e-6 relative max
+norm), the orthogonalised update O against the oracle run from the same inputs
+(relative Frobenius 2e-2 for bf16 NS, 1e-4 for fp32 NS), the weight W' against
+the oracle's apply step fed the GPU's O (1e-6), and the EMA against the oracle
+EMA fed the GPU's W' (1e-6).  Full-size workloads run in the same launch
+configuration as bench.py; there the oracle recomputes O on a sample of the
+matrices (one of every shape), and checks every element of M', W' and E'.
+"""
+
+import numpy as np
+import pytest
+
+import oracle.muon as om
+import workloads as wl
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_workload(cfg, seed, o_sample=None):
+    w = wl.workload(cfg)
+    gu.say(f"[parity] workload {cfg} ({w.name}) seed {seed}")
+    st = wl.make_state(w, seed)
+    coeffs = wl.coeff_table(w, seed)
+    nm = len(w.matrices)
+    mats, moms = st["params"][:nm], st["moms"]
+    grads = wl.make_grads(w, seed, 0)
+    w_gpu, m_gpu, o_gpu = gu.gpu_step(mats, grads, moms, lr=w.lr, momentum=w.momentum, wd=w.weight_decay,
+                                      coeffs=coeffs.tolist(), nesterov=w.nesterov, row_norm=w.row_norm,
+                                      ns_precision=w.ns_precision)
+    tol = gu.NS_TOL_BF16 if w.ns_precision == 0 else gu.NS_TOL_FP32
+    if o_sample is None:
+        o_sample = range(nm)
+    errs = {}
+    for i in range(nm):
+        e = gu.check_layers(mats[i], grads[i], moms[i], w_gpu[i], m_gpu[i], o_gpu[i], lr=w.lr,
+                            momentum=w.momentum, wd=w.weight_decay, coeffs=coeffs, nesterov=w.nesterov,
+                            row_norm=w.row_norm, ns_tol=tol, check_o=i in o_sample, label=w.matrices[i][0])
+        if e is not None:
+            errs[w.matrices[i][0]] = e
+    gu.say(f"[parity] workload {cfg} seed {seed} NS errors: " +
+           ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    return w, st, w_gpu
+
+
+def test_single_matrix_fp32_ns():
+    _run_workload(0, wl.PRIMARY_SEED)
+
+
+@pytest.mark.parametrize("seed", [wl.PRIMARY_SEED, *wl.ROBUST_SEEDS])
+def test_one_layer_bf16(seed):
+    _run_workload(1, seed)
+
+
+# l0.q, l1.k, l2.v, l3.o, l4.up, l5.down: every stored shape once, from different layers
+ONE_PER_SHAPE = {0, 7, 14, 21, 28, 35}
+
+
+def _check_ema(w, st, w_gpu, decay):
+    import torch
+    import muon_optimizer_step_amd as ms
+    nm = len(w.matrices)
+    post = list(w_gpu) + st["params"][nm:]
+    ema0 = wl.make_independent_ema(w, 7)
+    E = [gu.dev(e) for e in ema0]
+    P = [gu.dev(p) for p in post]
+    ms.ema_update(E, P, decay)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for i, (e0, p, e) in enumerate(zip(ema0, post, E)):
+        err = gu.rel_max(gu.host(e), om.ema_update(e0, p, gu.f32(decay)))
+        worst = max(worst, err)
+        assert err <= gu.ELEM_TOL, f"EMA tensor {i}: {err:.3e}"
+    gu.say(f"[parity] EMA over {len(E)} tensors, worst rel err {worst:.2e}")
+
+
+def test_full_model_512d_with_ema():
+    w, st, w_gpu = _run_workload(2, wl.PRIMARY_SEED, o_sample=ONE_PER_SHAPE)
+    _check_ema(w, st, w_gpu, w.ema_decay)
+
+
+def test_full_model_1024d_with_ema():
+    w, st, w_gpu = _run_workload(3, wl.PRIMARY_SEED, o_sample={0, 7, 28, 35})
+    _check_ema(w, st, w_gpu, w.ema_decay)
+
+
+def test_structured_gradients_ten_steps():
+    """Rank-8 + noise gradients, drawn 4-step table, momentum and EMA carried over 10 steps.
+
+    Each step is checked layer by layer against the oracle fed the GPU's state
+    from the step before (the momentum chain is exact fp32, the NS error is
+    re-measured every step on sampled matrices).  The drift of W after ten
+    steps relative to a pure-oracle run is reported too.
+    """
+    import torch
+    import muon_optimizer_step_amd as ms
+    w = wl.workload(4)
+    seed = wl.PRIMARY_SEED
+    st = wl.make_state(w, seed)
+    coeffs = wl.coeff_table(w, seed)
+    nm = len(w.matrices)
+    P = [gu.dev(p) for p in st["params"]]
+    M = [gu.dev(m) for m in st["moms"]]
+    E = [gu.dev(e) for e in st["ema"]]
+    O = [torch.empty_like(p) for p in P[:nm]]
+    sample = [1, 16, 40, 65]
+    ref_w = {i: st["params"][i].astype(np.float64) for i in sample}
+    ref_m = {i: st["moms"][i].astype(np.float64) for i in sample}
+    for step in range(w.steps):
+        gu.say(f"[parity] structured step {step}")
+        grads = wl.make_grads(w, seed, step)
+        w_in = [gu.host(p) for p in P[:nm]]
+        m_in = [gu.host(m) for m in M]
+        e_in = [gu.host(e) for e in E]
+        G = [gu.dev(g) for g in grads]
+        ms.muon_step(P[:nm], G, M, lr=w.lr, momentum=w.momentum, weight_decay=w.weight_decay,
+                     coeffs=coeffs.tolist(), nesterov=True, row_norm=True, update_outs=O)
+        ms.ema_update(E, P, w.ema_decay)
+        torch.cuda.synchronize()
+        w_out = [gu.host(p) for p in P[:nm]]
+        worst = 0.0
+        for i in range(nm):
+            e = gu.check_layers(w_in[i], grads[i], m_in[i], w_out[i], gu.host(M[i]), gu.host(O[i]), lr=w.lr,
+                                momentum=w.momentum, wd=w.weight_decay, coeffs=coeffs, nesterov=True,
+                                row_norm=True, ns_tol=gu.NS_TOL_BF16, check_o=i in sample,
+                                label=f"step {step} {w.matrices[i][0]}")
+            if e is not None:
+                worst = max(worst, e)
+        post = w_out + [gu.host(p) for p in P[nm:]]
+        for i, e in enumerate(E):
+            err = gu.rel_max(gu.host(e), om.ema_update(e_in[i], post[i], gu.f32(w.ema_decay)))
+            assert err <= gu.ELEM_TOL, f"step {step} EMA tensor {i}: {err:.3e}"
+        for i in sample:  # independent pure-oracle trajectory for the drift report
+            ref_w[i], ref_m[i], _ = om.muon_step_matrix(
+                ref_w[i], grads[i], ref_m[i], lr=gu.f32(w.lr), mu=gu.f32(w.momentum), nesterov=True,
+                wd=gu.f32(w.weight_decay), row_norm=True, coeffs=coeffs.astype(np.float64))
+        gu.say(f"[parity] structured step {step}: worst sampled NS err {worst:.2e}")
+    drift = max(gu.rel_frob(gu.host(P[i]) - st["params"][i], ref_w[i] - st["params"][i]) for i in sample)
+    gu.say(f"[parity] structured: relative drift of the 10-step weight change vs oracle {drift:.2e}")
+    assert drift <= gu.NS_TOL_BF16
+
+
+@pytest.mark.parametrize("ns_precision", [0, 1])
+@pytest.mark.parametrize("nesterov,row_norm", [(True, True), (False, False), (True, False)])
+def test_ragged_shapes(ns_precision, nesterov, row_norm):
+    """Odd shapes (wide, tall, square, 1-row, 1-col) leave ragged tails in every tiling."""
+    shapes = wl.small_ragged_matrices()
+    rng = np.random.default_rng(99)
+    mats = [(0.02 * rng.standard_normal((r, c))).astype(np.float32) for _, r, c in shapes]
+    grads = [rng.standard_normal((r, c)).astype(np.float32) for _, r, c in shapes]
+    moms = [(0.5 * rng.standard_normal((r, c))).astype(np.float32) for _, r, c in shapes]
+    coeffs = wl.coeff_table(wl.workload(4), 5).tolist()
+    gu.say(f"[parity] ragged shapes prec={ns_precision} nesterov={nesterov} row_norm={row_norm}")
+    w_gpu, m_gpu, o_gpu = gu.gpu_step(mats, grads, moms, lr=0.05, momentum=0.9, wd=0.1, coeffs=coeffs,
+                                      nesterov=nesterov, row_norm=row_norm, ns_precision=ns_precision)
+    tol = gu.NS_TOL_BF16 if ns_precision == 0 else gu.NS_TOL_FP32
+    for i, (nm, r, c) in enumerate(shapes):
+        gu.check_layers(mats[i], grads[i], moms[i], w_gpu[i], m_gpu[i], o_gpu[i], lr=0.05, momentum=0.9, wd=0.1,
+                        coeffs=coeffs, nesterov=nesterov, row_norm=row_norm, ns_tol=tol, label=f"{nm} {r}x{c}")

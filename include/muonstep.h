@@ -58,8 +58,9 @@ extern "C" {
 #define MUON_MAX_LONG_SIDE 65536    /* max(rows, cols) of a Muon matrix, at most */
 #define MUON_MAX_TENSORS 4096       /* tensors per call, at most */
 
-#define MUON_NS_BF16 0              /* NS products on bf16 MFMA, fp32 accumulation */
+#define MUON_NS_BF16 0              /* bf16 MFMA, fp32 accumulation; compensated below a short side of 192 */
 #define MUON_NS_FP32 1              /* NS products on fp32 MFMA */
+#define MUON_NS_BF16X3 2            /* bf16 MFMA with hi/lo compensation in every product */
 
 /* One Muon matrix.  param and momentum are updated in place; grad is read only.
  * update_out is optional (NULL to skip): when set, the orthogonalised update O
@@ -87,7 +88,14 @@ size_t muon_workspace_size(const muon_tensor_t* tensors, int32_t n, int32_t ns_p
  *   ns_steps      0 <= ns_steps <= MUON_MAX_NS_STEPS; 0 gives O = X0.
  *   ns_coeffs     host array of ns_steps rows (a_k, b_k, c_k), row-major,
  *                 finite; may be NULL only when ns_steps == 0.
- *   ns_precision  MUON_NS_BF16 or MUON_NS_FP32.
+ *   ns_precision  MUON_NS_BF16, MUON_NS_FP32 or MUON_NS_BF16X3.  Every NS
+ *                 product runs on MFMA with fp32 accumulation; X is carried to
+ *                 ~16 significant bits (bf16 hi + lo) or in fp32.  MUON_NS_BF16
+ *                 forms X X^T and B X from the bf16 hi parts only (and A A from
+ *                 hi*hi + hi*lo + lo*hi) for matrices whose short side is at
+ *                 least 192, and the compensated products (hi*hi + hi*lo +
+ *                 lo*hi everywhere) below that; MUON_NS_BF16X3 compensates every
+ *                 matrix.
  *   workspace     device buffer of at least muon_workspace_size(...) bytes,
  *                 256-byte aligned; its contents on entry do not matter.
  *   stream        hipStream_t to enqueue on.

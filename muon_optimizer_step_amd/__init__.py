@@ -6,7 +6,7 @@ Every step of the computation runs in the library's HIP kernels.
 """
 
 from ._lib import (  # noqa: F401
-    MUON_NS_BF16, MUON_NS_FP32, MuonError, LIB_PATH, load,
+    MUON_NS_BF16, MUON_NS_FP32, MUON_NS_BF16X3, MuonError, LIB_PATH, load,
 )
 from .api import (  # noqa: F401
     muon_step, ema_update, workspace_size, profile_enable, profile_read, version,

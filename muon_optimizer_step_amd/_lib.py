@@ -18,6 +18,7 @@ MUON_MAX_LONG_SIDE = 65536
 MUON_MAX_TENSORS = 4096
 MUON_NS_BF16 = 0
 MUON_NS_FP32 = 1
+MUON_NS_BF16X3 = 2
 
 
 class MuonTensor(ctypes.Structure):

@@ -99,7 +99,8 @@ struct Group {
     int m, n;        // short side, long side
     int M, N;        // padded
     int count = 0;
-    size_t x_off[2], xl_off[2], ah_off, al_off, b_off;
+    size_t x_off[2], xl_off[2], ah_off, al_off, b_off, bl_off;
+    bool comp = false;    // run the compensated bf16 products
     int scale_begin = 0;  // index of slot 0 in the scale array
 };
 
@@ -119,7 +120,9 @@ int transposed_rb(int cols) {
     return rb;
 }
 
-void make_plan(const muon_tensor_t* t, int n, int precision, Plan& p) {
+// mode: the ns_precision argument.  Storage is bf16 hi/lo planes except in fp32 mode.
+void make_plan(const muon_tensor_t* t, int n, int mode, Plan& p) {
+    const int precision = mode == kModeFp32 ? kNsFp32 : kNsBf16;
     std::map<std::pair<int, int>, int> index;
     p.group_of.resize(n);
     p.slot_of.resize(n);
@@ -138,6 +141,7 @@ void make_plan(const muon_tensor_t* t, int n, int precision, Plan& p) {
             G.n = nn;
             G.M = pad_to_tile(m);
             G.N = pad_to_tile(nn);
+            G.comp = mode == kModeBf16x3 || (mode == kModeBf16 && m < kCompensateBelow);
             p.groups.push_back(G);
         } else {
             g = it->second;
@@ -162,6 +166,7 @@ void make_plan(const muon_tensor_t* t, int n, int precision, Plan& p) {
         G.ah_off = off; off += aplane;
         if (precision == kNsBf16) { G.al_off = off; off += aplane; } else { G.al_off = G.ah_off; }
         G.b_off = off; off += aplane;
+        if (precision == kNsBf16) { G.bl_off = off; off += aplane; } else { G.bl_off = G.b_off; }
     }
     int scale_count = 0;
     for (Group& G : p.groups) { G.scale_begin = scale_count; scale_count += G.count; }
@@ -191,8 +196,8 @@ int check_overlaps(std::vector<Span>& spans, const char* what) {
 int validate_tensors(const muon_tensor_t* t, int32_t n, int32_t precision) {
     if (!t) return fail(MUON_ERR_INVALID_ARG, "tensors is NULL");
     if (n <= 0 || n > MUON_MAX_TENSORS) return fail(MUON_ERR_INVALID_ARG, "n = %d outside [1, %d]", n, MUON_MAX_TENSORS);
-    if (precision != MUON_NS_BF16 && precision != MUON_NS_FP32)
-        return fail(MUON_ERR_INVALID_ARG, "ns_precision = %d is neither MUON_NS_BF16 nor MUON_NS_FP32", precision);
+    if (precision != MUON_NS_BF16 && precision != MUON_NS_FP32 && precision != MUON_NS_BF16X3)
+        return fail(MUON_ERR_INVALID_ARG, "ns_precision = %d is not MUON_NS_BF16, MUON_NS_FP32 or MUON_NS_BF16X3", precision);
     for (int i = 0; i < n; ++i) {
         const muon_tensor_t& x = t[i];
         if (x.rows <= 0 || x.cols <= 0)
@@ -284,7 +289,7 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     float* rowsq = reinterpret_cast<float*>(ws + p.rowsq_base);
-    const int prec = ns_precision;
+    const int prec = ns_precision == MUON_NS_FP32 ? kNsFp32 : kNsBf16;  // storage precision
     hipError_t err;
 
     // ---- prep: momentum, row norm, X0 (short side first, zero padded)
@@ -345,41 +350,48 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
         if (err != hipSuccess) return fail(MUON_ERR_HIP, "frob launch failed: %s", hipGetErrorString(err));
     }
 
-    // ---- Newton-Schulz iterations
+    // ---- Newton-Schulz iterations: per phase, one launch for the base groups and
+    // one for the compensated groups (each skipped when empty)
     const int ngroups = (int)p.groups.size();
     for (int k = 0; k < ns_steps; ++k) {
         for (int phase = kGram; phase <= kUpdate; ++phase) {
-            for (int g0 = 0; g0 < ngroups; g0 += kMaxGroups) {
-                NsArgs a;
-                memset(&a, 0, sizeof(a));
-                a.src = k & 1;
-                a.first = (k == 0);
-                a.a = ns_coeffs[3 * k + 0];
-                a.b = ns_coeffs[3 * k + 1];
-                a.c = ns_coeffs[3 * k + 2];
-                int jobs = 0;
-                for (int g = g0; g < std::min(ngroups, g0 + kMaxGroups); ++g) {
-                    const Group& G = p.groups[g];
-                    NsGroup& D = a.g[a.ngroups++];
-                    for (int b = 0; b < 2; ++b) {
-                        D.x[b] = ws + G.x_off[b];
-                        D.xl[b] = ws + G.xl_off[b];
+            for (int comp = 0; comp < 2; ++comp) {
+                std::vector<int> gl;
+                for (int g = 0; g < ngroups; ++g)
+                    if ((int)p.groups[g].comp == comp) gl.push_back(g);
+                for (size_t g0 = 0; g0 < gl.size(); g0 += kMaxGroups) {
+                    NsArgs a;
+                    memset(&a, 0, sizeof(a));
+                    a.src = k & 1;
+                    a.first = (k == 0);
+                    a.a = ns_coeffs[3 * k + 0];
+                    a.b = ns_coeffs[3 * k + 1];
+                    a.c = ns_coeffs[3 * k + 2];
+                    int jobs = 0;
+                    for (size_t q = g0; q < std::min(gl.size(), g0 + kMaxGroups); ++q) {
+                        const Group& G = p.groups[gl[q]];
+                        NsGroup& D = a.g[a.ngroups++];
+                        for (int b = 0; b < 2; ++b) {
+                            D.x[b] = ws + G.x_off[b];
+                            D.xl[b] = ws + G.xl_off[b];
+                        }
+                        D.a_hi = ws + G.ah_off;
+                        D.a_lo = ws + G.al_off;
+                        D.b = ws + G.b_off;
+                        D.b_lo = ws + G.bl_off;
+                        D.scale = reinterpret_cast<const float*>(ws + p.scale_base) + G.scale_begin;
+                        D.count = G.count;
+                        D.M = G.M;
+                        D.N = G.N;
+                        D.job_begin = jobs;
+                        const int tm = G.M / kTile, tn = G.N / kTile;
+                        jobs += G.count * (phase == kUpdate ? tm * tn : tm * (tm + 1) / 2);
                     }
-                    D.a_hi = ws + G.ah_off;
-                    D.a_lo = ws + G.al_off;
-                    D.b = ws + G.b_off;
-                    D.scale = reinterpret_cast<const float*>(ws + p.scale_base) + G.scale_begin;
-                    D.count = G.count;
-                    D.M = G.M;
-                    D.N = G.N;
-                    D.job_begin = jobs;
-                    const int tm = G.M / kTile, tn = G.N / kTile;
-                    jobs += G.count * (phase == kUpdate ? tm * tn : tm * (tm + 1) / 2);
+                    a.total_jobs = jobs;
+                    const char* name = ns_kernel_name(phase, prec, comp != 0);
+                    err = timed_launch(name, s, [&] { return launch_ns(a, phase, prec, comp != 0, s); });
+                    if (err != hipSuccess) return fail(MUON_ERR_HIP, "%s launch failed: %s", name, hipGetErrorString(err));
                 }
-                a.total_jobs = jobs;
-                err = timed_launch(ns_kernel_name(phase, prec), s, [&] { return launch_ns(a, phase, prec, s); });
-                if (err != hipSuccess)
-                    return fail(MUON_ERR_HIP, "%s launch failed: %s", ns_kernel_name(phase, prec), hipGetErrorString(err));
             }
         }
     }

@@ -56,7 +56,8 @@ struct NsGroup {
     void* xl[2];     // bf16: lo planes; fp32: unused
     void* a_hi;      // bf16: hi of A; fp32: A.  [count][M][M]
     void* a_lo;      // bf16: lo of A; fp32: unused
-    void* b;         // bf16: B rounded; fp32: B.  [count][M][M]
+    void* b;         // bf16: hi of B; fp32: B.  [count][M][M]
+    void* b_lo;      // bf16: lo of B (written and read by the compensated kernels)
     const float* scale;  // [count] Frobenius scale of X0
     int count, M, N;     // padded, multiples of 128
     int job_begin;
@@ -71,6 +72,7 @@ struct NsArgs {
 };
 
 enum NsPhase { kGram = 0, kSquare = 1, kUpdate = 2 };
+enum NsMode { kModeBf16 = 0, kModeFp32 = 1, kModeBf16x3 = 2 };  // the ns_precision argument
 
 // ------------------------------------------------------------- apply (K3)
 struct ApplyTensor {
@@ -120,10 +122,15 @@ static_assert(sizeof(EmaArgs) <= 4096, "EMA kernel arguments exceed 4 KiB");
 // Launchers: enqueue on `s`, return hipGetLastError() of the launch.
 hipError_t launch_prep(const PrepArgs& a, int precision, int blocks, size_t lds_bytes, hipStream_t s);
 hipError_t launch_frob(const FrobArgs& a, hipStream_t s);
-hipError_t launch_ns(const NsArgs& a, int phase, int precision, hipStream_t s);
+hipError_t launch_ns(const NsArgs& a, int phase, int precision, bool compensated, hipStream_t s);
 hipError_t launch_apply(const ApplyArgs& a, int precision, int blocks, size_t lds_bytes, hipStream_t s);
 hipError_t launch_ema(const EmaArgs& a, int blocks, hipStream_t s);
 
-const char* ns_kernel_name(int phase, int precision);
+const char* ns_kernel_name(int phase, int precision, bool compensated);
+
+// Short side below which the bf16 precision runs the compensated products:
+// with fewer singular values the bf16 rounding of the base products no longer
+// averages out and the error can pass 2e-2.
+constexpr int kCompensateBelow = 192;
 
 }  // namespace muon

@@ -9,22 +9,28 @@
 //     X <- a X + B X       (kUpdate, m x n, contraction over m)
 // with X short-side-first (m <= n).
 //
-// bf16 numerics: X is kept to ~16 significant bits as a pair of bf16 planes
+// bf16 numerics.  X is kept to ~16 significant bits as two bf16 planes
 // (hi = rne(X), lo = rne(X - hi)); MFMA operands are bf16 and accumulate in
-// fp32.  A is likewise split, and A A is formed as hi*hi + hi*lo + lo*hi,
+// fp32.  A is split the same way and A A is formed as hi*hi + hi*lo + lo*hi,
 // because the plain bf16 square loses the small singular directions that the
-// iteration amplifies.  The a X term uses hi + lo.  The fp32 precision runs the
-// same three phases on fp32 MFMA (v_mfma_f32_32x32x2_f32).
+// iteration amplifies; the a X term always uses hi + lo.
+//   base:        A = Xh Xh^T,  B X = Bh Xh
+//   compensated: A = Xh Xh^T + Xh Xl^T + Xl Xh^T,  B X = Bh Xh + Bl Xh + Bh Xl
+// The base products keep the error within 2e-2 of float64 once the short side
+// has enough singular values to average the bf16 rounding (>= 192); smaller
+// groups, or every group on request, run compensated (~1e-4).  The fp32
+// precision runs the same phases on fp32 MFMA (v_mfma_f32_32x32x2_f32).
 //
-// Tiling: one workgroup (4 wave64s, 2 x 2) per 128 x 128 output tile, 64 x 64
-// per wave as 2 x 2 v_mfma_f32_32x32x16_bf16 accumulators; K is staged through
-// LDS 128 bytes per row at a time (64 bf16 or 32 fp32), with the next stage's
-// global loads in flight during the MFMAs.  A and B are symmetric: only tiles
-// with ti <= tj are computed and each is also written mirrored.  All work of
-// one phase for every matrix of every shape group is one launch; job indices
-// are remapped so that the tiles of one matrix share an XCD (and its L2).
-// Workspace dimensions are padded to 128 with zeros, which the iteration keeps
-// at zero, so the inner loops need no bounds checks.
+// Tiling.  One workgroup (4 wave64s, 2 x 2) per 128 x 128 output tile, 64 x 64
+// per wave as 2 x 2 v_mfma_f32_32x32x16_bf16 accumulators.  K is staged
+// through LDS 128 bytes per row at a time (64 bf16 or 32 fp32) with the next
+// stage's global loads in flight during the MFMAs.  A and B are symmetric:
+// only tiles with ti <= tj are computed and each is written twice (as is and
+// mirrored).  Epilogues go through LDS so that every global access is 16
+// bytes wide.  All work of one phase for every matrix of every shape group is
+// one launch; job indices are remapped so that the tiles of one matrix share
+// an XCD (and its L2).  Workspace dimensions are padded to 128 with zeros,
+// which the iteration keeps at zero, so no loop needs a bounds check.
 #include "common.h"
 #include "kernels.h"
 
@@ -36,6 +42,9 @@ constexpr int kThreads = 256;
 constexpr int kRowBytes = 128;              // K bytes per LDS stage per row
 constexpr int kPitch = kRowBytes + 16;      // padded LDS row pitch (conflict-free b128 reads)
 constexpr int kTileBytes = kTile * kPitch;  // one 128-row operand tile
+constexpr int kStagePitch = kTile + 4;      // fp32 epilogue staging row pitch
+constexpr int kStageBytes = 64 * kStagePitch * 4;  // half a tile (64 rows) of fp32
+static_assert(kStageBytes <= 2 * kTileBytes, "epilogue staging must fit in the operand LDS");
 
 template <int PREC> struct Elem;
 template <> struct Elem<kNsBf16> { typedef bf16 T; static constexpr int kBK = 64; };
@@ -99,7 +108,7 @@ template <> struct TLoader<kNsBf16> {
         const int jq = t % 32, kb = t / 32;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            // column c of the 8 x 4 block: element c of every k-row, packed two k per dword
+            // column c of the 8 x 4 block: element c of every k-row, two k per dword
             const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
             u32x4 w;
 #pragma unroll
@@ -138,10 +147,6 @@ __device__ inline u32x4 lds_frag(const uint8_t* tile, int row, int kc, int lane)
     return *reinterpret_cast<const u32x4*>(tile + row * kPitch + kc * 32 + (lane / 32) * 16);
 }
 
-// acc element (mi, ni, r) -> tile-local (row, col) for the 32x32 MFMA layout.
-__device__ inline int acc_row(int wm, int mi, int r, int lane) { return wm * 64 + mi * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4); }
-__device__ inline int acc_col(int wn, int ni, int lane) { return wn * 64 + ni * 32 + (lane % 32); }
-
 struct Job {
     int g, slot, ti, tj;
 };
@@ -174,11 +179,55 @@ __device__ inline bool decode_job(const NsArgs& args, Job& j) {
     return true;
 }
 
-template <int PHASE, int PREC>
+// 8 consecutive elements of a plane <-> 8 floats.
+template <int PREC>
+__device__ inline void load8(const void* plane, size_t idx, float* v) {
+    if constexpr (PREC == kNsBf16) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(plane) + idx);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            v[2 * p] = from_bf16(bits_bf16(w[p] & 0xFFFFu));
+            v[2 * p + 1] = from_bf16(bits_bf16(w[p] >> 16));
+        }
+    } else {
+        const floatx4* s = reinterpret_cast<const floatx4*>(static_cast<const float*>(plane) + idx);
+        const floatx4 a = s[0], b = s[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
+    }
+}
+
+// Store 8 values: bf16 -> hi plane (and lo plane when lo != nullptr); fp32 -> plane `hi`.
+template <int PREC>
+__device__ inline void store8(void* hi, void* lo, size_t idx, const float* v) {
+    if constexpr (PREC == kNsBf16) {
+        u32x4 wh, wl;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            bf16 h0, l0, h1, l1;
+            split_bf16(v[2 * p], h0, l0);
+            split_bf16(v[2 * p + 1], h1, l1);
+            wh[p] = bf16_bits(h0) | (bf16_bits(h1) << 16);
+            wl[p] = bf16_bits(l0) | (bf16_bits(l1) << 16);
+        }
+        *reinterpret_cast<u32x4*>(static_cast<bf16*>(hi) + idx) = wh;
+        if (lo) *reinterpret_cast<u32x4*>(static_cast<bf16*>(lo) + idx) = wl;
+    } else {
+        floatx4 a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { a[e] = v[e]; b[e] = v[4 + e]; }
+        floatx4* d = reinterpret_cast<floatx4*>(static_cast<float*>(hi) + idx);
+        d[0] = a;
+        d[1] = b;
+    }
+}
+
+template <int PHASE, int PREC, bool COMP>
 __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
     typedef typename Elem<PREC>::T T;
     constexpr int kBK = Elem<PREC>::kBK;
-    constexpr bool kSplitSquare = (PHASE == kSquare && PREC == kNsBf16);
+    // operands carry a lo plane (and the MFMAs run hi*hi + hi*lo + lo*hi)
+    constexpr bool kSplit = (PREC == kNsBf16) && (PHASE == kSquare || COMP);
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     Job job;
@@ -191,38 +240,45 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
 
     const size_t xplane = (size_t)job.slot * M * N;
     const size_t aplane = (size_t)job.slot * M * M;
-    const T* x_src = static_cast<const T*>(G.x[args.src]) + xplane;
+    const int src = args.src;
 
-    // Operand tiles in LDS: [0] A-operand (rows ti), [1] B-operand (rows tj),
-    // and for the split square [2] lo of rows ti, [3] lo of rows tj.
+    // LDS operand tiles: [0] hi of the A-side rows, [1] hi of the B-side rows,
+    // [2] / [3] the lo planes.  On diagonal tiles both sides are the same rows.
     uint8_t* t_a = lds;
     uint8_t* t_b = diag ? lds : lds + kTileBytes;
     uint8_t* t_al = lds + 2 * kTileBytes;
     uint8_t* t_bl = diag ? t_al : lds + 3 * kTileBytes;
 
     const uint8_t *ga = nullptr, *gb = nullptr, *gal = nullptr, *gbl = nullptr;
+    const T *xb = nullptr, *xbl = nullptr;  // update: B-side X planes
     size_t ld_bytes = 0;
     int K = 0;
     if (PHASE == kGram) {
+        const T* xh = static_cast<const T*>(G.x[src]) + xplane;
+        const T* xl = static_cast<const T*>(G.xl[src]) + xplane;
         ld_bytes = (size_t)N * sizeof(T);
-        ga = reinterpret_cast<const uint8_t*>(x_src + (size_t)job.ti * kTile * N);
-        gb = reinterpret_cast<const uint8_t*>(x_src + (size_t)job.tj * kTile * N);
+        ga = reinterpret_cast<const uint8_t*>(xh + (size_t)job.ti * kTile * N);
+        gb = reinterpret_cast<const uint8_t*>(xh + (size_t)job.tj * kTile * N);
+        gal = reinterpret_cast<const uint8_t*>(xl + (size_t)job.ti * kTile * N);
+        gbl = reinterpret_cast<const uint8_t*>(xl + (size_t)job.tj * kTile * N);
         K = N;
     } else if (PHASE == kSquare) {
         const T* ah = static_cast<const T*>(G.a_hi) + aplane;
+        const T* al = static_cast<const T*>(G.a_lo) + aplane;
         ld_bytes = (size_t)M * sizeof(T);
         ga = reinterpret_cast<const uint8_t*>(ah + (size_t)job.ti * kTile * M);
         gb = reinterpret_cast<const uint8_t*>(ah + (size_t)job.tj * kTile * M);
-        if (kSplitSquare) {
-            const T* al = static_cast<const T*>(G.a_lo) + aplane;
-            gal = reinterpret_cast<const uint8_t*>(al + (size_t)job.ti * kTile * M);
-            gbl = reinterpret_cast<const uint8_t*>(al + (size_t)job.tj * kTile * M);
-        }
+        gal = reinterpret_cast<const uint8_t*>(al + (size_t)job.ti * kTile * M);
+        gbl = reinterpret_cast<const uint8_t*>(al + (size_t)job.tj * kTile * M);
         K = M;
     } else {
-        const T* bm = static_cast<const T*>(G.b) + aplane;
+        const T* bh = static_cast<const T*>(G.b) + aplane;
+        const T* bl = static_cast<const T*>(G.b_lo) + aplane;
         ld_bytes = (size_t)M * sizeof(T);
-        ga = reinterpret_cast<const uint8_t*>(bm + (size_t)job.ti * kTile * M);
+        ga = reinterpret_cast<const uint8_t*>(bh + (size_t)job.ti * kTile * M);
+        gal = reinterpret_cast<const uint8_t*>(bl + (size_t)job.ti * kTile * M);
+        xb = static_cast<const T*>(G.x[src]) + xplane;
+        xbl = static_cast<const T*>(G.xl[src]) + xplane;
         K = M;
     }
 
@@ -235,30 +291,28 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
             for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
     NtLoader la, lb, lal, lbl;
-    TLoader<PREC> lt;
+    TLoader<PREC> lt, ltl;
     auto issue = [&](int k0) {
         const int kbyte = k0 * (int)sizeof(T);
         la.load(ga, ld_bytes, kbyte);
+        if (kSplit) lal.load(gal, ld_bytes, kbyte);
         if (PHASE == kUpdate) {
-            lt.load(x_src, (size_t)N, k0, job.tj * kTile);
-        } else {
-            if (!diag) lb.load(gb, ld_bytes, kbyte);
-            if (kSplitSquare) {
-                lal.load(gal, ld_bytes, kbyte);
-                if (!diag) lbl.load(gbl, ld_bytes, kbyte);
-            }
+            lt.load(xb, (size_t)N, k0, job.tj * kTile);
+            if (kSplit) ltl.load(xbl, (size_t)N, k0, job.tj * kTile);
+        } else if (!diag) {
+            lb.load(gb, ld_bytes, kbyte);
+            if (kSplit) lbl.load(gbl, ld_bytes, kbyte);
         }
     };
     auto commit = [&]() {
         la.store(t_a);
+        if (kSplit) lal.store(t_al);
         if (PHASE == kUpdate) {
             lt.store(t_b);
-        } else {
-            if (!diag) lb.store(t_b);
-            if (kSplitSquare) {
-                lal.store(t_al);
-                if (!diag) lbl.store(t_bl);
-            }
+            if (kSplit) ltl.store(t_bl);
+        } else if (!diag) {
+            lb.store(t_b);
+            if (kSplit) lbl.store(t_bl);
         }
     };
 
@@ -280,7 +334,7 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
             for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < 2; ++ni) mfma_chunk<PREC>(acc[mi][ni], fa[mi], fb[ni]);
-            if (kSplitSquare) {
+            if (kSplit) {
                 u32x4 fal[2], fbl[2];
 #pragma unroll
                 for (int mi = 0; mi < 2; ++mi) fal[mi] = lds_frag(t_al, wm * 64 + mi * 32 + lane % 32, kc, lane);
@@ -297,158 +351,141 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
         }
     }
 
-    // ------------------------------------------------------------ epilogues
+    // ---------------------------------------------------------- epilogue
+    // Two passes of 64 rows: the waves holding those rows park their fp32
+    // accumulators in LDS, then all threads finish 8 consecutive columns of a
+    // row each with 16-byte global accesses, and symmetric outputs also write
+    // the mirrored tile from the staged columns.
+    float* stage = reinterpret_cast<float*>(lds);
     const float s = G.scale[job.slot];
-    if (PHASE == kGram) {
-        const float sc = args.first ? s * s : 1.0f;
-        T* ah = static_cast<T*>(G.a_hi) + aplane;
-        T* al = static_cast<T*>(G.a_lo) + aplane;
+    const float sc = (PHASE == kGram) ? (args.first ? s * s : 1.0f) : (args.first ? s : 1.0f);
+    const int t = threadIdx.x;
+    for (int h = 0; h < 2; ++h) {
+        __syncthreads();
+        if (wm == h) {
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
+            for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni) {
-                const int col = job.tj * kTile + acc_col(wn, ni, lane);
+                for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int row0 = job.ti * kTile + acc_row(wm, mi, 4 * q, lane);
-                    T hv[4], lv[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float v = acc[mi][ni][4 * q + e] * sc;
-                        if constexpr (PREC == kNsBf16) {
-                            split_bf16(v, hv[e], lv[e]);
-                            ah[(size_t)(row0 + e) * M + col] = hv[e];
-                            al[(size_t)(row0 + e) * M + col] = lv[e];
-                        } else {
-                            hv[e] = v;
-                            ah[(size_t)(row0 + e) * M + col] = v;
-                        }
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = mi * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+                        const int col = wn * 64 + ni * 32 + (lane % 32);
+                        stage[row * kStagePitch + col] = acc[mi][ni][r];
                     }
-                    if (job.ti != job.tj) {
-                        // mirror: A[col][row0..row0+3] is contiguous
-                        if constexpr (PREC == kNsBf16) {
-                            u32x2 ph, pl;
-                            ph.x = bf16_bits(hv[0]) | (bf16_bits(hv[1]) << 16);
-                            ph.y = bf16_bits(hv[2]) | (bf16_bits(hv[3]) << 16);
-                            pl.x = bf16_bits(lv[0]) | (bf16_bits(lv[1]) << 16);
-                            pl.y = bf16_bits(lv[2]) | (bf16_bits(lv[3]) << 16);
-                            *reinterpret_cast<u32x2*>(ah + (size_t)col * M + row0) = ph;
-                            *reinterpret_cast<u32x2*>(al + (size_t)col * M + row0) = pl;
-                        } else {
-                            floatx4 pv;
-                            pv[0] = hv[0]; pv[1] = hv[1]; pv[2] = hv[2]; pv[3] = hv[3];
-                            *reinterpret_cast<floatx4*>(ah + (size_t)col * M + row0) = pv;
-                        }
-                    }
-                }
+        }
+        __syncthreads();
+        const int row_base = job.ti * kTile + h * 64;
+        // row pass: thread -> (row t/16 + 16p, columns 8*(t%16) .. +7)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int lr = t / 16 + 16 * p;
+            const int lc = 8 * (t % 16);
+            float* sp = stage + lr * kStagePitch + lc;
+            float v[8];
+            {
+                const floatx4 a = *reinterpret_cast<const floatx4*>(sp);
+                const floatx4 b = *reinterpret_cast<const floatx4*>(sp + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
             }
-    } else if (PHASE == kSquare) {
-        const T* ah = static_cast<const T*>(G.a_hi) + aplane;
-        const T* al = static_cast<const T*>(G.a_lo) + aplane;
-        T* bm = static_cast<T*>(G.b) + aplane;
-        const float cb = args.b, cc = args.c;
+            if (PHASE == kGram) {
+                const size_t idx = (size_t)(row_base + lr) * M + job.tj * kTile + lc;
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
+                for (int e = 0; e < 8; ++e) v[e] *= sc;
+                store8<PREC>(static_cast<T*>(G.a_hi) + aplane, static_cast<T*>(G.a_lo) + aplane, idx, v);
+            } else if (PHASE == kSquare) {
+                const size_t idx = (size_t)(row_base + lr) * M + job.tj * kTile + lc;
+                float ah[8], al[8];
+                load8<PREC>(static_cast<const T*>(G.a_hi) + aplane, idx, ah);
+                if constexpr (PREC == kNsBf16) load8<PREC>(static_cast<const T*>(G.a_lo) + aplane, idx, al);
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni) {
-                const int col = job.tj * kTile + acc_col(wn, ni, lane);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int row0 = job.ti * kTile + acc_row(wm, mi, 4 * q, lane);
-                    T bv[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const size_t idx = (size_t)(row0 + e) * M + col;
-                        float a;
-                        if constexpr (PREC == kNsBf16) a = from_bf16(ah[idx]) + from_bf16(al[idx]);
-                        else a = ah[idx];
-                        const float v = fmaf(cb, a, cc * acc[mi][ni][4 * q + e]);
-                        bv[e] = (T)v;
-                        bm[idx] = bv[e];
-                    }
-                    if (job.ti != job.tj) {
-                        if constexpr (PREC == kNsBf16) {
-                            u32x2 pb;
-                            pb.x = bf16_bits(bv[0]) | (bf16_bits(bv[1]) << 16);
-                            pb.y = bf16_bits(bv[2]) | (bf16_bits(bv[3]) << 16);
-                            *reinterpret_cast<u32x2*>(bm + (size_t)col * M + row0) = pb;
-                        } else {
-                            floatx4 pv;
-                            pv[0] = bv[0]; pv[1] = bv[1]; pv[2] = bv[2]; pv[3] = bv[3];
-                            *reinterpret_cast<floatx4*>(bm + (size_t)col * M + row0) = pv;
-                        }
-                    }
+                for (int e = 0; e < 8; ++e) {
+                    const float a = (PREC == kNsBf16) ? ah[e] + al[e] : ah[e];
+                    v[e] = fmaf(args.b, a, args.c * v[e]);
                 }
-            }
-    } else {
-        const float sc = args.first ? s : 1.0f;
-        const float ca = args.a;
-        const int dst = args.src ^ 1;
-        const T* xh = x_src;
-        const bf16* xl = static_cast<const bf16*>(G.xl[args.src]) + xplane;
-        T* yh = static_cast<T*>(G.x[dst]) + xplane;
-        bf16* yl = static_cast<bf16*>(G.xl[dst]) + xplane;
+                store8<PREC>(static_cast<T*>(G.b) + aplane, COMP ? static_cast<T*>(G.b_lo) + aplane : nullptr, idx, v);
+            } else {
+                const size_t idx = xplane + (size_t)(row_base + lr) * N + job.tj * kTile + lc;
+                float xh[8], xl[8];
+                load8<PREC>(G.x[src], idx, xh);
+                if constexpr (PREC == kNsBf16) load8<PREC>(G.xl[src], idx, xl);
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < 2; ++ni) {
-                const int col = job.tj * kTile + acc_col(wn, ni, lane);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = job.ti * kTile + acc_row(wm, mi, r, lane);
-                    const size_t idx = (size_t)row * N + col;
-                    float x;
-                    if constexpr (PREC == kNsBf16) x = from_bf16(xh[idx]) + from_bf16(xl[idx]);
-                    else x = xh[idx];
-                    const float v = sc * fmaf(ca, x, acc[mi][ni][r]);
-                    if constexpr (PREC == kNsBf16) {
-                        bf16 h, l;
-                        split_bf16(v, h, l);
-                        yh[idx] = h;
-                        yl[idx] = l;
-                    } else {
-                        yh[idx] = v;
-                    }
+                for (int e = 0; e < 8; ++e) {
+                    const float x = (PREC == kNsBf16) ? xh[e] + xl[e] : xh[e];
+                    v[e] = sc * fmaf(args.a, x, v[e]);
                 }
+                store8<PREC>(G.x[src ^ 1], G.xl[src ^ 1], idx, v);
             }
+            if (PHASE != kUpdate && !diag) {
+                // keep the final value for the mirrored write
+                floatx4 a, b;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { a[e] = v[e]; b[e] = v[4 + e]; }
+                *reinterpret_cast<floatx4*>(sp) = a;
+                *reinterpret_cast<floatx4*>(sp + 4) = b;
+            }
+        }
+        if (PHASE != kUpdate && !diag) {
+            __syncthreads();
+            // mirror pass: output row tj*128 + c, columns row_base + 8*chunk .. +7
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int chunk = t % 8;
+                const int c = t / 8 + 32 * p;
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = stage[(chunk * 8 + e) * kStagePitch + c];
+                const size_t idx = (size_t)(job.tj * kTile + c) * M + row_base + chunk * 8;
+                if (PHASE == kGram)
+                    store8<PREC>(static_cast<T*>(G.a_hi) + aplane, static_cast<T*>(G.a_lo) + aplane, idx, v);
+                else
+                    store8<PREC>(static_cast<T*>(G.b) + aplane, COMP ? static_cast<T*>(G.b_lo) + aplane : nullptr,
+                                 idx, v);
+            }
+        }
     }
 }
 
-size_t ns_lds_bytes(int phase, int precision) {
-    return (phase == kSquare && precision == kNsBf16) ? 4 * kTileBytes : 2 * kTileBytes;
+size_t ns_lds_bytes(int phase, int precision, bool comp) {
+    const bool split = precision == kNsBf16 && (phase == kSquare || comp);
+    return split ? 4 * kTileBytes : 2 * kTileBytes;
 }
 
-template <int PHASE, int PREC>
+template <int PHASE, int PREC, bool COMP>
 hipError_t launch_one(const NsArgs& a, hipStream_t s) {
-    const size_t lds = ns_lds_bytes(PHASE, PREC);
+    const size_t lds = ns_lds_bytes(PHASE, PREC, COMP);
     if (lds > 65536) {
         // more than the default 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU)
-        static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&ns_kernel<PHASE, PREC>),
+        static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&ns_kernel<PHASE, PREC, COMP>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (attr != hipSuccess) return attr;
     }
     const int grid = (a.total_jobs + kXcds - 1) / kXcds * kXcds;
-    ns_kernel<PHASE, PREC><<<grid, kThreads, lds, s>>>(a);
+    ns_kernel<PHASE, PREC, COMP><<<grid, kThreads, lds, s>>>(a);
     return hipGetLastError();
+}
+
+template <int PHASE>
+hipError_t launch_phase(const NsArgs& a, int precision, bool comp, hipStream_t s) {
+    if (precision == kNsFp32) return launch_one<PHASE, kNsFp32, false>(a, s);
+    return comp ? launch_one<PHASE, kNsBf16, true>(a, s) : launch_one<PHASE, kNsBf16, false>(a, s);
 }
 
 }  // namespace
 
-hipError_t launch_ns(const NsArgs& a, int phase, int precision, hipStream_t s) {
-    if (precision == kNsBf16) {
-        if (phase == kGram) return launch_one<kGram, kNsBf16>(a, s);
-        if (phase == kSquare) return launch_one<kSquare, kNsBf16>(a, s);
-        return launch_one<kUpdate, kNsBf16>(a, s);
-    }
-    if (phase == kGram) return launch_one<kGram, kNsFp32>(a, s);
-    if (phase == kSquare) return launch_one<kSquare, kNsFp32>(a, s);
-    return launch_one<kUpdate, kNsFp32>(a, s);
+hipError_t launch_ns(const NsArgs& a, int phase, int precision, bool comp, hipStream_t s) {
+    if (phase == kGram) return launch_phase<kGram>(a, precision, comp, s);
+    if (phase == kSquare) return launch_phase<kSquare>(a, precision, comp, s);
+    return launch_phase<kUpdate>(a, precision, comp, s);
 }
 
-const char* ns_kernel_name(int phase, int precision) {
-    static const char* names[2][3] = {{"ns_gram_bf16", "ns_square_bf16", "ns_update_bf16"},
+const char* ns_kernel_name(int phase, int precision, bool comp) {
+    static const char* names[3][3] = {{"ns_gram_bf16", "ns_square_bf16", "ns_update_bf16"},
+                                      {"ns_gram_bf16x3", "ns_square_bf16x3", "ns_update_bf16x3"},
                                       {"ns_gram_fp32", "ns_square_fp32", "ns_update_fp32"}};
-    return names[precision == kNsBf16 ? 0 : 1][phase];
+    const int v = precision == kNsFp32 ? 2 : (comp ? 1 : 0);
+    return names[v][phase];
 }
 
 }  // namespace muon

@@ -10,6 +10,7 @@ import oracle.muon as om
 
 NS_TOL_BF16 = 2e-2      # relative Frobenius error of O per matrix, bf16 NS
 NS_TOL_FP32 = 1e-4      # relative Frobenius error of O per matrix, fp32 NS
+NS_TOL_BF16X3 = 1e-3    # relative Frobenius error of O per matrix, compensated bf16 NS
 ELEM_TOL = 1e-6         # relative max-norm error of the fp32 elementwise parts
 
 

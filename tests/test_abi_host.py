@@ -47,7 +47,7 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     for name in ["MUON_OK", "MUON_ERR_INVALID_ARG", "MUON_ERR_UNSUPPORTED", "MUON_ERR_WORKSPACE", "MUON_ERR_HIP",
                  "MUON_MAX_NS_STEPS", "MUON_MAX_SHORT_SIDE", "MUON_MAX_LONG_SIDE", "MUON_MAX_TENSORS",
-                 "MUON_NS_BF16", "MUON_NS_FP32"]:
+                 "MUON_NS_BF16", "MUON_NS_FP32", "MUON_NS_BF16X3"]:
         m = re.search(rf"#define {name} \(?(-?\d+)\)?", text)
         assert m, name
         assert int(m.group(1)) == getattr(_lib, name), name
@@ -81,7 +81,7 @@ def _call(entries, lr=0.02, mu=0.95, nesterov=1, wd=0.1, row_norm=1, steps=5, co
 @pytest.mark.parametrize("kw,code,msg", [
     (dict(n=0), _lib.MUON_ERR_INVALID_ARG, "n = 0"),
     (dict(n=_lib.MUON_MAX_TENSORS + 1), _lib.MUON_ERR_INVALID_ARG, "outside"),
-    (dict(prec=2), _lib.MUON_ERR_INVALID_ARG, "ns_precision"),
+    (dict(prec=3), _lib.MUON_ERR_INVALID_ARG, "ns_precision"),
     (dict(lr=float("nan")), _lib.MUON_ERR_INVALID_ARG, "finite"),
     (dict(mu=float("inf")), _lib.MUON_ERR_INVALID_ARG, "finite"),
     (dict(wd=float("-inf")), _lib.MUON_ERR_INVALID_ARG, "finite"),
@@ -142,13 +142,14 @@ def test_workspace_size_properties():
     one = _ws([(512, 512)])
     # four bf16 planes of X (two ping-pong pairs) and three of the Gram-sized matrices
     assert one >= 4 * 2 * 512 * 512 + 3 * 2 * 512 * 512
-    assert _ws([(512, 512)], 1) > one                      # fp32 planes are wider
+    assert _ws([(512, 512)], 1) >= 4 * 2 * 512 * 512 + 2 * 4 * 512 * 512   # two fp32 X planes, A and B
     # orientation only changes the per-row sums (one float per stored row)
     assert 0 <= _ws([(2048, 512)]) - _ws([(512, 2048)]) <= 4 * (2048 - 512) + 256
     assert _ws([(100, 30)]) == _ws([(128, 128)])           # padded to 128 on both sides
     assert _ws([(512, 512)] * 22) > 21 * one
     assert _ws([(4, 4)]) % 256 == 0
     assert _ws([]) == 0 and _ws([(0, 4)]) == 0 and _ws([(4, 4)], 7) == 0
+    assert _ws([(512, 512)], 2) == one                   # the compensated mode needs no more
 
 
 def test_ema_rejects_bad_arguments():

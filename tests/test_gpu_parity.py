@@ -142,7 +142,24 @@ def test_structured_gradients_ten_steps():
     assert drift <= gu.NS_TOL_BF16
 
 
-@pytest.mark.parametrize("ns_precision", [0, 1])
+def test_compensated_mode_one_layer():
+    """MUON_NS_BF16X3: hi/lo compensation in every product, ~1e-4 of float64."""
+    w = wl.workload(1)
+    st = wl.make_state(w, wl.PRIMARY_SEED)
+    grads = wl.make_grads(w, wl.PRIMARY_SEED, 0)
+    coeffs = wl.coeff_table(w, wl.PRIMARY_SEED)
+    mats, moms = st["params"], st["moms"]
+    w_gpu, m_gpu, o_gpu = gu.gpu_step(mats, grads, moms, lr=w.lr, momentum=w.momentum, wd=w.weight_decay,
+                                      coeffs=coeffs.tolist(), ns_precision=2)
+    errs = []
+    for i in range(len(mats)):
+        errs.append(gu.check_layers(mats[i], grads[i], moms[i], w_gpu[i], m_gpu[i], o_gpu[i], lr=w.lr,
+                                    momentum=w.momentum, wd=w.weight_decay, coeffs=coeffs, nesterov=True,
+                                    row_norm=True, ns_tol=gu.NS_TOL_BF16X3, label=w.matrices[i][0]))
+    gu.say(f"[parity] compensated one layer: worst NS err {max(errs):.2e}")
+
+
+@pytest.mark.parametrize("ns_precision", [0, 1, 2])
 @pytest.mark.parametrize("nesterov,row_norm", [(True, True), (False, False), (True, False)])
 def test_ragged_shapes(ns_precision, nesterov, row_norm):
     """Odd shapes (wide, tall, square, 1-row, 1-col) leave ragged tails in every tiling."""
@@ -155,7 +172,7 @@ def test_ragged_shapes(ns_precision, nesterov, row_norm):
     gu.say(f"[parity] ragged shapes prec={ns_precision} nesterov={nesterov} row_norm={row_norm}")
     w_gpu, m_gpu, o_gpu = gu.gpu_step(mats, grads, moms, lr=0.05, momentum=0.9, wd=0.1, coeffs=coeffs,
                                       nesterov=nesterov, row_norm=row_norm, ns_precision=ns_precision)
-    tol = gu.NS_TOL_BF16 if ns_precision == 0 else gu.NS_TOL_FP32
+    tol = {0: gu.NS_TOL_BF16, 1: gu.NS_TOL_FP32, 2: gu.NS_TOL_BF16X3}[ns_precision]
     for i, (nm, r, c) in enumerate(shapes):
         gu.check_layers(mats[i], grads[i], moms[i], w_gpu[i], m_gpu[i], o_gpu[i], lr=0.05, momentum=0.9, wd=0.1,
                         coeffs=coeffs, nesterov=nesterov, row_norm=row_norm, ns_tol=tol, label=f"{nm} {r}x{c}")

@@ -44,7 +44,12 @@ def parse():
 
 
 def kernel_work(w):
-    """Algorithmic work per launch of each kernel (flops or HBM bytes) for workload w."""
+    """Algorithmic work of each kernel per step, summed over its launches (flops or HBM bytes).
+
+    The NS kernels launch once per iteration and prep, apply and ema may be
+    split into several launches by tensor-table chunking, so every rate is the
+    kernel's total work per step over its total time per step.
+    """
     flops_gram = flops_square = 0.0
     elems = 0
     for _, r, c in w.matrices:
@@ -53,9 +58,9 @@ def kernel_work(w):
         flops_square += 2.0 * m * m * m
         elems += r * c
     return {
-        "ns_gram_bf16": ("mfma", flops_gram),      # A = X X^T
-        "ns_square_bf16": ("mfma", flops_square),  # B = b A + c A A
-        "ns_update_bf16": ("mfma", flops_gram),    # X <- a X + B X
+        "ns_gram_bf16": ("mfma", flops_gram * w.ns_steps),      # A = X X^T
+        "ns_square_bf16": ("mfma", flops_square * w.ns_steps),  # B = b A + c A A
+        "ns_update_bf16": ("mfma", flops_gram * w.ns_steps),    # X <- a X + B X
         "prep": ("hbm", 16.0 * elems),             # read G, M; write M, X0 (bf16 hi + lo)
         "apply": ("hbm", 12.0 * elems),            # read W, X (bf16 hi + lo); write W
         "ema": ("hbm", 12.0 * w.n_params),         # read E, P; write E
@@ -176,25 +181,26 @@ def main():
     work = kernel_work(w)
     kernels = {}
     for name, (count, total_ms) in prof.items():
-        avg_ms = total_ms / max(count, 1)
-        entry = {"launches": count, "avg_us": avg_ms * 1e3, "ms_per_step": total_ms / args.steps}
+        step_s = total_ms * 1e-3 / args.steps
+        entry = {"launches_per_step": count / args.steps, "avg_us": total_ms / max(count, 1) * 1e3,
+                 "ms_per_step": step_s * 1e3}
         if name in work:
             bound, amount = work[name]
             if bound == "mfma":
-                entry["tflops"] = amount / (avg_ms * 1e-3) / 1e12
+                entry["tflops"] = amount / step_s / 1e12
             else:
-                entry["gbs"] = amount / (avg_ms * 1e-3) / 1e9
+                entry["gbs"] = amount / step_s / 1e9
         kernels[name] = entry
     dom = max((k for k in kernels if k in work), key=lambda k: kernels[k]["ms_per_step"])
     bound, amount = work[dom]
-    avg_s = kernels[dom]["avg_us"] * 1e-6
+    step_s = kernels[dom]["ms_per_step"] * 1e-3
     if bound == "mfma":
-        achieved, peak, unit = amount / avg_s / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
+        achieved, peak, unit = amount / step_s / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
     else:
-        achieved, peak, unit = amount / avg_s / 1e9, HBM_PEAK_GBS, "GB/s"
+        achieved, peak, unit = amount / step_s / 1e9, HBM_PEAK_GBS, "GB/s"
     ns_names = [k for k in kernels if k.startswith("ns_")]
     ns_ms = sum(kernels[k]["ms_per_step"] for k in ns_names)
-    ns_flops = sum(work[k][1] * kernels[k]["launches"] / args.steps for k in ns_names if k in work)
+    ns_flops = sum(work[k][1] for k in ns_names if k in work)
     ns_tflops = ns_flops / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else None
 
     out = {

@@ -54,6 +54,88 @@ __device__ inline float load_x(const void* xh, const void* xl, size_t idx) {
     }
 }
 
+// Four consecutive X elements (8-byte aligned in bf16, 16 in fp32).
+template <int PREC>
+__device__ inline void store_x4(void* xh, void* xl, size_t idx, float4 v) {
+    if (PREC == kNsBf16) {
+        bf16 h[4], l[4];
+        split_bf16(v.x, h[0], l[0]);
+        split_bf16(v.y, h[1], l[1]);
+        split_bf16(v.z, h[2], l[2]);
+        split_bf16(v.w, h[3], l[3]);
+        u32x2 ph, pl;
+        ph.x = bf16_bits(h[0]) | (bf16_bits(h[1]) << 16);
+        ph.y = bf16_bits(h[2]) | (bf16_bits(h[3]) << 16);
+        pl.x = bf16_bits(l[0]) | (bf16_bits(l[1]) << 16);
+        pl.y = bf16_bits(l[2]) | (bf16_bits(l[3]) << 16);
+        *reinterpret_cast<u32x2*>(static_cast<bf16*>(xh) + idx) = ph;
+        *reinterpret_cast<u32x2*>(static_cast<bf16*>(xl) + idx) = pl;
+    } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(xh) + idx) = v;
+    }
+}
+
+template <int PREC>
+__device__ inline float4 load_x4(const void* xh, const void* xl, size_t idx) {
+    if (PREC == kNsBf16) {
+        const u32x2 h = *reinterpret_cast<const u32x2*>(static_cast<const bf16*>(xh) + idx);
+        const u32x2 l = *reinterpret_cast<const u32x2*>(static_cast<const bf16*>(xl) + idx);
+        float4 r;
+        r.x = from_bf16(bits_bf16(h.x & 0xFFFFu)) + from_bf16(bits_bf16(l.x & 0xFFFFu));
+        r.y = from_bf16(bits_bf16(h.x >> 16)) + from_bf16(bits_bf16(l.x >> 16));
+        r.z = from_bf16(bits_bf16(h.y & 0xFFFFu)) + from_bf16(bits_bf16(l.y & 0xFFFFu));
+        r.w = from_bf16(bits_bf16(h.y >> 16)) + from_bf16(bits_bf16(l.y >> 16));
+        return r;
+    } else {
+        return *reinterpret_cast<const float4*>(static_cast<const float*>(xh) + idx);
+    }
+}
+
+constexpr int kRegVec = 16;  // float4 per lane kept in registers: rows of up to 4096 floats
+
+// One stored row of up to 4 * 64 * kRegVec floats (cols % 4 == 0, 16-byte
+// aligned), one wavefront, a single pass over G and M: M' is written at once,
+// U stays in registers until the row norm is known, then r = U/(|U|+eps) (or U)
+// is handed to emit4 four elements at a time.  Returns sum(r^2) on every lane.
+template <typename Emit4>
+__device__ inline float process_row_regs(const float* __restrict__ g, float* __restrict__ m, int cols, float mu,
+                                         int nesterov, int row_norm, int lane, Emit4 emit4) {
+    const float4* g4 = reinterpret_cast<const float4*>(g);
+    float4* m4 = reinterpret_cast<float4*>(m);
+    const int nv = cols / 4;
+    float4 u[kRegVec];
+    float ss = 0.f;
+#pragma unroll
+    for (int v = 0; v < kRegVec; ++v) {
+        const int j = lane + v * kWave;
+        if (j < nv) {
+            const float4 gv = g4[j], mv = m4[j];
+            float4 mn;
+            u[v].x = momentum_u(gv.x, mv.x, mu, nesterov, mn.x);
+            u[v].y = momentum_u(gv.y, mv.y, mu, nesterov, mn.y);
+            u[v].z = momentum_u(gv.z, mv.z, mu, nesterov, mn.z);
+            u[v].w = momentum_u(gv.w, mv.w, mu, nesterov, mn.w);
+            m4[j] = mn;
+            ss = fmaf(u[v].x, u[v].x, ss); ss = fmaf(u[v].y, u[v].y, ss);
+            ss = fmaf(u[v].z, u[v].z, ss); ss = fmaf(u[v].w, u[v].w, ss);
+        }
+    }
+    ss = wave_sum(ss);
+    const float denom = sqrtf(ss) + kEps;
+    float rs = 0.f;
+#pragma unroll
+    for (int v = 0; v < kRegVec; ++v) {
+        const int j = lane + v * kWave;
+        if (j < nv) {
+            float4 r = u[v];
+            if (row_norm) { r.x /= denom; r.y /= denom; r.z /= denom; r.w /= denom; }
+            rs = fmaf(r.x, r.x, rs); rs = fmaf(r.y, r.y, rs); rs = fmaf(r.z, r.z, rs); rs = fmaf(r.w, r.w, rs);
+            emit4(4 * j, r);
+        }
+    }
+    return wave_sum(rs);
+}
+
 // One stored row, one wavefront.  Pass 1 reduces sum(U^2) (no writes); pass 2
 // recomputes U, writes M', and hands r = U/(|U|+eps) (or U) to `emit`.
 // Returns sum(r^2) on every lane.
@@ -130,12 +212,21 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepArgs a) {
         if (row < T.rows) {
             const float* g = T.grad + (size_t)row * T.cols;
             float* m = T.mom + (size_t)row * T.cols;
-            const float rs = process_row(g, m, T.cols, T.vec, a.mu, a.nesterov, a.row_norm, lane,
-                                         [&](int j, float r) { store_x<PREC>(T.xh, T.xl, xrow + j, r); });
+            float rs;
+            if (T.vec && T.cols <= 4 * kWave * kRegVec) {
+                rs = process_row_regs(g, m, T.cols, a.mu, a.nesterov, a.row_norm, lane,
+                                      [&](int j, float4 r) { store_x4<PREC>(T.xh, T.xl, xrow + j, r); });
+                const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+                for (int j = T.cols + 4 * lane; j < T.n_pad; j += 4 * kWave) store_x4<PREC>(T.xh, T.xl, xrow + j, z);
+            } else {
+                rs = process_row(g, m, T.cols, T.vec, a.mu, a.nesterov, a.row_norm, lane,
+                                 [&](int j, float r) { store_x<PREC>(T.xh, T.xl, xrow + j, r); });
+                for (int j = T.cols + lane; j < T.n_pad; j += kWave) store_x<PREC>(T.xh, T.xl, xrow + j, 0.f);
+            }
             if (lane == 0) T.rowsq[row] = rs;
-            for (int j = T.cols + lane; j < T.n_pad; j += kWave) store_x<PREC>(T.xh, T.xl, xrow + j, 0.f);
         } else {
-            for (int j = lane; j < T.n_pad; j += kWave) store_x<PREC>(T.xh, T.xl, xrow + j, 0.f);
+            const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int j = 4 * lane; j < T.n_pad; j += 4 * kWave) store_x4<PREC>(T.xh, T.xl, xrow + j, z);
         }
         return;
     }
@@ -152,20 +243,45 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepArgs a) {
         if (row < T.rows) {
             const float* g = T.grad + (size_t)row * T.cols;
             float* m = T.mom + (size_t)row * T.cols;
-            const float rs = process_row(g, m, T.cols, T.vec, a.mu, a.nesterov, a.row_norm, lane,
-                                         [&](int j, float r) { dst[j] = r; });
+            float rs;
+            if (T.vec && T.cols <= 4 * kWave * kRegVec) {
+                rs = process_row_regs(g, m, T.cols, a.mu, a.nesterov, a.row_norm, lane, [&](int j, float4 r) {
+                    dst[j] = r.x; dst[j + 1] = r.y; dst[j + 2] = r.z; dst[j + 3] = r.w;
+                });
+            } else {
+                rs = process_row(g, m, T.cols, T.vec, a.mu, a.nesterov, a.row_norm, lane,
+                                 [&](int j, float r) { dst[j] = r; });
+            }
             if (lane == 0) T.rowsq[row] = rs;
         } else {
             for (int j = lane; j < T.cols; j += kWave) dst[j] = 0.f;
         }
     }
     __syncthreads();
-    const int items = T.m_pad * rb;
-    for (int it = threadIdx.x; it < items; it += blockDim.x) {
-        const int j = it / rb;
-        const int rr = it - j * rb;
-        const float v = (j < T.cols) ? lds_rows[(size_t)rr * pitch + j] : 0.f;
-        store_x<PREC>(T.xh, T.xl, (size_t)j * ld + row0 + rr, v);
+    if (rb % 4 == 0) {
+        // four consecutive X0 columns (= stored rows) per item: 8-byte bf16 stores
+        const int rq = rb / 4;
+        const int items = T.m_pad * rq;
+        for (int it = threadIdx.x; it < items; it += blockDim.x) {
+            const int j = it / rq;
+            const int rr = 4 * (it - j * rq);
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (j < T.cols) {
+                v.x = lds_rows[(size_t)(rr + 0) * pitch + j];
+                v.y = lds_rows[(size_t)(rr + 1) * pitch + j];
+                v.z = lds_rows[(size_t)(rr + 2) * pitch + j];
+                v.w = lds_rows[(size_t)(rr + 3) * pitch + j];
+            }
+            store_x4<PREC>(T.xh, T.xl, (size_t)j * ld + row0 + rr, v);
+        }
+    } else {
+        const int items = T.m_pad * rb;
+        for (int it = threadIdx.x; it < items; it += blockDim.x) {
+            const int j = it / rb;
+            const int rr = it - j * rb;
+            const float v = (j < T.cols) ? lds_rows[(size_t)rr * pitch + j] : 0.f;
+            store_x<PREC>(T.xh, T.xl, (size_t)j * ld + row0 + rr, v);
+        }
     }
 }
 
@@ -210,11 +326,8 @@ __global__ __launch_bounds__(256) void apply_kernel(const ApplyArgs a) {
             float4* w4 = reinterpret_cast<float4*>(w);
             float4* o4 = reinterpret_cast<float4*>(out);
             for (int j = lane; j < T.cols / 4; j += kWave) {
-                float4 o;
-                o.x = fac * load_x<PREC>(T.xh, T.xl, xrow + 4 * j + 0);
-                o.y = fac * load_x<PREC>(T.xh, T.xl, xrow + 4 * j + 1);
-                o.z = fac * load_x<PREC>(T.xh, T.xl, xrow + 4 * j + 2);
-                o.w = fac * load_x<PREC>(T.xh, T.xl, xrow + 4 * j + 3);
+                float4 o = load_x4<PREC>(T.xh, T.xl, xrow + 4 * j);
+                o.x *= fac; o.y *= fac; o.z *= fac; o.w *= fac;
                 float4 wv = w4[j];
                 wv.x = fmaf(-lr_s, o.x, keep * wv.x);
                 wv.y = fmaf(-lr_s, o.y, keep * wv.y);
@@ -237,11 +350,26 @@ __global__ __launch_bounds__(256) void apply_kernel(const ApplyArgs a) {
     const int rb = T.rb;
     const int pitch = T.cols + 1;
     const int row0 = blk * rb;
-    const int items = T.cols * rb;
-    for (int it = threadIdx.x; it < items; it += blockDim.x) {
-        const int j = it / rb;
-        const int rr = it - j * rb;
-        lds_o[(size_t)rr * pitch + j] = (row0 + rr < T.rows) ? fac * load_x<PREC>(T.xh, T.xl, (size_t)j * ld + row0 + rr) : 0.f;
+    if (rb % 4 == 0) {
+        // X columns row0 .. row0+rb lie in the zero-padded plane (n_pad >= row0 + rb)
+        const int rq = rb / 4;
+        const int items = T.cols * rq;
+        for (int it = threadIdx.x; it < items; it += blockDim.x) {
+            const int j = it / rq;
+            const int rr = 4 * (it - j * rq);
+            const float4 v = load_x4<PREC>(T.xh, T.xl, (size_t)j * ld + row0 + rr);
+            lds_o[(size_t)(rr + 0) * pitch + j] = fac * v.x;
+            lds_o[(size_t)(rr + 1) * pitch + j] = fac * v.y;
+            lds_o[(size_t)(rr + 2) * pitch + j] = fac * v.z;
+            lds_o[(size_t)(rr + 3) * pitch + j] = fac * v.w;
+        }
+    } else {
+        const int items = T.cols * rb;
+        for (int it = threadIdx.x; it < items; it += blockDim.x) {
+            const int j = it / rb;
+            const int rr = it - j * rb;
+            lds_o[(size_t)rr * pitch + j] = fac * load_x<PREC>(T.xh, T.xl, (size_t)j * ld + row0 + rr);
+        }
     }
     __syncthreads();
     for (int rr = wave; rr < rb; rr += 4) {

@@ -40,30 +40,53 @@ def parse():
     ap.add_argument("--seed", type=int, default=1337)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 5 device-to-device copies of MIB MiB (counter calibration) and exit")
     return ap.parse_args()
 
 
-def kernel_work(w):
-    """Algorithmic work of each kernel per step, summed over its launches (flops or HBM bytes).
+def calibrate_copy(mib: int) -> None:
+    """A plain copy of known size: the reference for scaling FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, device="cuda:0")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 5}), flush=True)
 
-    The NS kernels launch once per iteration and prep, apply and ema may be
-    split into several launches by tensor-table chunking, so every rate is the
-    kernel's total work per step over its total time per step.
+
+def kernel_model(w):
+    """Algorithmic work of each kernel: flops and HBM bytes.
+
+    NS kernels: per launch (one launch per iteration, every launch the same).
+    prep, apply and ema: per step (they may be split into several launches by
+    tensor-table chunking).  Bytes count each operand once at its stored width:
+    X is a bf16 hi + lo pair (4 B), A and B are bf16 (hi + lo for A), weights,
+    gradients, momenta and EMA shadows are fp32.
     """
-    flops_gram = flops_square = 0.0
+    gram_f = sq_f = 0.0
+    gram_b = sq_b = upd_b = upda_b = 0.0
     elems = 0
     for _, r, c in w.matrices:
         m, n = min(r, c), max(r, c)
-        flops_gram += 2.0 * m * m * n
-        flops_square += 2.0 * m * m * m
+        gram_f += 2.0 * m * m * n
+        sq_f += 2.0 * m * m * m
+        gram_b += 2.0 * m * n + 4.0 * m * m      # read X hi; write A hi + lo
+        sq_b += 4.0 * m * m + 2.0 * m * m        # read A hi + lo; write B
+        upd_b += 8.0 * m * n + 2.0 * m * m       # read X hi + lo and B; write X hi + lo
+        upda_b += 12.0 * m * n + 2.0 * m * m     # read X hi + lo and B; read + write W
         elems += r * c
     return {
-        "ns_gram_bf16": ("mfma", flops_gram * w.ns_steps),      # A = X X^T
-        "ns_square_bf16": ("mfma", flops_square * w.ns_steps),  # B = b A + c A A
-        "ns_update_bf16": ("mfma", flops_gram * w.ns_steps),    # X <- a X + B X
-        "prep": ("hbm", 16.0 * elems),             # read G, M; write M, X0 (bf16 hi + lo)
-        "apply": ("hbm", 12.0 * elems),            # read W, X (bf16 hi + lo); write W
-        "ema": ("hbm", 12.0 * w.n_params),         # read E, P; write E
+        "ns_gram_bf16": {"per": "launch", "flops": gram_f, "bytes": gram_b},      # A = X X^T
+        "ns_square_bf16": {"per": "launch", "flops": sq_f, "bytes": sq_b},        # B = b A + c A A
+        "ns_update_bf16": {"per": "launch", "flops": gram_f, "bytes": upd_b},     # X <- a X + B X
+        "ns_update_apply_bf16": {"per": "launch", "flops": gram_f, "bytes": upda_b},  # last X, then W'
+        "prep": {"per": "step", "flops": 0.0, "bytes": 16.0 * elems},   # read G, M; write M, X0 hi + lo
+        "apply": {"per": "step", "flops": 0.0, "bytes": 12.0 * elems},  # read W, X hi + lo; write W
+        "ema": {"per": "step", "flops": 0.0, "bytes": 12.0 * w.n_params},  # read E, P; write E
     }
 
 
@@ -130,6 +153,9 @@ def main():
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU sharding is a design note, not a measured path", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     import numpy as np
     import torch
     import muon_optimizer_step_amd as ms
@@ -178,30 +204,35 @@ def main():
     prof_elapsed = time.perf_counter() - tp0
     ms.profile_enable(False)
     prof = ms.profile_read(reset=True)
-    work = kernel_work(w)
+    model = kernel_model(w)
     kernels = {}
     for name, (count, total_ms) in prof.items():
         step_s = total_ms * 1e-3 / args.steps
-        entry = {"launches_per_step": count / args.steps, "avg_us": total_ms / max(count, 1) * 1e3,
-                 "ms_per_step": step_s * 1e3}
-        if name in work:
-            bound, amount = work[name]
-            if bound == "mfma":
-                entry["tflops"] = amount / step_s / 1e12
-            else:
-                entry["gbs"] = amount / step_s / 1e9
+        lps = count / args.steps
+        entry = {"launches_per_step": lps, "avg_us": total_ms / max(count, 1) * 1e3, "ms_per_step": step_s * 1e3}
+        if name in model:
+            mm = model[name]
+            scale = lps if mm["per"] == "launch" else 1.0
+            entry["flops_per_step"] = mm["flops"] * scale
+            entry["bytes_per_step"] = mm["bytes"] * scale
+            if mm["flops"] > 0:
+                entry["tflops"] = entry["flops_per_step"] / step_s / 1e12
+            entry["gbs"] = entry["bytes_per_step"] / step_s / 1e9
         kernels[name] = entry
-    dom = max((k for k in kernels if k in work), key=lambda k: kernels[k]["ms_per_step"])
-    bound, amount = work[dom]
-    step_s = kernels[dom]["ms_per_step"] * 1e-3
-    if bound == "mfma":
-        achieved, peak, unit = amount / step_s / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
+    dom = max((k for k in kernels if k in model), key=lambda k: kernels[k]["ms_per_step"])
+    d = kernels[dom]
+    # the binding roofline: whichever of MFMA time and HBM time is longer at peak
+    t_mfma = d["flops_per_step"] / (BF16_PEAK_TFLOPS * 1e12)
+    t_hbm = d["bytes_per_step"] / (HBM_PEAK_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        bound, achieved, peak, unit = "mfma", d["tflops"], BF16_PEAK_TFLOPS, "TFLOP/s"
     else:
-        achieved, peak, unit = amount / step_s / 1e9, HBM_PEAK_GBS, "GB/s"
+        bound, achieved, peak, unit = "hbm", d["gbs"], HBM_PEAK_GBS, "GB/s"
     ns_names = [k for k in kernels if k.startswith("ns_")]
     ns_ms = sum(kernels[k]["ms_per_step"] for k in ns_names)
-    ns_flops = sum(work[k][1] for k in ns_names if k in work)
+    ns_flops = sum(kernels[k].get("flops_per_step", 0.0) for k in ns_names)
     ns_tflops = ns_flops / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else None
+    traffic = traffic_for(dom)
 
     out = {
         "metric": METRIC,
@@ -220,7 +251,9 @@ def main():
                                f"5 NS steps bf16, then ema_update over {w.n_params:,} fp32 params",
                    "matrices": nm, "params": w.n_params, "ns_steps": w.ns_steps, "seed": args.seed},
         "roofline": {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                     "frac": round(achieved / peak, 4), "traffic": traffic_for(dom)},
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "mfma_frac": round(d.get("tflops", 0.0) / BF16_PEAK_TFLOPS, 4),
+                     "hbm_frac": round(d["gbs"] / HBM_PEAK_GBS, 4)},
         "ns": {"tflops_algorithmic": round(ns_tflops, 2) if ns_tflops else None,
                "frac_of_bf16_peak": round(ns_tflops / BF16_PEAK_TFLOPS, 4) if ns_tflops else None,
                "ms_per_step": round(ns_ms, 4)},

@@ -106,6 +106,7 @@ struct Group {
 
 struct Plan {
     std::vector<Group> groups;
+    std::vector<std::vector<int>> members;  // tensors of each group, by slot
     std::vector<int> group_of, slot_of;
     std::vector<size_t> rowsq_off;  // in floats
     size_t rowsq_base = 0;          // byte offset of the rowsq array
@@ -148,6 +149,8 @@ void make_plan(const muon_tensor_t* t, int n, int mode, Plan& p) {
         }
         p.group_of[i] = g;
         p.slot_of[i] = p.groups[g].count++;
+        if ((int)p.members.size() <= g) p.members.resize(g + 1);
+        p.members[g].push_back(i);
         p.rowsq_off[i] = rowsq_total;
         rowsq_total += (size_t)t[i].rows;
     }
@@ -353,6 +356,23 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
     // ---- Newton-Schulz iterations: per phase, one launch for the base groups and
     // one for the compensated groups (each skipped when empty)
     const int ngroups = (int)p.groups.size();
+    // The weight update runs inside the last NS update launch when every launch
+    // of that phase has at most kMaxFused matrices.
+    bool fuse = ns_steps > 0;
+    for (int comp = 0; comp < 2 && fuse; ++comp) {
+        std::vector<int> gl;
+        for (int g = 0; g < ngroups; ++g)
+            if ((int)p.groups[g].comp == comp) gl.push_back(g);
+        for (size_t g0 = 0; g0 < gl.size(); g0 += kMaxGroups) {
+            int cnt = 0;
+            for (size_t q = g0; q < std::min(gl.size(), g0 + kMaxGroups); ++q) cnt += p.groups[gl[q]].count;
+            if (cnt > kMaxFused) fuse = false;
+        }
+    }
+    const float keep = 1.0f - lr * weight_decay;
+    auto lr_scale = [&](const muon_tensor_t& x) {
+        return lr * (float)std::sqrt(std::max(1.0, (double)x.rows / (double)x.cols));
+    };
     for (int k = 0; k < ns_steps; ++k) {
         for (int phase = kGram; phase <= kUpdate; ++phase) {
             for (int comp = 0; comp < 2; ++comp) {
@@ -367,7 +387,9 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
                     a.a = ns_coeffs[3 * k + 0];
                     a.b = ns_coeffs[3 * k + 1];
                     a.c = ns_coeffs[3 * k + 2];
-                    int jobs = 0;
+                    a.fuse_apply = fuse && phase == kUpdate && k == ns_steps - 1;
+                    a.keep = keep;
+                    int jobs = 0, napply = 0;
                     for (size_t q = g0; q < std::min(gl.size(), g0 + kMaxGroups); ++q) {
                         const Group& G = p.groups[gl[q]];
                         NsGroup& D = a.g[a.ngroups++];
@@ -384,11 +406,26 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
                         D.M = G.M;
                         D.N = G.N;
                         D.job_begin = jobs;
+                        D.apply_begin = napply;
+                        if (a.fuse_apply) {
+                            for (int ti : p.members[gl[q]]) {
+                                const muon_tensor_t& x = tensors[ti];
+                                FusedApply& F = a.apply[napply++];
+                                F.param = x.param;
+                                F.out = x.update_out;
+                                F.rows = x.rows;
+                                F.cols = x.cols;
+                                F.transposed = x.rows > x.cols;
+                                F.vec = (x.cols % 4 == 0) && (reinterpret_cast<uintptr_t>(x.param) % 16 == 0) &&
+                                        (reinterpret_cast<uintptr_t>(x.update_out) % 16 == 0);
+                                F.lr_s = lr_scale(x);
+                            }
+                        }
                         const int tm = G.M / kTile, tn = G.N / kTile;
                         jobs += G.count * (phase == kUpdate ? tm * tn : tm * (tm + 1) / 2);
                     }
                     a.total_jobs = jobs;
-                    const char* name = ns_kernel_name(phase, prec, comp != 0);
+                    const char* name = ns_kernel_name(phase, prec, comp != 0, a.fuse_apply != 0);
                     err = timed_launch(name, s, [&] { return launch_ns(a, phase, prec, comp != 0, s); });
                     if (err != hipSuccess) return fail(MUON_ERR_HIP, "%s launch failed: %s", name, hipGetErrorString(err));
                 }
@@ -396,12 +433,12 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
         }
     }
 
-    // ---- apply: W' = (1 - lr wd) W - lr s O
+    // ---- apply: W' = (1 - lr wd) W - lr s O (unless the last NS update did it)
     const int final_buf = ns_steps & 1;
-    for (int c0 = 0; c0 < n; c0 += kPrepChunk) {
+    for (int c0 = 0; c0 < n && !fuse; c0 += kPrepChunk) {
         ApplyArgs a;
         memset(&a, 0, sizeof(a));
-        a.keep = 1.0f - lr * weight_decay;
+        a.keep = keep;
         a.use_scale = ns_steps == 0;
         int blocks = 0;
         size_t lds = 0;
@@ -416,7 +453,7 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
             T.xh = ws + G.x_off[final_buf] + slot_off;
             T.xl = ws + G.xl_off[final_buf] + slot_off;
             T.scale = reinterpret_cast<const float*>(ws + p.scale_base) + G.scale_begin + p.slot_of[i];
-            T.lr_s = lr * (float)std::sqrt(std::max(1.0, (double)x.rows / (double)x.cols));
+            T.lr_s = lr_scale(x);
             T.rows = x.rows;
             T.cols = x.cols;
             T.n_pad = G.N;

@@ -51,6 +51,19 @@ struct FrobArgs {
 };
 
 // ------------------------------------------------------------- NS phases
+// Weight update folded into the last NS update launch (one entry per matrix of
+// the launch): W' = keep*W - lr_s*O with O the final X, written in stored layout.
+constexpr int kMaxFused = 72;
+struct FusedApply {
+    float* param;
+    float* out;          // optional copy of O
+    int rows, cols;      // stored shape
+    int transposed;
+    int vec;             // param/out 16-byte aligned and the 8-wide runs are aligned
+    float lr_s;
+    int pad_;
+};
+
 struct NsGroup {
     void* x[2];      // bf16: hi planes (ping-pong); fp32: X planes.  [count][M][N]
     void* xl[2];     // bf16: lo planes; fp32: unused
@@ -61,6 +74,7 @@ struct NsGroup {
     const float* scale;  // [count] Frobenius scale of X0
     int count, M, N;     // padded, multiples of 128
     int job_begin;
+    int apply_begin;     // fused apply: entry of slot 0 in NsArgs::apply
 };
 struct NsArgs {
     NsGroup g[kMaxGroups];
@@ -69,6 +83,9 @@ struct NsArgs {
     int src;         // ping-pong plane holding the current X
     int first;       // iteration 0: fold the Frobenius scale in
     float a, b, c;
+    int fuse_apply;  // last update: write W' (and O) instead of X
+    float keep;      // 1 - lr*wd
+    FusedApply apply[kMaxFused];
 };
 
 enum NsPhase { kGram = 0, kSquare = 1, kUpdate = 2 };
@@ -126,7 +143,7 @@ hipError_t launch_ns(const NsArgs& a, int phase, int precision, bool compensated
 hipError_t launch_apply(const ApplyArgs& a, int precision, int blocks, size_t lds_bytes, hipStream_t s);
 hipError_t launch_ema(const EmaArgs& a, int blocks, hipStream_t s);
 
-const char* ns_kernel_name(int phase, int precision, bool compensated);
+const char* ns_kernel_name(int phase, int precision, bool compensated, bool fused_apply);
 
 // Short side below which the bf16 precision runs the compensated products:
 // with fewer singular values the bf16 rounding of the base products no longer

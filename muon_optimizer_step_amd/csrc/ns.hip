@@ -34,6 +34,16 @@
 #include "common.h"
 #include "kernels.h"
 
+#ifndef NS_DOUBLE_BUFFER
+#define NS_DOUBLE_BUFFER 0   // 1: base kernels double-buffer their LDS stages (costs occupancy)
+#endif
+#ifndef NS_KEEP_X
+#define NS_KEEP_X 1          // bf16 update: the epilogue reuses the X rows its K loop loaded last
+#endif
+#ifndef NS_TRANSPOSE_READ
+#define NS_TRANSPOSE_READ 1  // bf16 update reads X through ds_read_b64_tr_b16
+#endif
+
 namespace muon {
 
 namespace {
@@ -143,6 +153,48 @@ template <> struct TLoader<kNsFp32> {
     }
 };
 
+// bf16 X[k][j] tile for the update's B operand kept in its natural layout:
+// 64 k-rows x 128 j (256 bytes) per stage, rows padded to kXPitch so that the
+// transposing LDS reads below are free of bank conflicts.  Thread t moves 16
+// bytes: row t/16 + 16q, column chunk t%16.
+constexpr int kXPitch = 256 + 32;
+static_assert(64 * kXPitch <= kTileBytes, "X stage must fit one operand tile slot");
+struct XLoader {
+    u32x4 r[4];
+    __device__ inline void load(const bf16* x, size_t ld, int k0, int j0) {
+        const int t = threadIdx.x;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            r[q] = *reinterpret_cast<const u32x4*>(x + (size_t)(k0 + t / 16 + 16 * q) * ld + j0 + 8 * (t % 16));
+    }
+    __device__ inline void store(uint8_t* lds) const {
+        const int t = threadIdx.x;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<u32x4*>(lds + (t / 16 + 16 * q) * kXPitch + (t % 16) * 16) = r[q];
+    }
+};
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+
+// B-operand fragment of v_mfma_f32_32x32x16_bf16 from the natural [k][j] tile:
+// lane l needs X[k0 + 8(l/32) + e][j0 + l%32], e = 0..7.  ds_read_b64_tr_b16
+// hands lane l' of each 16-lane group element l'%4 of the 8-byte chunk read by
+// lane 4e + l'/4, so lane l points at row k0 + 8(l/32) + 4h + (l%16)/4,
+// columns j0 + 16((l/16)%2) + 4(l%4) .. +3, for the halves h = 0, 1.
+__device__ inline u32x4 lds_frag_tr(const uint8_t* tile, int k0, int j0, int lane) {
+    const int row = k0 + 8 * (lane / 32) + (lane % 16) / 4;
+    const int col = j0 + 16 * ((lane / 16) % 2) + 4 * (lane % 4);
+    typedef __attribute__((address_space(3))) short4v lds_short4;
+    const uint8_t* p0 = tile + row * kXPitch + col * 2;
+    const short4v a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p0));
+    const short4v b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p0 + 4 * kXPitch));
+    u32x4 r;
+    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+    r[0] = ua[0]; r[1] = ua[1]; r[2] = ub[0]; r[3] = ub[1];
+    return r;
+}
+
 __device__ inline u32x4 lds_frag(const uint8_t* tile, int row, int kc, int lane) {
     return *reinterpret_cast<const u32x4*>(tile + row * kPitch + kc * 32 + (lane / 32) * 16);
 }
@@ -177,6 +229,14 @@ __device__ inline bool decode_job(const NsArgs& args, Job& j) {
     }
     j.g = g;
     return true;
+}
+
+__device__ inline void unpack8(const u32x4& w, float* v) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        v[2 * p] = from_bf16(bits_bf16(w[p] & 0xFFFFu));
+        v[2 * p + 1] = from_bf16(bits_bf16(w[p] >> 16));
+    }
 }
 
 // 8 consecutive elements of a plane <-> 8 floats.
@@ -222,7 +282,36 @@ __device__ inline void store8(void* hi, void* lo, size_t idx, const float* v) {
     }
 }
 
-template <int PHASE, int PREC, bool COMP>
+// Fused weight update for up to 8 consecutive stored elements starting at idx:
+// W' = keep*W - lr_s*O, and the optional copy of O.
+__device__ inline void apply8(const FusedApply& F, size_t idx, int count, const float* v, float keep) {
+    if (count >= 8 && F.vec) {
+        floatx4* w4 = reinterpret_cast<floatx4*>(F.param + idx);
+        floatx4 w0 = w4[0], w1 = w4[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            w0[e] = fmaf(-F.lr_s, v[e], keep * w0[e]);
+            w1[e] = fmaf(-F.lr_s, v[4 + e], keep * w1[e]);
+        }
+        w4[0] = w0;
+        w4[1] = w1;
+        if (F.out) {
+            floatx4 o0, o1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { o0[e] = v[e]; o1[e] = v[4 + e]; }
+            floatx4* o4 = reinterpret_cast<floatx4*>(F.out + idx);
+            o4[0] = o0;
+            o4[1] = o1;
+        }
+        return;
+    }
+    for (int e = 0; e < count && e < 8; ++e) {
+        F.param[idx + e] = fmaf(-F.lr_s, v[e], keep * F.param[idx + e]);
+        if (F.out) F.out[idx + e] = v[e];
+    }
+}
+
+template <int PHASE, int PREC, bool COMP, bool FUSE>
 __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
     typedef typename Elem<PREC>::T T;
     constexpr int kBK = Elem<PREC>::kBK;
@@ -242,12 +331,18 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
     const size_t aplane = (size_t)job.slot * M * M;
     const int src = args.src;
 
-    // LDS operand tiles: [0] hi of the A-side rows, [1] hi of the B-side rows,
-    // [2] / [3] the lo planes.  On diagonal tiles both sides are the same rows.
-    uint8_t* t_a = lds;
-    uint8_t* t_b = diag ? lds : lds + kTileBytes;
-    uint8_t* t_al = lds + 2 * kTileBytes;
-    uint8_t* t_bl = diag ? t_al : lds + 3 * kTileBytes;
+    // LDS operand tiles per stage: [0] hi of the A-side rows, [1] hi of the
+    // B-side rows, [2] / [3] the lo planes.  On diagonal tiles both sides are
+    // the same rows.  The bf16 update keeps its X tile in natural [k][j] layout
+    // and reads it with transposing LDS loads.
+    constexpr bool kTr = (PHASE == kUpdate) && (PREC == kNsBf16) && (NS_TRANSPOSE_READ != 0);
+    constexpr int kStages = (kSplit || NS_DOUBLE_BUFFER == 0) ? 1 : 2;
+    constexpr int kStageTiles = kSplit ? 4 : 2;
+    auto tile = [&](int stage, int which) -> uint8_t* {
+        if (diag && which == 1) which = 0;
+        if (diag && which == 3) which = 2;
+        return lds + (stage * kStageTiles + which) * kTileBytes;
+    };
 
     const uint8_t *ga = nullptr, *gb = nullptr, *gal = nullptr, *gbl = nullptr;
     const T *xb = nullptr, *xbl = nullptr;  // update: B-side X planes
@@ -292,44 +387,56 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
 
     NtLoader la, lb, lal, lbl;
     TLoader<PREC> lt, ltl;
+    XLoader lx, lxl;
     auto issue = [&](int k0) {
         const int kbyte = k0 * (int)sizeof(T);
         la.load(ga, ld_bytes, kbyte);
         if (kSplit) lal.load(gal, ld_bytes, kbyte);
         if (PHASE == kUpdate) {
-            lt.load(xb, (size_t)N, k0, job.tj * kTile);
-            if (kSplit) ltl.load(xbl, (size_t)N, k0, job.tj * kTile);
+            if constexpr (kTr) {
+                lx.load(reinterpret_cast<const bf16*>(xb), (size_t)N, k0, job.tj * kTile);
+                if (kSplit) lxl.load(reinterpret_cast<const bf16*>(xbl), (size_t)N, k0, job.tj * kTile);
+            } else {
+                lt.load(xb, (size_t)N, k0, job.tj * kTile);
+                if (kSplit) ltl.load(xbl, (size_t)N, k0, job.tj * kTile);
+            }
         } else if (!diag) {
             lb.load(gb, ld_bytes, kbyte);
             if (kSplit) lbl.load(gbl, ld_bytes, kbyte);
         }
     };
-    auto commit = [&]() {
-        la.store(t_a);
-        if (kSplit) lal.store(t_al);
+    auto commit = [&](int stage) {
+        la.store(tile(stage, 0));
+        if (kSplit) lal.store(tile(stage, 2));
         if (PHASE == kUpdate) {
-            lt.store(t_b);
-            if (kSplit) ltl.store(t_bl);
+            if constexpr (kTr) {
+                lx.store(tile(stage, 1));
+                if (kSplit) lxl.store(tile(stage, 3));
+            } else {
+                lt.store(tile(stage, 1));
+                if (kSplit) ltl.store(tile(stage, 3));
+            }
         } else if (!diag) {
-            lb.store(t_b);
-            if (kSplit) lbl.store(t_bl);
+            lb.store(tile(stage, 1));
+            if (kSplit) lbl.store(tile(stage, 3));
         }
     };
-
-    const int nk = K / kBK;
-    issue(0);
-    for (int kt = 0; kt < nk; ++kt) {
-        __syncthreads();
-        commit();
-        __syncthreads();
-        if (kt + 1 < nk) issue((kt + 1) * kBK);
+    auto bfrag = [&](const uint8_t* tb, int ni, int kc) -> u32x4 {
+        if constexpr (kTr) return lds_frag_tr(tb, kc * 16, wn * 64 + ni * 32, lane);
+        else return lds_frag(tb, wn * 64 + ni * 32 + lane % 32, kc, lane);
+    };
+    auto compute = [&](int stage) {
+        const uint8_t* t_a = tile(stage, 0);
+        const uint8_t* t_b = tile(stage, 1);
+        const uint8_t* t_al = tile(stage, 2);
+        const uint8_t* t_bl = tile(stage, 3);
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
             u32x4 fa[2], fb[2];
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi) fa[mi] = lds_frag(t_a, wm * 64 + mi * 32 + lane % 32, kc, lane);
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni) fb[ni] = lds_frag(t_b, wn * 64 + ni * 32 + lane % 32, kc, lane);
+            for (int ni = 0; ni < 2; ++ni) fb[ni] = bfrag(t_b, ni, kc);
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -339,7 +446,7 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
 #pragma unroll
                 for (int mi = 0; mi < 2; ++mi) fal[mi] = lds_frag(t_al, wm * 64 + mi * 32 + lane % 32, kc, lane);
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni) fbl[ni] = lds_frag(t_bl, wn * 64 + ni * 32 + lane % 32, kc, lane);
+                for (int ni = 0; ni < 2; ++ni) fbl[ni] = bfrag(t_bl, ni, kc);
 #pragma unroll
                 for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -348,6 +455,56 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
                         mfma_chunk<PREC>(acc[mi][ni], fal[mi], fb[ni]);
                     }
             }
+        }
+    };
+
+    // The update's own output rows ti*128 .. +127 of X pass through the K loop
+    // as the B operand.  The K loop of the update starts right after them and
+    // wraps around, so they are its last two stages; the XLoader thread
+    // mapping (row t/16 + 16q, columns 8(t%16)) is the epilogue's row mapping,
+    // so each thread keeps those registers instead of reloading X from HBM.
+    constexpr bool kKeep = kTr && (kStages == 1) && (NS_KEEP_X != 0);
+    u32x4 keep_h[2][4], keep_l[2][4];
+    const int nk = K / kBK;
+    auto kstart = [&](int kt) -> int {
+        if constexpr (kKeep) return ((job.ti + 1) * kTile + kt * kBK) % K;
+        else return kt * kBK;
+    };
+    auto capture = [&](int kt) {
+        if constexpr (kKeep) {
+            if (kt == nk - 2) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) { keep_h[0][q] = lx.r[q]; if (kSplit) keep_l[0][q] = lxl.r[q]; }
+            }
+        }
+    };
+
+    if constexpr (kStages == 2) {
+        // LDS double buffer: one barrier per stage; the global loads of stage
+        // kt+2 are in flight while stage kt+1 waits in LDS and kt computes.
+        issue(0);
+        commit(0);
+        if (nk > 1) issue(kBK);
+        __syncthreads();
+        for (int kt = 0; kt < nk; ++kt) {
+            compute(kt & 1);
+            if (kt + 1 < nk) commit((kt + 1) & 1);
+            if (kt + 2 < nk) issue((kt + 2) * kBK);
+            __syncthreads();
+        }
+    } else {
+        issue(kstart(0));
+        for (int kt = 0; kt < nk; ++kt) {
+            __syncthreads();
+            commit(0);
+            capture(kt);
+            __syncthreads();
+            if (kt + 1 < nk) issue(kstart(kt + 1));
+            compute(0);
+        }
+        if constexpr (kKeep) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) { keep_h[1][q] = lx.r[q]; if (kSplit) keep_l[1][q] = lxl.r[q]; }
         }
     }
 
@@ -360,6 +517,7 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
     const float s = G.scale[job.slot];
     const float sc = (PHASE == kGram) ? (args.first ? s * s : 1.0f) : (args.first ? s : 1.0f);
     const int t = threadIdx.x;
+#pragma unroll
     for (int h = 0; h < 2; ++h) {
         __syncthreads();
         if (wm == h) {
@@ -408,22 +566,53 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
             } else {
                 const size_t idx = xplane + (size_t)(row_base + lr) * N + job.tj * kTile + lc;
                 float xh[8], xl[8];
-                load8<PREC>(G.x[src], idx, xh);
-                if constexpr (PREC == kNsBf16) load8<PREC>(G.xl[src], idx, xl);
+                if constexpr (kKeep) {
+                    unpack8(keep_h[h][p], xh);
+                    if constexpr (kSplit) unpack8(keep_l[h][p], xl);
+                    else load8<PREC>(G.xl[src], idx, xl);
+                } else {
+                    load8<PREC>(G.x[src], idx, xh);
+                    if constexpr (PREC == kNsBf16) load8<PREC>(G.xl[src], idx, xl);
+                }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float x = (PREC == kNsBf16) ? xh[e] + xl[e] : xh[e];
                     v[e] = sc * fmaf(args.a, x, v[e]);
                 }
-                store8<PREC>(G.x[src ^ 1], G.xl[src ^ 1], idx, v);
+                if (!FUSE) {
+                    store8<PREC>(G.x[src ^ 1], G.xl[src ^ 1], idx, v);
+                } else if (!args.apply[G.apply_begin + job.slot].transposed) {
+                    // X row = stored row, X column = stored column
+                    const FusedApply& F = args.apply[G.apply_begin + job.slot];
+                    const int gi = row_base + lr, gj = job.tj * kTile + lc;
+                    if (gi < F.rows) apply8(F, (size_t)gi * F.cols + gj, F.cols - gj, v, args.keep);
+                }
             }
-            if (PHASE != kUpdate && !diag) {
+            if ((PHASE != kUpdate && !diag) ||
+                (PHASE == kUpdate && FUSE && args.apply[G.apply_begin + job.slot].transposed)) {
                 // keep the final value for the mirrored write
                 floatx4 a, b;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) { a[e] = v[e]; b[e] = v[4 + e]; }
                 *reinterpret_cast<floatx4*>(sp) = a;
                 *reinterpret_cast<floatx4*>(sp + 4) = b;
+            }
+        }
+        if (PHASE == kUpdate && FUSE && args.apply[G.apply_begin + job.slot].transposed) {
+            __syncthreads();
+            // stored W is X^T: W row tj*128 + c, columns row_base + 8*chunk .. +7
+            const FusedApply& F = args.apply[G.apply_begin + job.slot];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int chunk = t % 8;
+                const int c = t / 8 + 32 * p;
+                const int wr = job.tj * kTile + c, wc = row_base + chunk * 8;
+                if (wr < F.rows && wc < F.cols) {
+                    float v[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = stage[(chunk * 8 + e) * kStagePitch + c];
+                    apply8(F, (size_t)wr * F.cols + wc, F.cols - wc, v, args.keep);
+                }
             }
         }
         if (PHASE != kUpdate && !diag) {
@@ -449,27 +638,38 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
 
 size_t ns_lds_bytes(int phase, int precision, bool comp) {
     const bool split = precision == kNsBf16 && (phase == kSquare || comp);
-    return split ? 4 * kTileBytes : 2 * kTileBytes;
+    const int stages = (split || NS_DOUBLE_BUFFER == 0) ? 1 : 2;
+    return (size_t)(split ? 4 : 2) * stages * kTileBytes;
 }
 
-template <int PHASE, int PREC, bool COMP>
+template <int PHASE, int PREC, bool COMP, bool FUSE>
 hipError_t launch_one(const NsArgs& a, hipStream_t s) {
     const size_t lds = ns_lds_bytes(PHASE, PREC, COMP);
     if (lds > 65536) {
         // more than the default 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU)
-        static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&ns_kernel<PHASE, PREC, COMP>),
+        static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&ns_kernel<PHASE, PREC, COMP, FUSE>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (attr != hipSuccess) return attr;
     }
     const int grid = (a.total_jobs + kXcds - 1) / kXcds * kXcds;
-    ns_kernel<PHASE, PREC, COMP><<<grid, kThreads, lds, s>>>(a);
+    ns_kernel<PHASE, PREC, COMP, FUSE><<<grid, kThreads, lds, s>>>(a);
     return hipGetLastError();
 }
 
 template <int PHASE>
 hipError_t launch_phase(const NsArgs& a, int precision, bool comp, hipStream_t s) {
-    if (precision == kNsFp32) return launch_one<PHASE, kNsFp32, false>(a, s);
-    return comp ? launch_one<PHASE, kNsBf16, true>(a, s) : launch_one<PHASE, kNsBf16, false>(a, s);
+    if (precision == kNsFp32) return launch_one<PHASE, kNsFp32, false, false>(a, s);
+    return comp ? launch_one<PHASE, kNsBf16, true, false>(a, s) : launch_one<PHASE, kNsBf16, false, false>(a, s);
+}
+
+template <>
+hipError_t launch_phase<kUpdate>(const NsArgs& a, int precision, bool comp, hipStream_t s) {
+    if (a.fuse_apply) {
+        if (precision == kNsFp32) return launch_one<kUpdate, kNsFp32, false, true>(a, s);
+        return comp ? launch_one<kUpdate, kNsBf16, true, true>(a, s) : launch_one<kUpdate, kNsBf16, false, true>(a, s);
+    }
+    if (precision == kNsFp32) return launch_one<kUpdate, kNsFp32, false, false>(a, s);
+    return comp ? launch_one<kUpdate, kNsBf16, true, false>(a, s) : launch_one<kUpdate, kNsBf16, false, false>(a, s);
 }
 
 }  // namespace
@@ -480,12 +680,13 @@ hipError_t launch_ns(const NsArgs& a, int phase, int precision, bool comp, hipSt
     return launch_phase<kUpdate>(a, precision, comp, s);
 }
 
-const char* ns_kernel_name(int phase, int precision, bool comp) {
-    static const char* names[3][3] = {{"ns_gram_bf16", "ns_square_bf16", "ns_update_bf16"},
-                                      {"ns_gram_bf16x3", "ns_square_bf16x3", "ns_update_bf16x3"},
-                                      {"ns_gram_fp32", "ns_square_fp32", "ns_update_fp32"}};
+const char* ns_kernel_name(int phase, int precision, bool comp, bool fused) {
+    static const char* names[3][4] = {
+        {"ns_gram_bf16", "ns_square_bf16", "ns_update_bf16", "ns_update_apply_bf16"},
+        {"ns_gram_bf16x3", "ns_square_bf16x3", "ns_update_bf16x3", "ns_update_apply_bf16x3"},
+        {"ns_gram_fp32", "ns_square_fp32", "ns_update_fp32", "ns_update_apply_fp32"}};
     const int v = precision == kNsFp32 ? 2 : (comp ? 1 : 0);
-    return names[v][phase];
+    return names[v][(phase == kUpdate && fused) ? 3 : phase];
 }
 
 }  // namespace muon

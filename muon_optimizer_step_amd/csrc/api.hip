@@ -115,9 +115,11 @@ struct Plan {
 };
 
 int transposed_rb(int cols) {
-    // stored rows per workgroup when X0 is the transpose: rb * (cols + 1) floats <= 16384
+    // stored rows per workgroup when X0 is the transpose: rb * (cols + 1) floats
+    // of LDS (at most 64 KiB; more costs occupancy), so that each X0 row
+    // segment a workgroup writes is rb * 2 bytes per bf16 plane
     int rb = 64;
-    while (rb > 1 && (size_t)rb * (cols + 1) > 16384) rb >>= 1;
+    while (rb > 1 && (size_t)rb * (cols + 1) * sizeof(float) > kTransposeLdsBytes) rb >>= 1;
     return rb;
 }
 

@@ -417,11 +417,23 @@ __global__ __launch_bounds__(kEmaThreads) void ema_kernel(const EmaArgs a) {
 
 }  // namespace
 
+template <typename K>
+hipError_t allow_lds(K kernel, size_t lds_bytes) {
+    // dynamic LDS beyond the default 64 KiB must be requested (gfx950: 160 KiB per CU)
+    if (lds_bytes <= 65536) return hipSuccess;
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)kTransposeLdsBytes);
+}
+
 hipError_t launch_prep(const PrepArgs& a, int precision, int blocks, size_t lds_bytes, hipStream_t s) {
-    if (precision == kNsBf16)
+    hipError_t e;
+    if (precision == kNsBf16) {
+        if ((e = allow_lds(&prep_kernel<kNsBf16>, lds_bytes)) != hipSuccess) return e;
         prep_kernel<kNsBf16><<<blocks, 256, lds_bytes, s>>>(a);
-    else
+    } else {
+        if ((e = allow_lds(&prep_kernel<kNsFp32>, lds_bytes)) != hipSuccess) return e;
         prep_kernel<kNsFp32><<<blocks, 256, lds_bytes, s>>>(a);
+    }
     return hipGetLastError();
 }
 
@@ -431,10 +443,14 @@ hipError_t launch_frob(const FrobArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_apply(const ApplyArgs& a, int precision, int blocks, size_t lds_bytes, hipStream_t s) {
-    if (precision == kNsBf16)
+    hipError_t e;
+    if (precision == kNsBf16) {
+        if ((e = allow_lds(&apply_kernel<kNsBf16>, lds_bytes)) != hipSuccess) return e;
         apply_kernel<kNsBf16><<<blocks, 256, lds_bytes, s>>>(a);
-    else
+    } else {
+        if ((e = allow_lds(&apply_kernel<kNsFp32>, lds_bytes)) != hipSuccess) return e;
         apply_kernel<kNsFp32><<<blocks, 256, lds_bytes, s>>>(a);
+    }
     return hipGetLastError();
 }
 

@@ -15,6 +15,7 @@ constexpr int kPrepChunk = 40;    // tensors per prep / apply launch
 constexpr int kFrobChunk = 256;   // matrices per Frobenius-scale launch
 constexpr int kEmaChunk = 112;    // tensors per EMA launch
 constexpr int kRowsPerWaveBlock = 4;  // stored rows per workgroup when no transpose is needed
+constexpr size_t kTransposeLdsBytes = 64 * 1024;  // LDS budget of the transposing prep / apply
 
 // ---------------------------------------------------------------- prep (K1)
 // Momentum update, optional row normalisation, per-row sum of squares, and the

@@ -37,6 +37,9 @@
 #ifndef NS_DOUBLE_BUFFER
 #define NS_DOUBLE_BUFFER 0   // 1: base kernels double-buffer their LDS stages (costs occupancy)
 #endif
+#ifndef NS_WIDE_STAGE
+#define NS_WIDE_STAGE 1      // bf16 base kernels stage 256 bytes of K per row
+#endif
 #ifndef NS_KEEP_X
 #define NS_KEEP_X 1          // bf16 update: the epilogue reuses the X rows its K loop loaded last
 #endif
@@ -49,16 +52,29 @@ namespace muon {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowBytes = 128;              // K bytes per LDS stage per row
-constexpr int kPitch = kRowBytes + 16;      // padded LDS row pitch (conflict-free b128 reads)
-constexpr int kTileBytes = kTile * kPitch;  // one 128-row operand tile
+constexpr int kXPitch = 256 + 32;           // row pitch of a natural-layout X stage (see XLoader)
+// K bytes per LDS stage per operand row: RB = 128 (64 bf16 / 32 fp32) or 256.
+// Rows are padded by 16 bytes, which keeps the b128 fragment reads conflict-free.
+template <int RB> struct Stage {
+    static constexpr int kPitch = RB + 16;
+    static constexpr int kBK = RB / 2;      // bf16 elements of K per stage
+    // one operand slot: 128 rows of K, or kBK rows of natural-layout X
+    static constexpr int kSlot = (kTile * kPitch > kBK * kXPitch) ? kTile * kPitch : kBK * kXPitch;
+};
 constexpr int kStagePitch = kTile + 4;      // fp32 epilogue staging row pitch
 constexpr int kStageBytes = 64 * kStagePitch * 4;  // half a tile (64 rows) of fp32
-static_assert(kStageBytes <= 2 * kTileBytes, "epilogue staging must fit in the operand LDS");
+static_assert(kStageBytes <= 2 * Stage<128>::kSlot, "epilogue staging must fit in the operand LDS");
+
+// K bytes per LDS stage: 256 for the bf16 base Gram, whose long contraction
+// gains from fewer, larger stages (two 128-row slots still fit 2 workgroups per
+// CU), 128 otherwise.
+constexpr int ns_stage_bytes(int phase, int precision, bool comp) {
+    return (precision == kNsBf16 && phase == kGram && !comp && NS_WIDE_STAGE != 0) ? 256 : 128;
+}
 
 template <int PREC> struct Elem;
-template <> struct Elem<kNsBf16> { typedef bf16 T; static constexpr int kBK = 64; };
-template <> struct Elem<kNsFp32> { typedef float T; static constexpr int kBK = 32; };
+template <> struct Elem<kNsBf16> { typedef bf16 T; };
+template <> struct Elem<kNsFp32> { typedef float T; };
 
 // Accumulate one 16-byte operand chunk per lane: bf16 -> one 32x32x16 MFMA;
 // fp32 -> four 32x32x2 MFMAs over the four components (the k permutation is the
@@ -78,23 +94,26 @@ __device__ inline void mfma_chunk(floatx16& acc, const u32x4& a, const u32x4& b)
     }
 }
 
-// 128 rows x 128 bytes of a row-major operand whose K index is contiguous
-// ("NT" operand).  Thread t moves 16 bytes of row t/8 + 32q, chunk t%8.
+// 128 rows x RB bytes of a row-major operand whose K index is contiguous
+// ("NT" operand).  Thread t moves 16 bytes of row t/C + (256/C)q, chunk t%C,
+// with C = RB/16 chunks per row.
+template <int RB>
 struct NtLoader {
-    u32x4 r[4];
+    static constexpr int C = RB / 16, Q = RB / 32;
+    u32x4 r[Q];
     __device__ inline void load(const uint8_t* base, size_t ld_bytes, int kbyte) {
         const int t = threadIdx.x;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint8_t* p = base + (size_t)(t / 8 + 32 * q) * ld_bytes + kbyte + (t % 8) * 16;
+        for (int q = 0; q < Q; ++q) {
+            const uint8_t* p = base + (size_t)(t / C + (256 / C) * q) * ld_bytes + kbyte + (t % C) * 16;
             r[q] = *reinterpret_cast<const u32x4*>(p);
         }
     }
     __device__ inline void store(uint8_t* lds) const {
         const int t = threadIdx.x;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<u32x4*>(lds + (t / 8 + 32 * q) * kPitch + (t % 8) * 16) = r[q];
+        for (int q = 0; q < Q; ++q)
+            *reinterpret_cast<u32x4*>(lds + (t / C + (256 / C) * q) * Stage<RB>::kPitch + (t % C) * 16) = r[q];
     }
 };
 
@@ -127,7 +146,7 @@ template <> struct TLoader<kNsBf16> {
                 const uint32_t hi_row = (c < 2) ? v[2 * p + 1].x : v[2 * p + 1].y;
                 w[p] = __builtin_amdgcn_perm(hi_row, lo_row, sel);
             }
-            *reinterpret_cast<u32x4*>(lds + (4 * jq + c) * kPitch + kb * 16) = w;
+            *reinterpret_cast<u32x4*>(lds + (4 * jq + c) * Stage<128>::kPitch + kb * 16) = w;
         }
     }
 };
@@ -148,29 +167,29 @@ template <> struct TLoader<kNsFp32> {
         for (int c = 0; c < 4; ++c) {
             floatx4 w;
             w[0] = v[0][c]; w[1] = v[1][c]; w[2] = v[2][c]; w[3] = v[3][c];
-            *reinterpret_cast<floatx4*>(lds + (4 * jq + c) * kPitch + kb * 16) = w;
+            *reinterpret_cast<floatx4*>(lds + (4 * jq + c) * Stage<128>::kPitch + kb * 16) = w;
         }
     }
 };
 
 // bf16 X[k][j] tile for the update's B operand kept in its natural layout:
-// 64 k-rows x 128 j (256 bytes) per stage, rows padded to kXPitch so that the
+// BK k-rows x 128 j (256 bytes) per stage, rows padded to kXPitch so that the
 // transposing LDS reads below are free of bank conflicts.  Thread t moves 16
 // bytes: row t/16 + 16q, column chunk t%16.
-constexpr int kXPitch = 256 + 32;
-static_assert(64 * kXPitch <= kTileBytes, "X stage must fit one operand tile slot");
+template <int BK>
 struct XLoader {
-    u32x4 r[4];
+    static constexpr int Q = BK / 16;
+    u32x4 r[Q];
     __device__ inline void load(const bf16* x, size_t ld, int k0, int j0) {
         const int t = threadIdx.x;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < Q; ++q)
             r[q] = *reinterpret_cast<const u32x4*>(x + (size_t)(k0 + t / 16 + 16 * q) * ld + j0 + 8 * (t % 16));
     }
     __device__ inline void store(uint8_t* lds) const {
         const int t = threadIdx.x;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < Q; ++q)
             *reinterpret_cast<u32x4*>(lds + (t / 16 + 16 * q) * kXPitch + (t % 16) * 16) = r[q];
     }
 };
@@ -195,8 +214,9 @@ __device__ inline u32x4 lds_frag_tr(const uint8_t* tile, int k0, int j0, int lan
     return r;
 }
 
+template <int RB>
 __device__ inline u32x4 lds_frag(const uint8_t* tile, int row, int kc, int lane) {
-    return *reinterpret_cast<const u32x4*>(tile + row * kPitch + kc * 32 + (lane / 32) * 16);
+    return *reinterpret_cast<const u32x4*>(tile + row * Stage<RB>::kPitch + kc * 32 + (lane / 32) * 16);
 }
 
 struct Job {
@@ -314,9 +334,12 @@ __device__ inline void apply8(const FusedApply& F, size_t idx, int count, const 
 template <int PHASE, int PREC, bool COMP, bool FUSE>
 __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
     typedef typename Elem<PREC>::T T;
-    constexpr int kBK = Elem<PREC>::kBK;
     // operands carry a lo plane (and the MFMAs run hi*hi + hi*lo + lo*hi)
     constexpr bool kSplit = (PREC == kNsBf16) && (PHASE == kSquare || COMP);
+    constexpr bool kTr = (PHASE == kUpdate) && (PREC == kNsBf16) && (NS_TRANSPOSE_READ != 0);
+    constexpr int kRB = ns_stage_bytes(PHASE, PREC, COMP);   // K bytes per stage per row
+    constexpr int kBK = kRB / (int)sizeof(T);                 // K elements per stage
+    constexpr int kSlot = Stage<kRB>::kSlot;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     Job job;
@@ -335,13 +358,12 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
     // B-side rows, [2] / [3] the lo planes.  On diagonal tiles both sides are
     // the same rows.  The bf16 update keeps its X tile in natural [k][j] layout
     // and reads it with transposing LDS loads.
-    constexpr bool kTr = (PHASE == kUpdate) && (PREC == kNsBf16) && (NS_TRANSPOSE_READ != 0);
     constexpr int kStages = (kSplit || NS_DOUBLE_BUFFER == 0) ? 1 : 2;
     constexpr int kStageTiles = kSplit ? 4 : 2;
     auto tile = [&](int stage, int which) -> uint8_t* {
         if (diag && which == 1) which = 0;
         if (diag && which == 3) which = 2;
-        return lds + (stage * kStageTiles + which) * kTileBytes;
+        return lds + (stage * kStageTiles + which) * kSlot;
     };
 
     const uint8_t *ga = nullptr, *gb = nullptr, *gal = nullptr, *gbl = nullptr;
@@ -385,9 +407,9 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
-    NtLoader la, lb, lal, lbl;
+    NtLoader<kRB> la, lb, lal, lbl;
     TLoader<PREC> lt, ltl;
-    XLoader lx, lxl;
+    XLoader<kBK> lx, lxl;
     auto issue = [&](int k0) {
         const int kbyte = k0 * (int)sizeof(T);
         la.load(ga, ld_bytes, kbyte);
@@ -423,7 +445,7 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
     };
     auto bfrag = [&](const uint8_t* tb, int ni, int kc) -> u32x4 {
         if constexpr (kTr) return lds_frag_tr(tb, kc * 16, wn * 64 + ni * 32, lane);
-        else return lds_frag(tb, wn * 64 + ni * 32 + lane % 32, kc, lane);
+        else return lds_frag<kRB>(tb, wn * 64 + ni * 32 + lane % 32, kc, lane);
     };
     auto compute = [&](int stage) {
         const uint8_t* t_a = tile(stage, 0);
@@ -431,10 +453,10 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
         const uint8_t* t_al = tile(stage, 2);
         const uint8_t* t_bl = tile(stage, 3);
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
+        for (int kc = 0; kc < kRB / 32; ++kc) {
             u32x4 fa[2], fb[2];
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi) fa[mi] = lds_frag(t_a, wm * 64 + mi * 32 + lane % 32, kc, lane);
+            for (int mi = 0; mi < 2; ++mi) fa[mi] = lds_frag<kRB>(t_a, wm * 64 + mi * 32 + lane % 32, kc, lane);
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni) fb[ni] = bfrag(t_b, ni, kc);
 #pragma unroll
@@ -444,7 +466,7 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
             if (kSplit) {
                 u32x4 fal[2], fbl[2];
 #pragma unroll
-                for (int mi = 0; mi < 2; ++mi) fal[mi] = lds_frag(t_al, wm * 64 + mi * 32 + lane % 32, kc, lane);
+                for (int mi = 0; mi < 2; ++mi) fal[mi] = lds_frag<kRB>(t_al, wm * 64 + mi * 32 + lane % 32, kc, lane);
 #pragma unroll
                 for (int ni = 0; ni < 2; ++ni) fbl[ni] = bfrag(t_bl, ni, kc);
 #pragma unroll
@@ -464,6 +486,7 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
     // mapping (row t/16 + 16q, columns 8(t%16)) is the epilogue's row mapping,
     // so each thread keeps those registers instead of reloading X from HBM.
     constexpr bool kKeep = kTr && (kStages == 1) && (NS_KEEP_X != 0);
+    constexpr int kOwnStages = kTile / kBK;   // stages holding the tile's own rows (1 or 2)
     u32x4 keep_h[2][4], keep_l[2][4];
     const int nk = K / kBK;
     auto kstart = [&](int kt) -> int {
@@ -471,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
         else return kt * kBK;
     };
     auto capture = [&](int kt) {
-        if constexpr (kKeep) {
+        if constexpr (kKeep && kOwnStages == 2) {
             if (kt == nk - 2) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) { keep_h[0][q] = lx.r[q]; if (kSplit) keep_l[0][q] = lxl.r[q]; }
@@ -503,8 +526,17 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
             compute(0);
         }
         if constexpr (kKeep) {
+            // the last stage: rows ti*128 + 64 .. +127, or the whole 128 rows
+            constexpr int base = (kOwnStages == 2) ? 0 : 4;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) { keep_h[1][q] = lx.r[q]; if (kSplit) keep_l[1][q] = lxl.r[q]; }
+            for (int q = 0; q < 4; ++q) {
+                keep_h[1][q] = lx.r[base + q];
+                if (kSplit) keep_l[1][q] = lxl.r[base + q];
+                if (kOwnStages == 1) {
+                    keep_h[0][q] = lx.r[q];
+                    if (kSplit) keep_l[0][q] = lxl.r[q];
+                }
+            }
         }
     }
 
@@ -639,7 +671,8 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
 size_t ns_lds_bytes(int phase, int precision, bool comp) {
     const bool split = precision == kNsBf16 && (phase == kSquare || comp);
     const int stages = (split || NS_DOUBLE_BUFFER == 0) ? 1 : 2;
-    return (size_t)(split ? 4 : 2) * stages * kTileBytes;
+    const int slot = ns_stage_bytes(phase, precision, comp) == 256 ? Stage<256>::kSlot : Stage<128>::kSlot;
+    return (size_t)(split ? 4 : 2) * stages * slot;
 }
 
 template <int PHASE, int PREC, bool COMP, bool FUSE>

@@ -37,6 +37,9 @@
 #ifndef NS_DOUBLE_BUFFER
 #define NS_DOUBLE_BUFFER 0   // 1: base kernels double-buffer their LDS stages (costs occupancy)
 #endif
+#ifndef NS_PREFETCH_XL
+#define NS_PREFETCH_XL 1     // bf16 update / square: fetch the epilogue's inputs before staging
+#endif
 #ifndef NS_WIDE_STAGE
 #define NS_WIDE_STAGE 1      // bf16 base kernels stage 256 bytes of K per row
 #endif
@@ -546,11 +549,38 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
     // row each with 16-byte global accesses, and symmetric outputs also write
     // the mirrored tile from the staged columns.
     float* stage = reinterpret_cast<float*>(lds);
+    // Base bf16 update: the lo plane of X for both halves is fetched before the
+    // accumulators are staged, so one memory latency overlaps the LDS work.
+    constexpr bool kPreXl = kKeep && !kSplit && (NS_PREFETCH_XL != 0);
+    u32x4 xl_pre[2][4];
+    if constexpr (kPreXl) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const size_t idx = xplane + (size_t)(job.ti * kTile + h * 64 + threadIdx.x / 16 + 16 * p) * N +
+                                   job.tj * kTile + 8 * (threadIdx.x % 16);
+                xl_pre[h][p] = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(G.xl[src]) + idx);
+            }
+    }
     const float s = G.scale[job.slot];
     const float sc = (PHASE == kGram) ? (args.first ? s * s : 1.0f) : (args.first ? s : 1.0f);
     const int t = threadIdx.x;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+        // the square's epilogue input (A hi and lo of this half) is in flight
+        // while the accumulators are staged
+        constexpr bool kPreA = (PHASE == kSquare) && (PREC == kNsBf16) && (NS_PREFETCH_XL != 0);
+        u32x4 a_pre[2][4];
+        if constexpr (kPreA) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const size_t idx = aplane + (size_t)(job.ti * kTile + h * 64 + threadIdx.x / 16 + 16 * p) * M +
+                                   job.tj * kTile + 8 * (threadIdx.x % 16);
+                a_pre[0][p] = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(G.a_hi) + idx);
+                a_pre[1][p] = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(G.a_lo) + idx);
+            }
+        }
         __syncthreads();
         if (wm == h) {
 #pragma unroll
@@ -587,8 +617,13 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
             } else if (PHASE == kSquare) {
                 const size_t idx = (size_t)(row_base + lr) * M + job.tj * kTile + lc;
                 float ah[8], al[8];
-                load8<PREC>(static_cast<const T*>(G.a_hi) + aplane, idx, ah);
-                if constexpr (PREC == kNsBf16) load8<PREC>(static_cast<const T*>(G.a_lo) + aplane, idx, al);
+                if constexpr (kPreA) {
+                    unpack8(a_pre[0][p], ah);
+                    unpack8(a_pre[1][p], al);
+                } else {
+                    load8<PREC>(static_cast<const T*>(G.a_hi) + aplane, idx, ah);
+                    if constexpr (PREC == kNsBf16) load8<PREC>(static_cast<const T*>(G.a_lo) + aplane, idx, al);
+                }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float a = (PREC == kNsBf16) ? ah[e] + al[e] : ah[e];
@@ -601,6 +636,7 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
                 if constexpr (kKeep) {
                     unpack8(keep_h[h][p], xh);
                     if constexpr (kSplit) unpack8(keep_l[h][p], xl);
+                    else if constexpr (kPreXl) unpack8(xl_pre[h][p], xl);
                     else load8<PREC>(G.xl[src], idx, xl);
                 } else {
                     load8<PREC>(G.x[src], idx, xh);

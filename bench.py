@@ -42,7 +42,66 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter files of this bench and of "
+                         "--calibrate-copy into profiles/hbm_traffic.json, then exit (no GPU needed)")
     return ap.parse_args()
+
+
+def _kernel_key(name: str) -> str:
+    """Library kernel symbol -> the name the profiling hook reports."""
+    import re
+    m = re.search(r"ns_kernel<(\d), (\d), (true|false), (true|false)>", name)
+    if m:
+        phase, prec, comp, fuse = int(m.group(1)), int(m.group(2)), m.group(3) == "true", m.group(4) == "true"
+        base = ["ns_gram", "ns_square", "ns_update", "ns_update"][phase]
+        if phase == 2 and fuse:
+            base = "ns_update_apply"
+        return base + ("_fp32" if prec == 1 else ("_bf16x3" if comp else "_bf16"))
+    for k in ("prep_kernel", "apply_kernel", "ema_kernel", "frob_kernel"):
+        if k in name:
+            return k.replace("_kernel", "")
+    return "copy" if "copyBuffer" in name else name
+
+
+def _per_dispatch(path: str, counter: str):
+    """{kernel: mean counter value per dispatch} from a rocprofv3 counter_collection.csv."""
+    import csv
+    import collections
+    tot = collections.defaultdict(float)
+    disp = collections.defaultdict(set)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            k = _kernel_key(r["Kernel_Name"])
+            tot[k] += float(r["Counter_Value"])
+            disp[k].add(r["Dispatch_Id"])
+    return {k: tot[k] / len(disp[k]) for k in tot}
+
+
+def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes=1 << 30):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by the copy calibration."""
+    cf = _per_dispatch(copy_fetch_csv, "FETCH_SIZE").get("copy")
+    cw = _per_dispatch(copy_write_csv, "WRITE_SIZE").get("copy")
+    f_scale = copy_bytes / (cf * 1024.0)
+    w_scale = copy_bytes / (cw * 1024.0)
+    fetch = _per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = _per_dispatch(write_csv, "WRITE_SIZE")
+    kernels = {}
+    for k in sorted(set(fetch) & set(write)):
+        if k == "copy":
+            continue
+        fb = fetch[k] * 1024.0 * f_scale
+        wb = write[k] * 1024.0 * w_scale
+        kernels[k] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb)}
+    out = {"source_hash": source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,
+           "calibration": f"{copy_bytes} B device-to-device copy (5 runs): FETCH_SIZE {cf:.0f} KiB, WRITE_SIZE {cw:.0f} KiB per dispatch",
+           "kernels": kernels}
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def calibrate_copy(mib: int) -> None:
@@ -155,6 +214,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
         return
     import numpy as np
     import torch

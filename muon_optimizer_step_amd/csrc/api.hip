@@ -297,8 +297,11 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
     const int prec = ns_precision == MUON_NS_FP32 ? kNsFp32 : kNsBf16;  // storage precision
     hipError_t err;
 
-    // ---- prep: momentum, row norm, X0 (short side first, zero padded)
-    for (int c0 = 0; c0 < n; c0 += kPrepChunk) {
+    // ---- prep: momentum, row norm, X0 (short side first, zero padded), in
+    // evenly sized launches of at most kPrepChunk tensors
+    const int prep_launches = (n + kPrepChunk - 1) / kPrepChunk;
+    const int prep_take = (n + prep_launches - 1) / prep_launches;
+    for (int c0 = 0; c0 < n;) {
         PrepArgs a;
         memset(&a, 0, sizeof(a));
         a.mu = momentum;
@@ -306,7 +309,8 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
         a.row_norm = row_norm;
         int blocks = 0;
         size_t lds = 0;
-        for (int i = c0; i < std::min(n, c0 + kPrepChunk); ++i) {
+        for (int k = 0; k < prep_take && c0 < n; ++k, ++c0) {
+            const int i = c0;
             const muon_tensor_t& x = tensors[i];
             const Group& G = p.groups[p.group_of[i]];
             PrepTensor& T = a.t[a.n++];

@@ -91,22 +91,20 @@ __device__ inline float4 load_x4(const void* xh, const void* xl, size_t idx) {
     }
 }
 
-constexpr int kRegVec = 16;  // float4 per lane kept in registers: rows of up to 4096 floats
-
-// One stored row of up to 4 * 64 * kRegVec floats (cols % 4 == 0, 16-byte
+// One stored row of up to 4 * 64 * RV floats (cols % 4 == 0, 16-byte
 // aligned), one wavefront, a single pass over G and M: M' is written at once,
 // U stays in registers until the row norm is known, then r = U/(|U|+eps) (or U)
 // is handed to emit4 four elements at a time.  Returns sum(r^2) on every lane.
-template <typename Emit4>
+template <int RV, typename Emit4>
 __device__ inline float process_row_regs(const float* __restrict__ g, float* __restrict__ m, int cols, float mu,
                                          int nesterov, int row_norm, int lane, Emit4 emit4) {
     const float4* g4 = reinterpret_cast<const float4*>(g);
     float4* m4 = reinterpret_cast<float4*>(m);
     const int nv = cols / 4;
-    float4 u[kRegVec];
+    float4 u[RV];
     float ss = 0.f;
 #pragma unroll
-    for (int v = 0; v < kRegVec; ++v) {
+    for (int v = 0; v < RV; ++v) {
         const int j = lane + v * kWave;
         if (j < nv) {
             const float4 gv = g4[j], mv = m4[j];
@@ -124,7 +122,7 @@ __device__ inline float process_row_regs(const float* __restrict__ g, float* __r
     const float denom = sqrtf(ss) + kEps;
     float rs = 0.f;
 #pragma unroll
-    for (int v = 0; v < kRegVec; ++v) {
+    for (int v = 0; v < RV; ++v) {
         const int j = lane + v * kWave;
         if (j < nv) {
             float4 r = u[v];
@@ -194,7 +192,9 @@ __device__ inline float process_row(const float* __restrict__ g, float* __restri
     return wave_sum(rs);
 }
 
-template <int PREC>
+// RV: float4 per lane a row may keep in registers (rows of up to 256 * RV floats
+// take the single-pass path; longer rows re-read G and M).
+template <int PREC, int RV>
 __global__ __launch_bounds__(256) void prep_kernel(const PrepArgs a) {
     extern __shared__ float lds_rows[];
     const int ti = find_tensor(a.t, a.n, blockIdx.x);
@@ -213,9 +213,9 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepArgs a) {
             const float* g = T.grad + (size_t)row * T.cols;
             float* m = T.mom + (size_t)row * T.cols;
             float rs;
-            if (T.vec && T.cols <= 4 * kWave * kRegVec) {
-                rs = process_row_regs(g, m, T.cols, a.mu, a.nesterov, a.row_norm, lane,
-                                      [&](int j, float4 r) { store_x4<PREC>(T.xh, T.xl, xrow + j, r); });
+            if (T.vec && T.cols <= 4 * kWave * RV) {
+                rs = process_row_regs<RV>(g, m, T.cols, a.mu, a.nesterov, a.row_norm, lane,
+                                          [&](int j, float4 r) { store_x4<PREC>(T.xh, T.xl, xrow + j, r); });
                 const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
                 for (int j = T.cols + 4 * lane; j < T.n_pad; j += 4 * kWave) store_x4<PREC>(T.xh, T.xl, xrow + j, z);
             } else {
@@ -244,8 +244,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepArgs a) {
             const float* g = T.grad + (size_t)row * T.cols;
             float* m = T.mom + (size_t)row * T.cols;
             float rs;
-            if (T.vec && T.cols <= 4 * kWave * kRegVec) {
-                rs = process_row_regs(g, m, T.cols, a.mu, a.nesterov, a.row_norm, lane, [&](int j, float4 r) {
+            if (T.vec && T.cols <= 4 * kWave * RV) {
+                rs = process_row_regs<RV>(g, m, T.cols, a.mu, a.nesterov, a.row_norm, lane, [&](int j, float4 r) {
                     dst[j] = r.x; dst[j + 1] = r.y; dst[j + 2] = r.z; dst[j + 3] = r.w;
                 });
             } else {
@@ -425,16 +425,27 @@ hipError_t allow_lds(K kernel, size_t lds_bytes) {
                                (int)kTransposeLdsBytes);
 }
 
-hipError_t launch_prep(const PrepArgs& a, int precision, int blocks, size_t lds_bytes, hipStream_t s) {
-    hipError_t e;
-    if (precision == kNsBf16) {
-        if ((e = allow_lds(&prep_kernel<kNsBf16>, lds_bytes)) != hipSuccess) return e;
-        prep_kernel<kNsBf16><<<blocks, 256, lds_bytes, s>>>(a);
-    } else {
-        if ((e = allow_lds(&prep_kernel<kNsFp32>, lds_bytes)) != hipSuccess) return e;
-        prep_kernel<kNsFp32><<<blocks, 256, lds_bytes, s>>>(a);
-    }
+template <int PREC, int RV>
+hipError_t launch_prep_rv(const PrepArgs& a, int blocks, size_t lds_bytes, hipStream_t s) {
+    hipError_t e = allow_lds(&prep_kernel<PREC, RV>, lds_bytes);
+    if (e != hipSuccess) return e;
+    prep_kernel<PREC, RV><<<blocks, 256, lds_bytes, s>>>(a);
     return hipGetLastError();
+}
+
+template <int PREC>
+hipError_t launch_prep_prec(const PrepArgs& a, int max_cols, int blocks, size_t lds_bytes, hipStream_t s) {
+    // the register row buffer sized to the widest row of the launch keeps occupancy up
+    if (max_cols <= 1024) return launch_prep_rv<PREC, 4>(a, blocks, lds_bytes, s);
+    if (max_cols <= 2048) return launch_prep_rv<PREC, 8>(a, blocks, lds_bytes, s);
+    return launch_prep_rv<PREC, 16>(a, blocks, lds_bytes, s);
+}
+
+hipError_t launch_prep(const PrepArgs& a, int precision, int blocks, size_t lds_bytes, hipStream_t s) {
+    int max_cols = 0;
+    for (int i = 0; i < a.n; ++i) max_cols = max(max_cols, a.t[i].cols);
+    if (precision == kNsBf16) return launch_prep_prec<kNsBf16>(a, max_cols, blocks, lds_bytes, s);
+    return launch_prep_prec<kNsFp32>(a, max_cols, blocks, lds_bytes, s);
 }
 
 hipError_t launch_frob(const FrobArgs& a, hipStream_t s) {

@@ -11,7 +11,7 @@
 namespace muon {
 
 constexpr int kMaxGroups = 12;    // NS shape groups per NS launch
-constexpr int kPrepChunk = 40;    // tensors per prep / apply launch
+constexpr int kPrepChunk = 52;    // tensors per prep / apply launch
 constexpr int kFrobChunk = 256;   // matrices per Frobenius-scale launch
 constexpr int kEmaChunk = 112;    // tensors per EMA launch
 constexpr int kRowsPerWaveBlock = 4;  // stored rows per workgroup when no transpose is needed

@@ -40,6 +40,9 @@
 #ifndef NS_PREFETCH_XL
 #define NS_PREFETCH_XL 1     // bf16 update / square: fetch the epilogue's inputs before staging
 #endif
+#ifndef NS_WIDE_UPDATE
+#define NS_WIDE_UPDATE 0     // 1: the bf16 base update stages 256 bytes of K too
+#endif
 #ifndef NS_WIDE_STAGE
 #define NS_WIDE_STAGE 1      // bf16 base kernels stage 256 bytes of K per row
 #endif
@@ -72,7 +75,8 @@ static_assert(kStageBytes <= 2 * Stage<128>::kSlot, "epilogue staging must fit i
 // gains from fewer, larger stages (two 128-row slots still fit 2 workgroups per
 // CU), 128 otherwise.
 constexpr int ns_stage_bytes(int phase, int precision, bool comp) {
-    return (precision == kNsBf16 && phase == kGram && !comp && NS_WIDE_STAGE != 0) ? 256 : 128;
+    return (precision == kNsBf16 && !comp && NS_WIDE_STAGE != 0 &&
+            (phase == kGram || (phase == kUpdate && NS_WIDE_UPDATE != 0 && NS_TRANSPOSE_READ != 0))) ? 256 : 128;
 }
 
 template <int PREC> struct Elem;

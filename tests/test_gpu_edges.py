@@ -163,3 +163,17 @@ def test_ema_layouts_and_chunking():
         if decay == 1.0:
             assert all(np.array_equal(gu.host(E[i]), e0[i]) for i in range(len(e0)))
         big_e[1:].copy_(gu.dev(rng.standard_normal(10000).astype(np.float32)))
+
+
+def test_more_matrices_than_the_fused_apply_table():
+    """80 matrices of one shape: the last NS launch cannot carry all weight
+    updates, so the separate apply kernel runs after the iteration."""
+    rng = np.random.default_rng(21)
+    shapes = [(64, 96)] * 80
+    mats = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    grads = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    moms = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    w_gpu, m_gpu, o_gpu = gu.gpu_step(mats, grads, moms, lr=0.03, momentum=0.9, wd=0.1, coeffs=STD)
+    for i in range(0, 80, 7):
+        gu.check_layers(mats[i], grads[i], moms[i], w_gpu[i], m_gpu[i], o_gpu[i], lr=0.03, momentum=0.9, wd=0.1,
+                        coeffs=STD, nesterov=True, row_norm=True, ns_tol=gu.NS_TOL_BF16, label=f"{i}")

@@ -94,6 +94,40 @@ hipError_t timed_launch(const char* name, hipStream_t s, F launch) {
     return hipSuccess;
 }
 
+// ------------------------------------------------------------- NS lanes
+// Shape groups are independent NS problems.  The groups are spread over up to
+// kLanes streams (the caller's stream and internal non-blocking streams of
+// default priority), forked from and joined back into the caller's stream with
+// events, so that short chains (small matrices) fill the compute units the
+// long ones leave idle.  Nothing waits on the host.
+#ifndef NS_LANES
+#define NS_LANES 2
+#endif
+constexpr int kLanes = NS_LANES;
+struct LaneSet {
+    hipStream_t stream[kLanes] = {};   // [0] unused: lane 0 is the caller's stream
+    hipEvent_t fork = nullptr;
+    hipEvent_t join[kLanes] = {};
+    bool ready = false;
+};
+std::mutex g_lane_mu;
+std::map<int, LaneSet> g_lanes;
+
+hipError_t lanes_for_device(int dev, LaneSet*& out) {
+    LaneSet& L = g_lanes[dev];
+    if (!L.ready) {
+        hipError_t e;
+        for (int i = 1; i < kLanes; ++i) {
+            if ((e = hipStreamCreateWithFlags(&L.stream[i], hipStreamNonBlocking)) != hipSuccess) return e;
+            if ((e = hipEventCreateWithFlags(&L.join[i], hipEventDisableTiming)) != hipSuccess) return e;
+        }
+        if ((e = hipEventCreateWithFlags(&L.fork, hipEventDisableTiming)) != hipSuccess) return e;
+        L.ready = true;
+    }
+    out = &L;
+    return hipSuccess;
+}
+
 // ------------------------------------------------------------- planning
 struct Group {
     int m, n;        // short side, long side
@@ -359,84 +393,133 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
         if (err != hipSuccess) return fail(MUON_ERR_HIP, "frob launch failed: %s", hipGetErrorString(err));
     }
 
-    // ---- Newton-Schulz iterations: per phase, one launch for the base groups and
-    // one for the compensated groups (each skipped when empty)
+    // ---- Newton-Schulz iterations.  Groups go to lanes (longest first onto the
+    // least loaded lane by NS flops); within a lane, one launch per phase for
+    // its base groups and one for its compensated groups (each skipped when
+    // empty), kMaxGroups groups per launch.
     const int ngroups = (int)p.groups.size();
-    // The weight update runs inside the last NS update launch when every launch
-    // of that phase has at most kMaxFused matrices.
-    bool fuse = ns_steps > 0;
-    for (int comp = 0; comp < 2 && fuse; ++comp) {
-        std::vector<int> gl;
-        for (int g = 0; g < ngroups; ++g)
-            if ((int)p.groups[g].comp == comp) gl.push_back(g);
-        for (size_t g0 = 0; g0 < gl.size(); g0 += kMaxGroups) {
-            int cnt = 0;
-            for (size_t q = g0; q < std::min(gl.size(), g0 + kMaxGroups); ++q) cnt += p.groups[gl[q]].count;
-            if (cnt > kMaxFused) fuse = false;
+    const int nlanes = std::min(kLanes, ngroups);
+    std::vector<int> lane_of(ngroups, 0);
+    {
+        std::vector<std::pair<double, int>> work;
+        for (int g = 0; g < ngroups; ++g) {
+            const Group& G = p.groups[g];
+            work.push_back({(double)G.count * (4.0 * G.M * G.M * G.N + 2.0 * G.M * G.M * (double)G.M), g});
         }
+        std::sort(work.begin(), work.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
+        std::vector<double> load(nlanes, 0.0);
+        for (const auto& wg : work) {
+            const int l = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+            lane_of[wg.second] = l;
+            load[l] += wg.first;
+        }
+    }
+    // launches: (lane, comp, chunk of groups)
+    struct NsLaunchSet {
+        int lane, comp;
+        std::vector<int> groups;
+    };
+    std::vector<NsLaunchSet> sets;
+    for (int l = 0; l < nlanes; ++l)
+        for (int comp = 0; comp < 2; ++comp) {
+            std::vector<int> gl;
+            for (int g = 0; g < ngroups; ++g)
+                if (lane_of[g] == l && (int)p.groups[g].comp == comp) gl.push_back(g);
+            for (size_t g0 = 0; g0 < gl.size(); g0 += kMaxGroups)
+                sets.push_back({l, comp, std::vector<int>(gl.begin() + g0, gl.begin() + std::min(gl.size(), g0 + kMaxGroups))});
+        }
+    // The weight update runs inside the last NS update launch when every launch
+    // holds at most kMaxFused matrices.
+    bool fuse = ns_steps > 0;
+    for (const NsLaunchSet& ls : sets) {
+        int cnt = 0;
+        for (int g : ls.groups) cnt += p.groups[g].count;
+        if (cnt > kMaxFused) fuse = false;
     }
     const float keep = 1.0f - lr * weight_decay;
     auto lr_scale = [&](const muon_tensor_t& x) {
         return lr * (float)std::sqrt(std::max(1.0, (double)x.rows / (double)x.cols));
     };
+
+    std::unique_lock<std::mutex> lane_lock(g_lane_mu, std::defer_lock);
+    hipStream_t lane_stream[kLanes] = {s};
+    LaneSet* L = nullptr;
+    if (ns_steps > 0 && nlanes > 1) {
+        lane_lock.lock();
+        int dev = 0;
+        err = hipGetDevice(&dev);
+        if (err == hipSuccess) err = lanes_for_device(dev, L);
+        if (err == hipSuccess) err = hipEventRecord(L->fork, s);
+        for (int l = 1; l < nlanes && err == hipSuccess; ++l) {
+            lane_stream[l] = L->stream[l];
+            err = hipStreamWaitEvent(lane_stream[l], L->fork, 0);
+        }
+        if (err != hipSuccess) return fail(MUON_ERR_HIP, "NS lane fork failed: %s", hipGetErrorString(err));
+    }
+
     for (int k = 0; k < ns_steps; ++k) {
         for (int phase = kGram; phase <= kUpdate; ++phase) {
-            for (int comp = 0; comp < 2; ++comp) {
-                std::vector<int> gl;
-                for (int g = 0; g < ngroups; ++g)
-                    if ((int)p.groups[g].comp == comp) gl.push_back(g);
-                for (size_t g0 = 0; g0 < gl.size(); g0 += kMaxGroups) {
-                    NsArgs a;
-                    memset(&a, 0, sizeof(a));
-                    a.src = k & 1;
-                    a.first = (k == 0);
-                    a.a = ns_coeffs[3 * k + 0];
-                    a.b = ns_coeffs[3 * k + 1];
-                    a.c = ns_coeffs[3 * k + 2];
-                    a.fuse_apply = fuse && phase == kUpdate && k == ns_steps - 1;
-                    a.keep = keep;
-                    int jobs = 0, napply = 0;
-                    for (size_t q = g0; q < std::min(gl.size(), g0 + kMaxGroups); ++q) {
-                        const Group& G = p.groups[gl[q]];
-                        NsGroup& D = a.g[a.ngroups++];
-                        for (int b = 0; b < 2; ++b) {
-                            D.x[b] = ws + G.x_off[b];
-                            D.xl[b] = ws + G.xl_off[b];
-                        }
-                        D.a_hi = ws + G.ah_off;
-                        D.a_lo = ws + G.al_off;
-                        D.b = ws + G.b_off;
-                        D.b_lo = ws + G.bl_off;
-                        D.scale = reinterpret_cast<const float*>(ws + p.scale_base) + G.scale_begin;
-                        D.count = G.count;
-                        D.M = G.M;
-                        D.N = G.N;
-                        D.job_begin = jobs;
-                        D.apply_begin = napply;
-                        if (a.fuse_apply) {
-                            for (int ti : p.members[gl[q]]) {
-                                const muon_tensor_t& x = tensors[ti];
-                                FusedApply& F = a.apply[napply++];
-                                F.param = x.param;
-                                F.out = x.update_out;
-                                F.rows = x.rows;
-                                F.cols = x.cols;
-                                F.transposed = x.rows > x.cols;
-                                F.vec = (x.cols % 4 == 0) && (reinterpret_cast<uintptr_t>(x.param) % 16 == 0) &&
-                                        (reinterpret_cast<uintptr_t>(x.update_out) % 16 == 0);
-                                F.lr_s = lr_scale(x);
-                            }
-                        }
-                        const int tm = G.M / kTile, tn = G.N / kTile;
-                        jobs += G.count * (phase == kUpdate ? tm * tn : tm * (tm + 1) / 2);
+            for (const NsLaunchSet& ls : sets) {
+                hipStream_t ls_stream = lane_stream[ls.lane];
+                NsArgs a;
+                memset(&a, 0, sizeof(a));
+                a.src = k & 1;
+                a.first = (k == 0);
+                a.a = ns_coeffs[3 * k + 0];
+                a.b = ns_coeffs[3 * k + 1];
+                a.c = ns_coeffs[3 * k + 2];
+                a.fuse_apply = fuse && phase == kUpdate && k == ns_steps - 1;
+                a.keep = keep;
+                int jobs = 0, napply = 0;
+                for (int gi : ls.groups) {
+                    const Group& G = p.groups[gi];
+                    NsGroup& D = a.g[a.ngroups++];
+                    for (int b = 0; b < 2; ++b) {
+                        D.x[b] = ws + G.x_off[b];
+                        D.xl[b] = ws + G.xl_off[b];
                     }
-                    a.total_jobs = jobs;
-                    const char* name = ns_kernel_name(phase, prec, comp != 0, a.fuse_apply != 0);
-                    err = timed_launch(name, s, [&] { return launch_ns(a, phase, prec, comp != 0, s); });
-                    if (err != hipSuccess) return fail(MUON_ERR_HIP, "%s launch failed: %s", name, hipGetErrorString(err));
+                    D.a_hi = ws + G.ah_off;
+                    D.a_lo = ws + G.al_off;
+                    D.b = ws + G.b_off;
+                    D.b_lo = ws + G.bl_off;
+                    D.scale = reinterpret_cast<const float*>(ws + p.scale_base) + G.scale_begin;
+                    D.count = G.count;
+                    D.M = G.M;
+                    D.N = G.N;
+                    D.job_begin = jobs;
+                    D.apply_begin = napply;
+                    if (a.fuse_apply) {
+                        for (int ti : p.members[gi]) {
+                            const muon_tensor_t& x = tensors[ti];
+                            FusedApply& F = a.apply[napply++];
+                            F.param = x.param;
+                            F.out = x.update_out;
+                            F.rows = x.rows;
+                            F.cols = x.cols;
+                            F.transposed = x.rows > x.cols;
+                            F.vec = (x.cols % 4 == 0) && (reinterpret_cast<uintptr_t>(x.param) % 16 == 0) &&
+                                    (reinterpret_cast<uintptr_t>(x.update_out) % 16 == 0);
+                            F.lr_s = lr_scale(x);
+                        }
+                    }
+                    const int tm = G.M / kTile, tn = G.N / kTile;
+                    jobs += G.count * (phase == kUpdate ? tm * tn : tm * (tm + 1) / 2);
                 }
+                a.total_jobs = jobs;
+                const bool comp = ls.comp != 0;
+                const char* name = ns_kernel_name(phase, prec, comp, a.fuse_apply != 0);
+                err = timed_launch(name, ls_stream, [&] { return launch_ns(a, phase, prec, comp, ls_stream); });
+                if (err != hipSuccess) return fail(MUON_ERR_HIP, "%s launch failed: %s", name, hipGetErrorString(err));
             }
         }
+    }
+
+    if (L) {
+        for (int l = 1; l < nlanes && err == hipSuccess; ++l) {
+            err = hipEventRecord(L->join[l], lane_stream[l]);
+            if (err == hipSuccess) err = hipStreamWaitEvent(s, L->join[l], 0);
+        }
+        if (err != hipSuccess) return fail(MUON_ERR_HIP, "NS lane join failed: %s", hipGetErrorString(err));
     }
 
     // ---- apply: W' = (1 - lr wd) W - lr s O (unless the last NS update did it)

@@ -40,6 +40,9 @@
 #ifndef NS_PREFETCH_XL
 #define NS_PREFETCH_XL 1     // bf16 update / square: fetch the epilogue's inputs before staging
 #endif
+#ifndef NS_UPDATE_COLMAJOR
+#define NS_UPDATE_COLMAJOR 1  // update jobs ordered by X column panel
+#endif
 #ifndef NS_WIDE_UPDATE
 #define NS_WIDE_UPDATE 0     // 1: the bf16 base update stages 256 bytes of K too
 #endif
@@ -240,11 +243,18 @@ __device__ inline bool decode_job(const NsArgs& args, Job& j) {
     const int tm = G.M / kTile, tn = G.N / kTile;
     const int local = job - G.job_begin;
     if (PHASE == kUpdate) {
+        // column-panel-major: the tm row tiles that read the same X column panel
+        // are neighbours in job order (and so on one XCD at about the same time)
         const int per = tm * tn;
         j.slot = local / per;
         const int t = local - j.slot * per;
-        j.ti = t / tn;
-        j.tj = t - j.ti * tn;
+        if (NS_UPDATE_COLMAJOR) {
+            j.tj = t / tm;
+            j.ti = t - j.tj * tm;
+        } else {
+            j.ti = t / tn;
+            j.tj = t - j.ti * tn;
+        }
     } else {
         const int per = tm * (tm + 1) / 2;
         j.slot = local / per;
@@ -414,40 +424,41 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
-    NtLoader<kRB> la, lb, lal, lbl;
-    TLoader<PREC> lt, ltl;
-    XLoader<kBK> lx, lxl;
-    auto issue = [&](int k0) {
+    // Registers staging one K stage from global memory into LDS.
+    NtLoader<kRB> la[1], lb[1], lal[1], lbl[1];
+    TLoader<PREC> lt[1], ltl[1];
+    XLoader<kBK> lx[1], lxl[1];
+    auto issue = [&](int k0, int set) {
         const int kbyte = k0 * (int)sizeof(T);
-        la.load(ga, ld_bytes, kbyte);
-        if (kSplit) lal.load(gal, ld_bytes, kbyte);
+        la[set].load(ga, ld_bytes, kbyte);
+        if (kSplit) lal[set].load(gal, ld_bytes, kbyte);
         if (PHASE == kUpdate) {
             if constexpr (kTr) {
-                lx.load(reinterpret_cast<const bf16*>(xb), (size_t)N, k0, job.tj * kTile);
-                if (kSplit) lxl.load(reinterpret_cast<const bf16*>(xbl), (size_t)N, k0, job.tj * kTile);
+                lx[set].load(reinterpret_cast<const bf16*>(xb), (size_t)N, k0, job.tj * kTile);
+                if (kSplit) lxl[set].load(reinterpret_cast<const bf16*>(xbl), (size_t)N, k0, job.tj * kTile);
             } else {
-                lt.load(xb, (size_t)N, k0, job.tj * kTile);
-                if (kSplit) ltl.load(xbl, (size_t)N, k0, job.tj * kTile);
+                lt[set].load(xb, (size_t)N, k0, job.tj * kTile);
+                if (kSplit) ltl[set].load(xbl, (size_t)N, k0, job.tj * kTile);
             }
         } else if (!diag) {
-            lb.load(gb, ld_bytes, kbyte);
-            if (kSplit) lbl.load(gbl, ld_bytes, kbyte);
+            lb[set].load(gb, ld_bytes, kbyte);
+            if (kSplit) lbl[set].load(gbl, ld_bytes, kbyte);
         }
     };
-    auto commit = [&](int stage) {
-        la.store(tile(stage, 0));
-        if (kSplit) lal.store(tile(stage, 2));
+    auto commit = [&](int stage, int set) {
+        la[set].store(tile(stage, 0));
+        if (kSplit) lal[set].store(tile(stage, 2));
         if (PHASE == kUpdate) {
             if constexpr (kTr) {
-                lx.store(tile(stage, 1));
-                if (kSplit) lxl.store(tile(stage, 3));
+                lx[set].store(tile(stage, 1));
+                if (kSplit) lxl[set].store(tile(stage, 3));
             } else {
-                lt.store(tile(stage, 1));
-                if (kSplit) ltl.store(tile(stage, 3));
+                lt[set].store(tile(stage, 1));
+                if (kSplit) ltl[set].store(tile(stage, 3));
             }
         } else if (!diag) {
-            lb.store(tile(stage, 1));
-            if (kSplit) lbl.store(tile(stage, 3));
+            lb[set].store(tile(stage, 1));
+            if (kSplit) lbl[set].store(tile(stage, 3));
         }
     };
     auto bfrag = [&](const uint8_t* tb, int ni, int kc) -> u32x4 {
@@ -504,7 +515,7 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
         if constexpr (kKeep && kOwnStages == 2) {
             if (kt == nk - 2) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) { keep_h[0][q] = lx.r[q]; if (kSplit) keep_l[0][q] = lxl.r[q]; }
+                for (int q = 0; q < 4; ++q) { keep_h[0][q] = lx[0].r[q]; if (kSplit) keep_l[0][q] = lxl[0].r[q]; }
             }
         }
     };
@@ -512,24 +523,24 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
     if constexpr (kStages == 2) {
         // LDS double buffer: one barrier per stage; the global loads of stage
         // kt+2 are in flight while stage kt+1 waits in LDS and kt computes.
-        issue(0);
-        commit(0);
-        if (nk > 1) issue(kBK);
+        issue(kstart(0), 0);
+        commit(0, 0);
+        if (nk > 1) issue(kstart(1), 0);
         __syncthreads();
         for (int kt = 0; kt < nk; ++kt) {
             compute(kt & 1);
-            if (kt + 1 < nk) commit((kt + 1) & 1);
-            if (kt + 2 < nk) issue((kt + 2) * kBK);
+            if (kt + 1 < nk) commit((kt + 1) & 1, 0);
+            if (kt + 2 < nk) issue(kstart(kt + 2), 0);
             __syncthreads();
         }
-    } else {
-        issue(kstart(0));
+    } else if (nk > 0) {
+        issue(kstart(0), 0);
         for (int kt = 0; kt < nk; ++kt) {
             __syncthreads();
-            commit(0);
+            commit(0, 0);
             capture(kt);
             __syncthreads();
-            if (kt + 1 < nk) issue(kstart(kt + 1));
+            if (kt + 1 < nk) issue(kstart(kt + 1), 0);
             compute(0);
         }
         if constexpr (kKeep) {
@@ -537,11 +548,11 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
             constexpr int base = (kOwnStages == 2) ? 0 : 4;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                keep_h[1][q] = lx.r[base + q];
-                if (kSplit) keep_l[1][q] = lxl.r[base + q];
+                keep_h[1][q] = lx[0].r[base + q];
+                if (kSplit) keep_l[1][q] = lxl[0].r[base + q];
                 if (kOwnStages == 1) {
-                    keep_h[0][q] = lx.r[q];
-                    if (kSplit) keep_l[0][q] = lxl.r[q];
+                    keep_h[0][q] = lx[0].r[q];
+                    if (kSplit) keep_l[0][q] = lxl[0].r[q];
                 }
             }
         }

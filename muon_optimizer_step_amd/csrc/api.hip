@@ -329,74 +329,13 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     float* rowsq = reinterpret_cast<float*>(ws + p.rowsq_base);
     const int prec = ns_precision == MUON_NS_FP32 ? kNsFp32 : kNsBf16;  // storage precision
-    hipError_t err;
+    const size_t xe = prec == kNsBf16 ? 2 : 4;                           // bytes per X element
+    hipError_t err = hipSuccess;
 
-    // ---- prep: momentum, row norm, X0 (short side first, zero padded), in
-    // evenly sized launches of at most kPrepChunk tensors
-    const int prep_launches = (n + kPrepChunk - 1) / kPrepChunk;
-    const int prep_take = (n + prep_launches - 1) / prep_launches;
-    for (int c0 = 0; c0 < n;) {
-        PrepArgs a;
-        memset(&a, 0, sizeof(a));
-        a.mu = momentum;
-        a.nesterov = nesterov;
-        a.row_norm = row_norm;
-        int blocks = 0;
-        size_t lds = 0;
-        for (int k = 0; k < prep_take && c0 < n; ++k, ++c0) {
-            const int i = c0;
-            const muon_tensor_t& x = tensors[i];
-            const Group& G = p.groups[p.group_of[i]];
-            PrepTensor& T = a.t[a.n++];
-            T.grad = x.grad;
-            T.mom = x.momentum;
-            const size_t xe = prec == kNsBf16 ? 2 : 4;
-            const size_t slot_off = (size_t)p.slot_of[i] * G.M * G.N * xe;
-            T.xh = ws + G.x_off[0] + slot_off;
-            T.xl = ws + G.xl_off[0] + slot_off;
-            T.rowsq = rowsq + p.rowsq_off[i];
-            T.rows = x.rows;
-            T.cols = x.cols;
-            T.transposed = x.rows > x.cols;
-            T.m_pad = G.M;
-            T.n_pad = G.N;
-            T.vec = (x.cols % 4 == 0) && (reinterpret_cast<uintptr_t>(x.grad) % 16 == 0) &&
-                    (reinterpret_cast<uintptr_t>(x.momentum) % 16 == 0);
-            T.block_begin = blocks;
-            if (T.transposed) {
-                T.rb = transposed_rb(x.cols);
-                blocks += G.N / T.rb;
-                lds = std::max(lds, (size_t)T.rb * (x.cols + 1) * sizeof(float));
-            } else {
-                T.rb = kRowsPerWaveBlock;
-                blocks += G.M / kRowsPerWaveBlock;
-            }
-        }
-        err = timed_launch("prep", s, [&] { return launch_prep(a, prec, blocks, lds, s); });
-        if (err != hipSuccess) return fail(MUON_ERR_HIP, "prep launch failed: %s", hipGetErrorString(err));
-    }
-
-    // ---- Frobenius scales
-    for (int c0 = 0; c0 < n; c0 += kFrobChunk) {
-        FrobArgs a;
-        memset(&a, 0, sizeof(a));
-        a.rowsq = rowsq;
-        a.scale = reinterpret_cast<float*>(ws + p.scale_base);
-        for (int i = c0; i < std::min(n, c0 + kFrobChunk); ++i) {
-            const Group& G = p.groups[p.group_of[i]];
-            a.rowsq_off[a.n] = (int)p.rowsq_off[i];
-            a.rows[a.n] = tensors[i].rows;
-            a.scale_idx[a.n] = G.scale_begin + p.slot_of[i];
-            ++a.n;
-        }
-        err = timed_launch("frob", s, [&] { return launch_frob(a, s); });
-        if (err != hipSuccess) return fail(MUON_ERR_HIP, "frob launch failed: %s", hipGetErrorString(err));
-    }
-
-    // ---- Newton-Schulz iterations.  Groups go to lanes (longest first onto the
-    // least loaded lane by NS flops); within a lane, one launch per phase for
-    // its base groups and one for its compensated groups (each skipped when
-    // empty), kMaxGroups groups per launch.
+    // ---- lanes: shape groups are independent NS problems.  Groups go to lanes
+    // longest first onto the least loaded lane (by NS flops); each lane runs
+    // prep -> frob -> NS iterations -> apply for its own matrices on its own
+    // stream, so short chains fill the compute units the long ones leave idle.
     const int ngroups = (int)p.groups.size();
     const int nlanes = std::min(kLanes, ngroups);
     std::vector<int> lane_of(ngroups, 0);
@@ -414,7 +353,7 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
             load[l] += wg.first;
         }
     }
-    // launches: (lane, comp, chunk of groups)
+    // NS launch sets: (lane, compensated?, up to kMaxGroups groups)
     struct NsLaunchSet {
         int lane, comp;
         std::vector<int> groups;
@@ -442,9 +381,10 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
     };
 
     std::unique_lock<std::mutex> lane_lock(g_lane_mu, std::defer_lock);
-    hipStream_t lane_stream[kLanes] = {s};
+    hipStream_t lane_stream[kLanes];
+    for (int l = 0; l < kLanes; ++l) lane_stream[l] = s;
     LaneSet* L = nullptr;
-    if (ns_steps > 0 && nlanes > 1) {
+    if (nlanes > 1) {
         lane_lock.lock();
         int dev = 0;
         err = hipGetDevice(&dev);
@@ -454,63 +394,175 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
             lane_stream[l] = L->stream[l];
             err = hipStreamWaitEvent(lane_stream[l], L->fork, 0);
         }
-        if (err != hipSuccess) return fail(MUON_ERR_HIP, "NS lane fork failed: %s", hipGetErrorString(err));
+        if (err != hipSuccess) return fail(MUON_ERR_HIP, "lane fork failed: %s", hipGetErrorString(err));
     }
 
-    for (int k = 0; k < ns_steps; ++k) {
-        for (int phase = kGram; phase <= kUpdate; ++phase) {
-            for (const NsLaunchSet& ls : sets) {
-                hipStream_t ls_stream = lane_stream[ls.lane];
-                NsArgs a;
-                memset(&a, 0, sizeof(a));
-                a.src = k & 1;
-                a.first = (k == 0);
-                a.a = ns_coeffs[3 * k + 0];
-                a.b = ns_coeffs[3 * k + 1];
-                a.c = ns_coeffs[3 * k + 2];
-                a.fuse_apply = fuse && phase == kUpdate && k == ns_steps - 1;
-                a.keep = keep;
-                int jobs = 0, napply = 0;
-                for (int gi : ls.groups) {
-                    const Group& G = p.groups[gi];
-                    NsGroup& D = a.g[a.ngroups++];
-                    for (int b = 0; b < 2; ++b) {
-                        D.x[b] = ws + G.x_off[b];
-                        D.xl[b] = ws + G.xl_off[b];
-                    }
-                    D.a_hi = ws + G.ah_off;
-                    D.a_lo = ws + G.al_off;
-                    D.b = ws + G.b_off;
-                    D.b_lo = ws + G.bl_off;
-                    D.scale = reinterpret_cast<const float*>(ws + p.scale_base) + G.scale_begin;
-                    D.count = G.count;
-                    D.M = G.M;
-                    D.N = G.N;
-                    D.job_begin = jobs;
-                    D.apply_begin = napply;
-                    if (a.fuse_apply) {
-                        for (int ti : p.members[gi]) {
-                            const muon_tensor_t& x = tensors[ti];
-                            FusedApply& F = a.apply[napply++];
-                            F.param = x.param;
-                            F.out = x.update_out;
-                            F.rows = x.rows;
-                            F.cols = x.cols;
-                            F.transposed = x.rows > x.cols;
-                            F.vec = (x.cols % 4 == 0) && (reinterpret_cast<uintptr_t>(x.param) % 16 == 0) &&
-                                    (reinterpret_cast<uintptr_t>(x.update_out) % 16 == 0);
-                            F.lr_s = lr_scale(x);
-                        }
-                    }
-                    const int tm = G.M / kTile, tn = G.N / kTile;
-                    jobs += G.count * (phase == kUpdate ? tm * tn : tm * (tm + 1) / 2);
+    for (int lane = 0; lane < nlanes; ++lane) {
+        hipStream_t ls_stream = lane_stream[lane];
+        std::vector<int> mine;  // this lane's tensors, in call order
+        for (int i = 0; i < n; ++i)
+            if (lane_of[p.group_of[i]] == lane) mine.push_back(i);
+        const int nm = (int)mine.size();
+
+        // ---- prep: momentum, row norm, X0 (short side first, zero padded), in
+        // evenly sized launches of at most kPrepChunk tensors
+        const int prep_launches = (nm + kPrepChunk - 1) / kPrepChunk;
+        const int prep_take = (nm + prep_launches - 1) / prep_launches;
+        for (int c0 = 0; c0 < nm;) {
+            PrepArgs a;
+            memset(&a, 0, sizeof(a));
+            a.mu = momentum;
+            a.nesterov = nesterov;
+            a.row_norm = row_norm;
+            int blocks = 0;
+            size_t lds = 0;
+            for (int k = 0; k < prep_take && c0 < nm; ++k, ++c0) {
+                const int i = mine[c0];
+                const muon_tensor_t& x = tensors[i];
+                const Group& G = p.groups[p.group_of[i]];
+                PrepTensor& T = a.t[a.n++];
+                T.grad = x.grad;
+                T.mom = x.momentum;
+                const size_t slot_off = (size_t)p.slot_of[i] * G.M * G.N * xe;
+                T.xh = ws + G.x_off[0] + slot_off;
+                T.xl = ws + G.xl_off[0] + slot_off;
+                T.rowsq = rowsq + p.rowsq_off[i];
+                T.rows = x.rows;
+                T.cols = x.cols;
+                T.transposed = x.rows > x.cols;
+                T.m_pad = G.M;
+                T.n_pad = G.N;
+                T.vec = (x.cols % 4 == 0) && (reinterpret_cast<uintptr_t>(x.grad) % 16 == 0) &&
+                        (reinterpret_cast<uintptr_t>(x.momentum) % 16 == 0);
+                T.block_begin = blocks;
+                if (T.transposed) {
+                    T.rb = transposed_rb(x.cols);
+                    blocks += G.N / T.rb;
+                    lds = std::max(lds, (size_t)T.rb * (x.cols + 1) * sizeof(float));
+                } else {
+                    T.rb = kRowsPerWaveBlock;
+                    blocks += G.M / kRowsPerWaveBlock;
                 }
-                a.total_jobs = jobs;
-                const bool comp = ls.comp != 0;
-                const char* name = ns_kernel_name(phase, prec, comp, a.fuse_apply != 0);
-                err = timed_launch(name, ls_stream, [&] { return launch_ns(a, phase, prec, comp, ls_stream); });
-                if (err != hipSuccess) return fail(MUON_ERR_HIP, "%s launch failed: %s", name, hipGetErrorString(err));
             }
+            err = timed_launch("prep", ls_stream, [&] { return launch_prep(a, prec, blocks, lds, ls_stream); });
+            if (err != hipSuccess) return fail(MUON_ERR_HIP, "prep launch failed: %s", hipGetErrorString(err));
+        }
+
+        // ---- Frobenius scales
+        for (int c0 = 0; c0 < nm; c0 += kFrobChunk) {
+            FrobArgs a;
+            memset(&a, 0, sizeof(a));
+            a.rowsq = rowsq;
+            a.scale = reinterpret_cast<float*>(ws + p.scale_base);
+            for (int c = c0; c < std::min(nm, c0 + kFrobChunk); ++c) {
+                const int i = mine[c];
+                const Group& G = p.groups[p.group_of[i]];
+                a.rowsq_off[a.n] = (int)p.rowsq_off[i];
+                a.rows[a.n] = tensors[i].rows;
+                a.scale_idx[a.n] = G.scale_begin + p.slot_of[i];
+                ++a.n;
+            }
+            err = timed_launch("frob", ls_stream, [&] { return launch_frob(a, ls_stream); });
+            if (err != hipSuccess) return fail(MUON_ERR_HIP, "frob launch failed: %s", hipGetErrorString(err));
+        }
+
+        // ---- Newton-Schulz iterations: one launch per phase per launch set
+        for (int k = 0; k < ns_steps; ++k) {
+            for (int phase = kGram; phase <= kUpdate; ++phase) {
+                for (const NsLaunchSet& ls : sets) {
+                    if (ls.lane != lane) continue;
+                    NsArgs a;
+                    memset(&a, 0, sizeof(a));
+                    a.src = k & 1;
+                    a.first = (k == 0);
+                    a.a = ns_coeffs[3 * k + 0];
+                    a.b = ns_coeffs[3 * k + 1];
+                    a.c = ns_coeffs[3 * k + 2];
+                    a.fuse_apply = fuse && phase == kUpdate && k == ns_steps - 1;
+                    a.keep = keep;
+                    int jobs = 0, napply = 0;
+                    for (int gi : ls.groups) {
+                        const Group& G = p.groups[gi];
+                        NsGroup& D = a.g[a.ngroups++];
+                        for (int b = 0; b < 2; ++b) {
+                            D.x[b] = ws + G.x_off[b];
+                            D.xl[b] = ws + G.xl_off[b];
+                        }
+                        D.a_hi = ws + G.ah_off;
+                        D.a_lo = ws + G.al_off;
+                        D.b = ws + G.b_off;
+                        D.b_lo = ws + G.bl_off;
+                        D.scale = reinterpret_cast<const float*>(ws + p.scale_base) + G.scale_begin;
+                        D.count = G.count;
+                        D.M = G.M;
+                        D.N = G.N;
+                        D.job_begin = jobs;
+                        D.apply_begin = napply;
+                        if (a.fuse_apply) {
+                            for (int ti : p.members[gi]) {
+                                const muon_tensor_t& x = tensors[ti];
+                                FusedApply& F = a.apply[napply++];
+                                F.param = x.param;
+                                F.out = x.update_out;
+                                F.rows = x.rows;
+                                F.cols = x.cols;
+                                F.transposed = x.rows > x.cols;
+                                F.vec = (x.cols % 4 == 0) && (reinterpret_cast<uintptr_t>(x.param) % 16 == 0) &&
+                                        (reinterpret_cast<uintptr_t>(x.update_out) % 16 == 0);
+                                F.lr_s = lr_scale(x);
+                            }
+                        }
+                        const int tm = G.M / kTile, tn = G.N / kTile;
+                        jobs += G.count * (phase == kUpdate ? tm * tn : tm * (tm + 1) / 2);
+                    }
+                    a.total_jobs = jobs;
+                    const bool comp = ls.comp != 0;
+                    const char* name = ns_kernel_name(phase, prec, comp, a.fuse_apply != 0);
+                    err = timed_launch(name, ls_stream, [&] { return launch_ns(a, phase, prec, comp, ls_stream); });
+                    if (err != hipSuccess) return fail(MUON_ERR_HIP, "%s launch failed: %s", name, hipGetErrorString(err));
+                }
+            }
+        }
+
+        // ---- apply: W' = (1 - lr wd) W - lr s O (unless the last NS update did it)
+        const int final_buf = ns_steps & 1;
+        for (int c0 = 0; c0 < nm && !fuse; c0 += kPrepChunk) {
+            ApplyArgs a;
+            memset(&a, 0, sizeof(a));
+            a.keep = keep;
+            a.use_scale = ns_steps == 0;
+            int blocks = 0;
+            size_t lds = 0;
+            for (int c = c0; c < std::min(nm, c0 + kPrepChunk); ++c) {
+                const int i = mine[c];
+                const muon_tensor_t& x = tensors[i];
+                const Group& G = p.groups[p.group_of[i]];
+                ApplyTensor& T = a.t[a.n++];
+                T.param = x.param;
+                T.out = x.update_out;
+                const size_t slot_off = (size_t)p.slot_of[i] * G.M * G.N * xe;
+                T.xh = ws + G.x_off[final_buf] + slot_off;
+                T.xl = ws + G.xl_off[final_buf] + slot_off;
+                T.scale = reinterpret_cast<const float*>(ws + p.scale_base) + G.scale_begin + p.slot_of[i];
+                T.lr_s = lr_scale(x);
+                T.rows = x.rows;
+                T.cols = x.cols;
+                T.n_pad = G.N;
+                T.transposed = x.rows > x.cols;
+                T.vec = (x.cols % 4 == 0) && (reinterpret_cast<uintptr_t>(x.param) % 16 == 0) &&
+                        (reinterpret_cast<uintptr_t>(x.update_out) % 16 == 0);
+                T.block_begin = blocks;
+                if (T.transposed) {
+                    T.rb = transposed_rb(x.cols);
+                    blocks += (x.rows + T.rb - 1) / T.rb;
+                    lds = std::max(lds, (size_t)T.rb * (x.cols + 1) * sizeof(float));
+                } else {
+                    T.rb = kRowsPerWaveBlock;
+                    blocks += (x.rows + kRowsPerWaveBlock - 1) / kRowsPerWaveBlock;
+                }
+            }
+            err = timed_launch("apply", ls_stream, [&] { return launch_apply(a, prec, blocks, lds, ls_stream); });
+            if (err != hipSuccess) return fail(MUON_ERR_HIP, "apply launch failed: %s", hipGetErrorString(err));
         }
     }
 
@@ -519,48 +571,7 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
             err = hipEventRecord(L->join[l], lane_stream[l]);
             if (err == hipSuccess) err = hipStreamWaitEvent(s, L->join[l], 0);
         }
-        if (err != hipSuccess) return fail(MUON_ERR_HIP, "NS lane join failed: %s", hipGetErrorString(err));
-    }
-
-    // ---- apply: W' = (1 - lr wd) W - lr s O (unless the last NS update did it)
-    const int final_buf = ns_steps & 1;
-    for (int c0 = 0; c0 < n && !fuse; c0 += kPrepChunk) {
-        ApplyArgs a;
-        memset(&a, 0, sizeof(a));
-        a.keep = keep;
-        a.use_scale = ns_steps == 0;
-        int blocks = 0;
-        size_t lds = 0;
-        for (int i = c0; i < std::min(n, c0 + kPrepChunk); ++i) {
-            const muon_tensor_t& x = tensors[i];
-            const Group& G = p.groups[p.group_of[i]];
-            ApplyTensor& T = a.t[a.n++];
-            T.param = x.param;
-            T.out = x.update_out;
-            const size_t xe = prec == kNsBf16 ? 2 : 4;
-            const size_t slot_off = (size_t)p.slot_of[i] * G.M * G.N * xe;
-            T.xh = ws + G.x_off[final_buf] + slot_off;
-            T.xl = ws + G.xl_off[final_buf] + slot_off;
-            T.scale = reinterpret_cast<const float*>(ws + p.scale_base) + G.scale_begin + p.slot_of[i];
-            T.lr_s = lr_scale(x);
-            T.rows = x.rows;
-            T.cols = x.cols;
-            T.n_pad = G.N;
-            T.transposed = x.rows > x.cols;
-            T.vec = (x.cols % 4 == 0) && (reinterpret_cast<uintptr_t>(x.param) % 16 == 0) &&
-                    (reinterpret_cast<uintptr_t>(x.update_out) % 16 == 0);
-            T.block_begin = blocks;
-            if (T.transposed) {
-                T.rb = transposed_rb(x.cols);
-                blocks += (x.rows + T.rb - 1) / T.rb;
-                lds = std::max(lds, (size_t)T.rb * (x.cols + 1) * sizeof(float));
-            } else {
-                T.rb = kRowsPerWaveBlock;
-                blocks += (x.rows + kRowsPerWaveBlock - 1) / kRowsPerWaveBlock;
-            }
-        }
-        err = timed_launch("apply", s, [&] { return launch_apply(a, prec, blocks, lds, s); });
-        if (err != hipSuccess) return fail(MUON_ERR_HIP, "apply launch failed: %s", hipGetErrorString(err));
+        if (err != hipSuccess) return fail(MUON_ERR_HIP, "lane join failed: %s", hipGetErrorString(err));
     }
     return MUON_OK;
 }

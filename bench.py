@@ -2,8 +2,9 @@
 
 One step = muon_step over the 66 Muon matrices of the 11-layer 512d model
 (momentum, MuonEq-R row norm, Frobenius scale, 5 quintic Newton-Schulz
-iterations in bf16 MFMA, shape-scaled LR, decoupled weight decay) followed by
-ema_update over all 34,401,372 parameters.  Inputs are synthetic and seeded
+iterations in bf16 MFMA, shape-scaled LR, decoupled weight decay, and the
+matrices' weight EMA in the pass that writes W') followed by ema_update over
+the remaining parameters: the EMA covers all 34,401,372 parameters.  Inputs are synthetic and seeded
 (workloads.workload(2)) and resident in HBM before timing starts.
 
 Prints one JSON line (steps/s) with a roofline entry for the dominant kernel
@@ -124,7 +125,9 @@ def kernel_model(w):
     prep, apply and ema: per step (they may be split into several launches by
     tensor-table chunking).  Bytes count each operand once at its stored width:
     X is a bf16 hi + lo pair (4 B), A and B are bf16 (hi + lo for A), weights,
-    gradients, momenta and EMA shadows are fp32.
+    gradients, momenta and EMA shadows are fp32.  The matrices' EMA rides on
+    the weight apply (fused into the last NS update, or the apply kernel);
+    the ema kernel covers the other parameters.
     """
     gram_f = sq_f = 0.0
     gram_b = sq_b = upd_b = upda_b = 0.0
@@ -136,16 +139,16 @@ def kernel_model(w):
         gram_b += 2.0 * m * n + 4.0 * m * m      # read X hi; write A hi + lo
         sq_b += 4.0 * m * m + 2.0 * m * m        # read A hi + lo; write B
         upd_b += 8.0 * m * n + 2.0 * m * m       # read X hi + lo and B; write X hi + lo
-        upda_b += 12.0 * m * n + 2.0 * m * m     # read X hi + lo and B; read + write W
+        upda_b += 20.0 * m * n + 2.0 * m * m     # read X hi + lo and B; read + write W and E
         elems += r * c
     return {
         "ns_gram_bf16": {"per": "launch", "flops": gram_f, "bytes": gram_b},      # A = X X^T
         "ns_square_bf16": {"per": "launch", "flops": sq_f, "bytes": sq_b},        # B = b A + c A A
         "ns_update_bf16": {"per": "launch", "flops": gram_f, "bytes": upd_b},     # X <- a X + B X
-        "ns_update_apply_bf16": {"per": "launch", "flops": gram_f, "bytes": upda_b},  # last X, then W'
+        "ns_update_apply_bf16": {"per": "launch", "flops": gram_f, "bytes": upda_b},  # last X, then W', E'
         "prep": {"per": "step", "flops": 0.0, "bytes": 16.0 * elems},   # read G, M; write M, X0 hi + lo
-        "apply": {"per": "step", "flops": 0.0, "bytes": 12.0 * elems},  # read W, X hi + lo; write W
-        "ema": {"per": "step", "flops": 0.0, "bytes": 12.0 * w.n_params},  # read E, P; write E
+        "apply": {"per": "step", "flops": 0.0, "bytes": 20.0 * elems},  # read W, E, X hi + lo; write W, E
+        "ema": {"per": "step", "flops": 0.0, "bytes": 12.0 * (w.n_params - elems)},  # read E, P; write E
     }
 
 
@@ -235,12 +238,13 @@ def main():
     M = [torch.from_numpy(m).to(dev) for m in st["moms"]]
     E = [torch.from_numpy(e).to(dev) for e in st["ema"]]
     del st, grads
-    step_muon = ms.PreparedMuonStep(P[:nm], G, M)
-    step_ema = ms.PreparedEma(E, P)
+    step_muon = ms.PreparedMuonStep(P[:nm], G, M, emas=E[:nm])
+    step_ema = ms.PreparedEma(E[nm:], P[nm:])
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        step_muon(lr=w.lr, momentum=w.momentum, weight_decay=w.weight_decay, coeffs=coeffs, stream=stream)
+        step_muon(lr=w.lr, momentum=w.momentum, weight_decay=w.weight_decay, coeffs=coeffs,
+                  ema_decay=w.ema_decay, stream=stream)
         step_ema(w.ema_decay, stream=stream)
 
     print(f"[bench] workload {w.name}: {nm} matrices, {w.n_params:,} params, warmup {args.warmup}", flush=True)
@@ -310,7 +314,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: muon_step over 66 matrices (11 layers x Q/K/V/O/up/down at d=512), "
-                               f"5 NS steps bf16, then ema_update over {w.n_params:,} fp32 params",
+                               f"5 NS steps bf16, EMA over all {w.n_params:,} fp32 params "
+                               f"(matrices inside the step, {len(w.extras)} other tensors in ema_update)",
                    "matrices": nm, "params": w.n_params, "ns_steps": w.ns_steps, "seed": args.seed},
         "roofline": {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,

@@ -64,13 +64,19 @@ extern "C" {
 
 /* One Muon matrix.  param and momentum are updated in place; grad is read only.
  * update_out is optional (NULL to skip): when set, the orthogonalised update O
- * (rows x cols, fp32, before the lr and shape scaling) is written there.  The
- * four buffers must not overlap. */
+ * (rows x cols, fp32, before the lr and shape scaling) is written there.
+ * ema is optional (NULL to skip): when set, the weight EMA of this matrix is
+ * advanced in the same pass that writes W':  ema = d*ema + (1-d)*W'  with
+ * d = ema_decay of the call (the batched EMA of "Record: Improved Parallel
+ * Residuals + Systems Optimization" (PR #1584), "Summary", folded into the
+ * step; identical to ema_update on the post-step weights).  None of the
+ * buffers of any tensor of a call may overlap. */
 typedef struct muon_tensor_t {
     float* param;
     const float* grad;
     float* momentum;
     float* update_out;
+    float* ema;
     int32_t rows;
     int32_t cols;
 } muon_tensor_t;
@@ -96,13 +102,15 @@ size_t muon_workspace_size(const muon_tensor_t* tensors, int32_t n, int32_t ns_p
  *                 least 192, and the compensated products (hi*hi + hi*lo +
  *                 lo*hi everywhere) below that; MUON_NS_BF16X3 compensates every
  *                 matrix.
+ *   ema_decay     EMA decay d for the tensors whose ema is set; finite, in [0, 1]
+ *                 (checked on every call).
  *   workspace     device buffer of at least muon_workspace_size(...) bytes,
  *                 256-byte aligned; its contents on entry do not matter.
  *   stream        hipStream_t to enqueue on.
  * NaN or Inf inside the tensors is not checked and propagates. */
 int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
               int32_t nesterov, float weight_decay, int32_t row_norm, int32_t ns_steps,
-              const float* ns_coeffs, int32_t ns_precision, void* workspace,
+              const float* ns_coeffs, int32_t ns_precision, float ema_decay, void* workspace,
               size_t workspace_bytes, void* stream);
 
 /* Weight EMA over n fp32 tensors: ema[i][j] = decay*ema[i][j] + (1-decay)*params[i][j]

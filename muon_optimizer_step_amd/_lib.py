@@ -27,6 +27,7 @@ class MuonTensor(ctypes.Structure):
         ("grad", ctypes.c_void_p),
         ("momentum", ctypes.c_void_p),
         ("update_out", ctypes.c_void_p),
+        ("ema", ctypes.c_void_p),
         ("rows", ctypes.c_int32),
         ("cols", ctypes.c_int32),
     ]
@@ -57,7 +58,7 @@ def load() -> ctypes.CDLL:
     f = lib.muon_step
     f.argtypes = [ctypes.POINTER(MuonTensor), ctypes.c_int32, ctypes.c_float, ctypes.c_float, ctypes.c_int32,
                   ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_float), ctypes.c_int32,
-                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+                  ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     f.restype = ctypes.c_int
     f = lib.ema_update
     f.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_int64),
@@ -82,11 +83,11 @@ def check(rc: int) -> None:
 
 
 def tensor_table(entries) -> "ctypes.Array[MuonTensor]":
-    """entries: iterable of (param, grad, momentum, update_out, rows, cols) with int pointers."""
+    """entries: iterable of (param, grad, momentum, update_out, ema, rows, cols) with int pointers."""
     entries = list(entries)
     arr = (MuonTensor * max(1, len(entries)))()
-    for i, (p, g, m, o, r, c) in enumerate(entries):
-        arr[i] = MuonTensor(p, g, m, o, r, c)
+    for i, (p, g, m, o, e, r, c) in enumerate(entries):
+        arr[i] = MuonTensor(p, g, m, o, e, r, c)
     return arr
 
 

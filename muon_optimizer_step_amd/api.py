@@ -38,11 +38,35 @@ def _stream_handle(stream, device):
 
 def workspace_size(shapes: Sequence[Tuple[int, int]], ns_precision: int = _lib.MUON_NS_BF16) -> int:
     """Bytes of workspace muon_step needs for these (rows, cols) shapes."""
-    table = _lib.tensor_table((0, 0, 0, 0, int(r), int(c)) for r, c in shapes)
+    table = _lib.tensor_table((0, 0, 0, 0, 0, int(r), int(c)) for r, c in shapes)
     n = _lib.load().muon_workspace_size(table, len(shapes), int(ns_precision))
     if n == 0:
         raise _lib.MuonError(_lib.MUON_ERR_INVALID_ARG, _lib.load().muon_last_error().decode())
     return int(n)
+
+
+def _entries(params, grads, moms, update_outs, emas):
+    """Checked descriptor tuples (param, grad, momentum, update_out, ema, rows, cols)."""
+    n = len(params)
+    outs = update_outs if update_outs is not None else [None] * n
+    emas = emas if emas is not None else [None] * n
+    if len(outs) != n or len(emas) != n:
+        raise ValueError("update_outs and emas must have one entry per parameter")
+    entries = []
+    for i, (p, g, m, o, e) in enumerate(zip(params, grads, moms, outs, emas)):
+        _check_tensor(p, f"params[{i}]", 2)
+        _check_tensor(g, f"grads[{i}]", 2)
+        _check_tensor(m, f"moms[{i}]", 2)
+        if g.shape != p.shape or m.shape != p.shape:
+            raise ValueError(f"tensor {i}: shapes differ {tuple(p.shape)} {tuple(g.shape)} {tuple(m.shape)}")
+        for t, nm in ((o, "update_outs"), (e, "emas")):
+            if t is not None:
+                _check_tensor(t, f"{nm}[{i}]", 2)
+                if t.shape != p.shape:
+                    raise ValueError(f"{nm}[{i}] shape {tuple(t.shape)} != {tuple(p.shape)}")
+        entries.append((p.data_ptr(), g.data_ptr(), m.data_ptr(), o.data_ptr() if o is not None else 0,
+                        e.data_ptr() if e is not None else 0, p.shape[0], p.shape[1]))
+    return entries
 
 
 def _workspace_for(nbytes: int, device):
@@ -58,30 +82,20 @@ def _workspace_for(nbytes: int, device):
 
 def muon_step(params, grads, moms, *, lr: float, momentum: float, weight_decay: float,
               coeffs, nesterov: bool = True, row_norm: bool = True,
-              ns_precision: int = _lib.MUON_NS_BF16, update_outs=None, workspace=None, stream=None) -> None:
+              ns_precision: int = _lib.MUON_NS_BF16, update_outs=None, emas=None, ema_decay: float = 0.0,
+              workspace=None, stream=None) -> None:
     """One Muon step over lists of 2-D fp32 tensors (params and moms updated in place).
 
     coeffs: ns_steps rows of (a, b, c); update_outs: optional list of tensors
-    (or None entries) that receive the orthogonalised update O.
+    (or None entries) that receive the orthogonalised update O; emas: optional
+    list of tensors (or None entries) advanced as ema = d*ema + (1-d)*W' with
+    d = ema_decay, in the pass that writes W'.
     """
     lib = _lib.load()
     n = len(params)
     if len(grads) != n or len(moms) != n:
         raise ValueError("params, grads and moms must have the same length")
-    outs = update_outs if update_outs is not None else [None] * n
-    entries = []
-    for i, (p, g, m, o) in enumerate(zip(params, grads, moms, outs)):
-        _check_tensor(p, f"params[{i}]", 2)
-        _check_tensor(g, f"grads[{i}]", 2)
-        _check_tensor(m, f"moms[{i}]", 2)
-        if g.shape != p.shape or m.shape != p.shape:
-            raise ValueError(f"tensor {i}: shapes differ {tuple(p.shape)} {tuple(g.shape)} {tuple(m.shape)}")
-        if o is not None:
-            _check_tensor(o, f"update_outs[{i}]", 2)
-            if o.shape != p.shape:
-                raise ValueError(f"update_outs[{i}] shape {tuple(o.shape)} != {tuple(p.shape)}")
-        entries.append((p.data_ptr(), g.data_ptr(), m.data_ptr(), o.data_ptr() if o is not None else 0,
-                        p.shape[0], p.shape[1]))
+    entries = _entries(params, grads, moms, update_outs, emas)
     table = _lib.tensor_table(entries)
     carr, steps = _lib.coeff_array(coeffs)
     device = params[0].device if n else None
@@ -91,7 +105,7 @@ def muon_step(params, grads, moms, *, lr: float, momentum: float, weight_decay: 
             raise _lib.MuonError(_lib.MUON_ERR_INVALID_ARG, lib.muon_last_error().decode())
         workspace = _workspace_for(int(need), device)
     rc = lib.muon_step(table, n, float(lr), float(momentum), int(bool(nesterov)), float(weight_decay),
-                       int(bool(row_norm)), steps, carr if steps else None, int(ns_precision),
+                       int(bool(row_norm)), steps, carr if steps else None, int(ns_precision), float(ema_decay),
                        ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
                        _stream_handle(stream, device))
     _lib.check(rc)
@@ -152,19 +166,11 @@ class PreparedMuonStep:
     """
 
     def __init__(self, params, grads, moms, *, ns_precision: int = _lib.MUON_NS_BF16, update_outs=None,
-                 workspace=None):
-        self._keep = (list(params), list(grads), list(moms), update_outs, workspace)
-        outs = update_outs if update_outs is not None else [None] * len(params)
-        entries = []
-        for i, (p, g, m, o) in enumerate(zip(params, grads, moms, outs)):
-            for t, nm in ((p, "params"), (g, "grads"), (m, "moms")):
-                _check_tensor(t, f"{nm}[{i}]", 2)
-                if t.shape != p.shape:
-                    raise ValueError(f"tensor {i}: shape mismatch")
-            if o is not None:
-                _check_tensor(o, f"update_outs[{i}]", 2)
-            entries.append((p.data_ptr(), g.data_ptr(), m.data_ptr(), o.data_ptr() if o is not None else 0,
-                            p.shape[0], p.shape[1]))
+                 emas=None, workspace=None):
+        if len(grads) != len(params) or len(moms) != len(params):
+            raise ValueError("params, grads and moms must have the same length")
+        self._keep = (list(params), list(grads), list(moms), update_outs, emas, workspace)
+        entries = _entries(params, grads, moms, update_outs, emas)
         self.n = len(entries)
         self.table = _lib.tensor_table(entries)
         self.ns_precision = int(ns_precision)
@@ -180,14 +186,15 @@ class PreparedMuonStep:
         self._ws_bytes = workspace.numel() * workspace.element_size()
         self._coeffs = None
 
-    def __call__(self, *, lr, momentum, weight_decay, coeffs, nesterov=True, row_norm=True, stream=None):
+    def __call__(self, *, lr, momentum, weight_decay, coeffs, nesterov=True, row_norm=True, ema_decay=0.0,
+                 stream=None):
         if self._coeffs is None or self._coeffs[0] != coeffs:
             key = [tuple(float(v) for v in row) for row in coeffs]
             self._coeffs = (coeffs, _lib.coeff_array(key))
         carr, steps = self._coeffs[1]
         rc = _lib.load().muon_step(self.table, self.n, float(lr), float(momentum), int(bool(nesterov)),
                                    float(weight_decay), int(bool(row_norm)), steps, carr if steps else None,
-                                   self.ns_precision, self._ws_ptr, self._ws_bytes,
+                                   self.ns_precision, float(ema_decay), self._ws_ptr, self._ws_bytes,
                                    _stream_handle(stream, self.device))
         _lib.check(rc)
 

@@ -250,14 +250,14 @@ int validate_tensors(const muon_tensor_t* t, int32_t n, int32_t precision) {
 
 int validate_pointers(const muon_tensor_t* t, int32_t n) {
     std::vector<Span> spans;
-    spans.reserve(4 * (size_t)n);
+    spans.reserve(5 * (size_t)n);
     for (int i = 0; i < n; ++i) {
         const muon_tensor_t& x = t[i];
         if (!x.param || !x.grad || !x.momentum)
             return fail(MUON_ERR_INVALID_ARG, "tensor %d: param, grad and momentum must be non-NULL", i);
         const size_t bytes = (size_t)x.rows * x.cols * sizeof(float);
-        const void* ptrs[4] = {x.param, x.grad, x.momentum, x.update_out};
-        for (int k = 0; k < 4; ++k) {
+        const void* ptrs[5] = {x.param, x.grad, x.momentum, x.update_out, x.ema};
+        for (int k = 0; k < 5; ++k) {
             if (!ptrs[k]) continue;
             if (reinterpret_cast<uintptr_t>(ptrs[k]) % sizeof(float))
                 return fail(MUON_ERR_INVALID_ARG, "tensor %d: pointer %d is not 4-byte aligned", i, k);
@@ -288,11 +288,13 @@ size_t muon_workspace_size(const muon_tensor_t* tensors, int32_t n, int32_t ns_p
 
 int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum, int32_t nesterov,
               float weight_decay, int32_t row_norm, int32_t ns_steps, const float* ns_coeffs,
-              int32_t ns_precision, void* workspace, size_t workspace_bytes, void* stream) {
+              int32_t ns_precision, float ema_decay, void* workspace, size_t workspace_bytes, void* stream) {
     int rc = validate_tensors(tensors, n, ns_precision);
     if (rc) return rc;
     if (!std::isfinite(lr) || !std::isfinite(momentum) || !std::isfinite(weight_decay))
         return fail(MUON_ERR_INVALID_ARG, "lr, momentum and weight_decay must be finite");
+    if (!std::isfinite(ema_decay) || ema_decay < 0.f || ema_decay > 1.f)
+        return fail(MUON_ERR_INVALID_ARG, "ema_decay must be finite and in [0, 1]");
     if ((nesterov != 0 && nesterov != 1) || (row_norm != 0 && row_norm != 1))
         return fail(MUON_ERR_INVALID_ARG, "nesterov and row_norm must be 0 or 1");
     if (ns_steps < 0 || ns_steps > MUON_MAX_NS_STEPS)
@@ -315,8 +317,8 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
         for (int i = 0; i < n; ++i) {
             const muon_tensor_t& x = tensors[i];
             const size_t bytes = (size_t)x.rows * x.cols * sizeof(float);
-            const void* ptrs[4] = {x.param, x.grad, x.momentum, x.update_out};
-            for (int k = 0; k < 4; ++k) {
+            const void* ptrs[5] = {x.param, x.grad, x.momentum, x.update_out, x.ema};
+            for (int k = 0; k < 5; ++k) {
                 if (!ptrs[k]) continue;
                 const uintptr_t lo = reinterpret_cast<uintptr_t>(ptrs[k]);
                 if (lo < whi && wlo < lo + bytes)
@@ -376,6 +378,11 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
         if (cnt > kMaxFused) fuse = false;
     }
     const float keep = 1.0f - lr * weight_decay;
+    // 16-byte accesses to the caller's W / O / EMA rows
+    auto vec_ok = [](const muon_tensor_t& x) {
+        return (x.cols % 4 == 0) && (reinterpret_cast<uintptr_t>(x.param) % 16 == 0) &&
+               (reinterpret_cast<uintptr_t>(x.update_out) % 16 == 0) && (reinterpret_cast<uintptr_t>(x.ema) % 16 == 0);
+    };
     auto lr_scale = [&](const muon_tensor_t& x) {
         return lr * (float)std::sqrt(std::max(1.0, (double)x.rows / (double)x.cols));
     };
@@ -480,6 +487,8 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
                     a.c = ns_coeffs[3 * k + 2];
                     a.fuse_apply = fuse && phase == kUpdate && k == ns_steps - 1;
                     a.keep = keep;
+                    a.decay = ema_decay;
+                    a.one_minus_decay = 1.0f - ema_decay;
                     int jobs = 0, napply = 0;
                     for (int gi : ls.groups) {
                         const Group& G = p.groups[gi];
@@ -504,11 +513,11 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
                                 FusedApply& F = a.apply[napply++];
                                 F.param = x.param;
                                 F.out = x.update_out;
+                                F.ema = x.ema;
                                 F.rows = x.rows;
                                 F.cols = x.cols;
-                                F.transposed = x.rows > x.cols;
-                                F.vec = (x.cols % 4 == 0) && (reinterpret_cast<uintptr_t>(x.param) % 16 == 0) &&
-                                        (reinterpret_cast<uintptr_t>(x.update_out) % 16 == 0);
+                                F.flags = (x.rows > x.cols ? kApplyTransposed : 0) |
+                                          (vec_ok(x) ? kApplyVec : 0);
                                 F.lr_s = lr_scale(x);
                             }
                         }
@@ -526,20 +535,23 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
 
         // ---- apply: W' = (1 - lr wd) W - lr s O (unless the last NS update did it)
         const int final_buf = ns_steps & 1;
-        for (int c0 = 0; c0 < nm && !fuse; c0 += kPrepChunk) {
+        for (int c0 = 0; c0 < nm && !fuse; c0 += kApplyChunk) {
             ApplyArgs a;
             memset(&a, 0, sizeof(a));
             a.keep = keep;
+            a.decay = ema_decay;
+            a.one_minus_decay = 1.0f - ema_decay;
             a.use_scale = ns_steps == 0;
             int blocks = 0;
             size_t lds = 0;
-            for (int c = c0; c < std::min(nm, c0 + kPrepChunk); ++c) {
+            for (int c = c0; c < std::min(nm, c0 + kApplyChunk); ++c) {
                 const int i = mine[c];
                 const muon_tensor_t& x = tensors[i];
                 const Group& G = p.groups[p.group_of[i]];
                 ApplyTensor& T = a.t[a.n++];
                 T.param = x.param;
                 T.out = x.update_out;
+                T.ema = x.ema;
                 const size_t slot_off = (size_t)p.slot_of[i] * G.M * G.N * xe;
                 T.xh = ws + G.x_off[final_buf] + slot_off;
                 T.xl = ws + G.xl_off[final_buf] + slot_off;
@@ -549,8 +561,7 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
                 T.cols = x.cols;
                 T.n_pad = G.N;
                 T.transposed = x.rows > x.cols;
-                T.vec = (x.cols % 4 == 0) && (reinterpret_cast<uintptr_t>(x.param) % 16 == 0) &&
-                        (reinterpret_cast<uintptr_t>(x.update_out) % 16 == 0);
+                T.vec = vec_ok(x);
                 T.block_begin = blocks;
                 if (T.transposed) {
                     T.rb = transposed_rb(x.cols);

@@ -314,6 +314,7 @@ __global__ __launch_bounds__(256) void apply_kernel(const ApplyArgs a) {
     const float fac = a.use_scale ? *T.scale : 1.0f;
     const float keep = a.keep;
     const float lr_s = T.lr_s;
+    const float d = a.decay, omd = a.one_minus_decay;
     const size_t ld = (size_t)T.n_pad;
 
     if (!T.transposed) {
@@ -321,10 +322,12 @@ __global__ __launch_bounds__(256) void apply_kernel(const ApplyArgs a) {
         if (row >= T.rows) return;
         float* w = T.param + (size_t)row * T.cols;
         float* out = T.out ? T.out + (size_t)row * T.cols : nullptr;
+        float* ema = T.ema ? T.ema + (size_t)row * T.cols : nullptr;
         const size_t xrow = (size_t)row * ld;
         if (T.vec) {
             float4* w4 = reinterpret_cast<float4*>(w);
             float4* o4 = reinterpret_cast<float4*>(out);
+            float4* e4 = reinterpret_cast<float4*>(ema);
             for (int j = lane; j < T.cols / 4; j += kWave) {
                 float4 o = load_x4<PREC>(T.xh, T.xl, xrow + 4 * j);
                 o.x *= fac; o.y *= fac; o.z *= fac; o.w *= fac;
@@ -335,12 +338,22 @@ __global__ __launch_bounds__(256) void apply_kernel(const ApplyArgs a) {
                 wv.w = fmaf(-lr_s, o.w, keep * wv.w);
                 w4[j] = wv;
                 if (o4) o4[j] = o;
+                if (e4) {
+                    float4 ev = e4[j];
+                    ev.x = fmaf(d, ev.x, omd * wv.x);
+                    ev.y = fmaf(d, ev.y, omd * wv.y);
+                    ev.z = fmaf(d, ev.z, omd * wv.z);
+                    ev.w = fmaf(d, ev.w, omd * wv.w);
+                    e4[j] = ev;
+                }
             }
         } else {
             for (int j = lane; j < T.cols; j += kWave) {
                 const float o = fac * load_x<PREC>(T.xh, T.xl, xrow + j);
-                w[j] = fmaf(-lr_s, o, keep * w[j]);
+                const float wv = fmaf(-lr_s, o, keep * w[j]);
+                w[j] = wv;
                 if (out) out[j] = o;
+                if (ema) ema[j] = fmaf(d, ema[j], omd * wv);
             }
         }
         return;
@@ -377,10 +390,13 @@ __global__ __launch_bounds__(256) void apply_kernel(const ApplyArgs a) {
         if (row >= T.rows) break;
         float* w = T.param + (size_t)row * T.cols;
         float* out = T.out ? T.out + (size_t)row * T.cols : nullptr;
+        float* ema = T.ema ? T.ema + (size_t)row * T.cols : nullptr;
         const float* o = lds_o + (size_t)rr * pitch;
         for (int j = lane; j < T.cols; j += kWave) {
-            w[j] = fmaf(-lr_s, o[j], keep * w[j]);
+            const float wv = fmaf(-lr_s, o[j], keep * w[j]);
+            w[j] = wv;
             if (out) out[j] = o[j];
+            if (ema) ema[j] = fmaf(d, ema[j], omd * wv);
         }
     }
 }

@@ -58,12 +58,13 @@ constexpr int kMaxFused = 72;
 struct FusedApply {
     float* param;
     float* out;          // optional copy of O
+    float* ema;          // optional weight EMA advanced with W'
     int rows, cols;      // stored shape
-    int transposed;
-    int vec;             // param/out 16-byte aligned and the 8-wide runs are aligned
     float lr_s;
-    int pad_;
+    int flags;           // kApplyTransposed | kApplyVec
 };
+constexpr int kApplyTransposed = 1;  // stored W is X^T
+constexpr int kApplyVec = 2;         // param/out/ema 16-byte aligned and cols % 4 == 0
 
 struct NsGroup {
     void* x[2];      // bf16: hi planes (ping-pong); fp32: X planes.  [count][M][N]
@@ -86,6 +87,7 @@ struct NsArgs {
     float a, b, c;
     int fuse_apply;  // last update: write W' (and O) instead of X
     float keep;      // 1 - lr*wd
+    float decay, one_minus_decay;  // weight EMA
     FusedApply apply[kMaxFused];
 };
 
@@ -96,6 +98,7 @@ enum NsMode { kModeBf16 = 0, kModeFp32 = 1, kModeBf16x3 = 2 };  // the ns_precis
 struct ApplyTensor {
     float* param;
     float* out;          // optional copy of O (stored layout)
+    float* ema;          // optional weight EMA advanced with W'
     const void* xh;      // final X: bf16 hi plane or fp32 plane
     const void* xl;      // bf16 lo plane
     const float* scale;  // Frobenius scale (used when no NS step ran)
@@ -105,12 +108,14 @@ struct ApplyTensor {
     int transposed;
     int rb;
     int block_begin;
-    int vec;             // param/out 16-byte aligned and cols % 4 == 0
+    int vec;             // param/out/ema 16-byte aligned and cols % 4 == 0
 };
+constexpr int kApplyChunk = 46;    // tensors per apply launch
 struct ApplyArgs {
-    ApplyTensor t[kPrepChunk];
+    ApplyTensor t[kApplyChunk];
     int n;
     float keep;          // 1 - lr*wd
+    float decay, one_minus_decay;  // weight EMA
     int use_scale;       // 1 when ns_steps == 0
 };
 

@@ -320,9 +320,11 @@ __device__ inline void store8(void* hi, void* lo, size_t idx, const float* v) {
 }
 
 // Fused weight update for up to 8 consecutive stored elements starting at idx:
-// W' = keep*W - lr_s*O, and the optional copy of O.
-__device__ inline void apply8(const FusedApply& F, size_t idx, int count, const float* v, float keep) {
-    if (count >= 8 && F.vec) {
+// W' = keep*W - lr_s*O, the optional copy of O, and the optional weight EMA
+// E' = d*E + (1-d)*W'.
+__device__ inline void apply8(const FusedApply& F, size_t idx, int count, const float* v, float keep, float d,
+                              float omd) {
+    if (count >= 8 && (F.flags & kApplyVec)) {
         floatx4* w4 = reinterpret_cast<floatx4*>(F.param + idx);
         floatx4 w0 = w4[0], w1 = w4[1];
 #pragma unroll
@@ -340,11 +342,24 @@ __device__ inline void apply8(const FusedApply& F, size_t idx, int count, const 
             o4[0] = o0;
             o4[1] = o1;
         }
+        if (F.ema) {
+            floatx4* e4 = reinterpret_cast<floatx4*>(F.ema + idx);
+            floatx4 e0 = e4[0], e1 = e4[1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                e0[e] = fmaf(d, e0[e], omd * w0[e]);
+                e1[e] = fmaf(d, e1[e], omd * w1[e]);
+            }
+            e4[0] = e0;
+            e4[1] = e1;
+        }
         return;
     }
     for (int e = 0; e < count && e < 8; ++e) {
-        F.param[idx + e] = fmaf(-F.lr_s, v[e], keep * F.param[idx + e]);
+        const float w = fmaf(-F.lr_s, v[e], keep * F.param[idx + e]);
+        F.param[idx + e] = w;
         if (F.out) F.out[idx + e] = v[e];
+        if (F.ema) F.ema[idx + e] = fmaf(d, F.ema[idx + e], omd * w);
     }
 }
 
@@ -664,15 +679,15 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
                 }
                 if (!FUSE) {
                     store8<PREC>(G.x[src ^ 1], G.xl[src ^ 1], idx, v);
-                } else if (!args.apply[G.apply_begin + job.slot].transposed) {
+                } else if (!(args.apply[G.apply_begin + job.slot].flags & kApplyTransposed)) {
                     // X row = stored row, X column = stored column
                     const FusedApply& F = args.apply[G.apply_begin + job.slot];
                     const int gi = row_base + lr, gj = job.tj * kTile + lc;
-                    if (gi < F.rows) apply8(F, (size_t)gi * F.cols + gj, F.cols - gj, v, args.keep);
+                    if (gi < F.rows) apply8(F, (size_t)gi * F.cols + gj, F.cols - gj, v, args.keep, args.decay, args.one_minus_decay);
                 }
             }
             if ((PHASE != kUpdate && !diag) ||
-                (PHASE == kUpdate && FUSE && args.apply[G.apply_begin + job.slot].transposed)) {
+                (PHASE == kUpdate && FUSE && (args.apply[G.apply_begin + job.slot].flags & kApplyTransposed))) {
                 // keep the final value for the mirrored write
                 floatx4 a, b;
 #pragma unroll
@@ -681,7 +696,7 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
                 *reinterpret_cast<floatx4*>(sp + 4) = b;
             }
         }
-        if (PHASE == kUpdate && FUSE && args.apply[G.apply_begin + job.slot].transposed) {
+        if (PHASE == kUpdate && FUSE && (args.apply[G.apply_begin + job.slot].flags & kApplyTransposed)) {
             __syncthreads();
             // stored W is X^T: W row tj*128 + c, columns row_base + 8*chunk .. +7
             const FusedApply& F = args.apply[G.apply_begin + job.slot];
@@ -694,7 +709,7 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
                     float v[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] = stage[(chunk * 8 + e) * kStagePitch + c];
-                    apply8(F, (size_t)wr * F.cols + wc, F.cols - wc, v, args.keep);
+                    apply8(F, (size_t)wr * F.cols + wc, F.cols - wc, v, args.keep, args.decay, args.one_minus_decay);
                 }
             }
         }

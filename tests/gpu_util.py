@@ -49,18 +49,38 @@ def f32(x) -> float:
 
 
 def gpu_step(mats, grads, moms, *, lr, momentum, wd, coeffs, nesterov=True, row_norm=True,
-             ns_precision=0, want_o=True, workspace=None):
-    """Upload, run one library step, return (W', M', O) as host arrays (O None if not requested)."""
+             ns_precision=0, want_o=True, workspace=None, emas=None, ema_decay=0.0):
+    """Upload, run one library step, return (W', M', O, E') as host arrays.
+
+    O is None if not requested; emas (host arrays or None entries) are the EMA
+    shadows advanced inside the step, E' is None where no shadow was given.
+    """
     import torch
     import muon_optimizer_step_amd as ms
     P = [dev(w) for w in mats]
     G = [dev(g) for g in grads]
     M = [dev(m) for m in moms]
     O = [torch.full_like(p, float("nan")) for p in P] if want_o else None
+    E = [dev(e) if e is not None else None for e in emas] if emas is not None else None
     ms.muon_step(P, G, M, lr=lr, momentum=momentum, weight_decay=wd, coeffs=coeffs, nesterov=nesterov,
-                 row_norm=row_norm, ns_precision=ns_precision, update_outs=O, workspace=workspace)
+                 row_norm=row_norm, ns_precision=ns_precision, update_outs=O, workspace=workspace,
+                 emas=E, ema_decay=ema_decay)
     torch.cuda.synchronize()
-    return [host(p) for p in P], [host(m) for m in M], ([host(o) for o in O] if want_o else None)
+    e_out = [host(e) if e is not None else None for e in E] if E is not None else None
+    return [host(p) for p in P], [host(m) for m in M], ([host(o) for o in O] if want_o else None), e_out
+
+
+def check_fused_ema(e_in, w_gpu, e_gpu, decay, label=""):
+    """E' of the step against the oracle EMA fed the GPU's W'; returns the worst error."""
+    worst = 0.0
+    for i, (e0, w, e) in enumerate(zip(e_in, w_gpu, e_gpu)):
+        if e0 is None:
+            assert e is None
+            continue
+        err = rel_max(e, om.ema_update(e0, w, f32(decay)))
+        assert err <= ELEM_TOL, f"{label} fused EMA tensor {i}: {err:.3e}"
+        worst = max(worst, err)
+    return worst
 
 
 def check_layers(w_in, g_in, m_in, w_gpu, m_gpu, o_gpu, *, lr, momentum, wd, coeffs, nesterov, row_norm,

@@ -51,21 +51,21 @@ def test_header_constants_match_binding():
         m = re.search(rf"#define {name} \(?(-?\d+)\)?", text)
         assert m, name
         assert int(m.group(1)) == getattr(_lib, name), name
-    assert ctypes.sizeof(_lib.MuonTensor) == 40
+    assert ctypes.sizeof(_lib.MuonTensor) == 48
 
 
 # Fake, well-separated device addresses: validation only compares them.
 BASE = 1 << 40
 
 
-def _t(i, rows, cols, out=False):
+def _t(i, rows, cols, out=False, ema=False):
     span = 1 << 30
-    p = BASE + 4 * i * span
-    return (p, p + span, p + 2 * span, (p + 3 * span) if out else 0, rows, cols)
+    p = BASE + 5 * i * span
+    return (p, p + span, p + 2 * span, (p + 3 * span) if out else 0, (p + 4 * span) if ema else 0, rows, cols)
 
 
 def _call(entries, lr=0.02, mu=0.95, nesterov=1, wd=0.1, row_norm=1, steps=5, coeffs="std",
-          prec=0, ws=BASE + (1 << 45), ws_bytes=1 << 40, n=None):
+          prec=0, ema_decay=0.9965, ws=BASE + (1 << 45), ws_bytes=1 << 40, n=None):
     lib = _lib.load()
     table = _lib.tensor_table(entries)
     if coeffs == "std":
@@ -74,7 +74,7 @@ def _call(entries, lr=0.02, mu=0.95, nesterov=1, wd=0.1, row_norm=1, steps=5, co
     else:
         cptr = coeffs
     rc = lib.muon_step(table, len(entries) if n is None else n, lr, mu, nesterov, wd, row_norm, steps, cptr, prec,
-                       ctypes.c_void_p(ws), ws_bytes, None)
+                       ema_decay, ctypes.c_void_p(ws), ws_bytes, None)
     return rc, lib.muon_last_error().decode()
 
 
@@ -90,12 +90,15 @@ def _call(entries, lr=0.02, mu=0.95, nesterov=1, wd=0.1, row_norm=1, steps=5, co
     (dict(steps=-1), _lib.MUON_ERR_INVALID_ARG, "ns_steps"),
     (dict(steps=_lib.MUON_MAX_NS_STEPS + 1), _lib.MUON_ERR_INVALID_ARG, "ns_steps"),
     (dict(steps=3, coeffs=None), _lib.MUON_ERR_INVALID_ARG, "ns_coeffs is NULL"),
+    (dict(ema_decay=1.5), _lib.MUON_ERR_INVALID_ARG, "ema_decay"),
+    (dict(ema_decay=-0.25), _lib.MUON_ERR_INVALID_ARG, "ema_decay"),
+    (dict(ema_decay=float("nan")), _lib.MUON_ERR_INVALID_ARG, "ema_decay"),
     (dict(ws=0), _lib.MUON_ERR_WORKSPACE, "workspace is NULL"),
     (dict(ws=BASE + (1 << 45) + 16), _lib.MUON_ERR_WORKSPACE, "256-byte"),
     (dict(ws_bytes=1024), _lib.MUON_ERR_WORKSPACE, "needs"),
 ])
 def test_muon_step_rejects_bad_arguments(kw, code, msg):
-    rc, err = _call([_t(0, 64, 32), _t(1, 16, 48)], **kw)
+    rc, err = _call([_t(0, 64, 32, ema=True), _t(1, 16, 48)], **kw)
     assert rc == code and msg in err, (rc, err)
 
 
@@ -116,25 +119,33 @@ def test_muon_step_rejects_bad_shapes(shape, code):
 
 
 def test_muon_step_rejects_null_and_aliased_buffers():
-    p, g, m, o, r, c = _t(0, 64, 64)
-    rc, err = _call([(0, g, m, 0, r, c)])
+    p, g, m, o, e, r, c = _t(0, 64, 64, ema=True)
+    rc, err = _call([(0, g, m, 0, 0, r, c)])
     assert rc == _lib.MUON_ERR_INVALID_ARG and "non-NULL" in err
-    rc, err = _call([(p, p, m, 0, r, c)])          # grad aliases param
+    rc, err = _call([(p, p, m, 0, 0, r, c)])          # grad aliases param
     assert rc == _lib.MUON_ERR_UNSUPPORTED and "overlap" in err
-    rc, err = _call([(p, g, m, g + 256, r, c)])    # update_out overlaps grad
+    rc, err = _call([(p, g, m, g + 256, 0, r, c)])    # update_out overlaps grad
     assert rc == _lib.MUON_ERR_UNSUPPORTED
-    q = _t(1, 64, 64)
-    rc, err = _call([(p, g, m, 0, r, c), (q[0], q[1], m + 4, 0, r, c)])  # two tensors share a buffer
-    assert rc == _lib.MUON_ERR_UNSUPPORTED and "tensors 0 and 1" in err
-    rc, err = _call([(p + 2, g, m, 0, r, c)])      # misaligned
+    rc, err = _call([(p, g, m, 0, p + 512, r, c)])    # ema overlaps param
+    assert rc == _lib.MUON_ERR_UNSUPPORTED and "overlap" in err
+    rc, err = _call([(p, g, m, 0, e + 2, r, c)])      # misaligned ema
     assert rc == _lib.MUON_ERR_INVALID_ARG and "aligned" in err
-    rc, err = _call([(p, g, m, 0, r, c)], ws=p - 256)  # workspace overlaps a tensor
+    q = _t(1, 64, 64)
+    rc, err = _call([(p, g, m, 0, 0, r, c), (q[0], q[1], m + 4, 0, 0, r, c)])  # two tensors share a buffer
+    assert rc == _lib.MUON_ERR_UNSUPPORTED and "tensors 0 and 1" in err
+    rc, err = _call([(p, g, m, 0, e, r, c), (q[0], q[1], q[2], 0, e + 64, r, c)])  # two tensors share an ema
+    assert rc == _lib.MUON_ERR_UNSUPPORTED and "tensors 0 and 1" in err
+    rc, err = _call([(p + 2, g, m, 0, 0, r, c)])      # misaligned
+    assert rc == _lib.MUON_ERR_INVALID_ARG and "aligned" in err
+    rc, err = _call([(p, g, m, 0, 0, r, c)], ws=p - 256)  # workspace overlaps a tensor
+    assert rc == _lib.MUON_ERR_UNSUPPORTED and "workspace" in err
+    rc, err = _call([(p, g, m, 0, e, r, c)], ws=e + 1024)  # workspace overlaps an ema
     assert rc == _lib.MUON_ERR_UNSUPPORTED and "workspace" in err
 
 
 def _ws(shapes, prec=0):
     lib = _lib.load()
-    table = _lib.tensor_table((0, 0, 0, 0, r, c) for r, c in shapes)
+    table = _lib.tensor_table((0, 0, 0, 0, 0, r, c) for r, c in shapes)
     return lib.muon_workspace_size(table, len(shapes), prec)
 
 

@@ -20,8 +20,10 @@ def test_zero_ns_steps_gives_x0(ns_precision, tol):
     mats = [rng.standard_normal(s).astype(np.float32) for s in shapes]
     grads = [rng.standard_normal(s).astype(np.float32) for s in shapes]
     moms = [rng.standard_normal(s).astype(np.float32) for s in shapes]
-    w_gpu, m_gpu, o_gpu = gu.gpu_step(mats, grads, moms, lr=0.1, momentum=0.5, wd=0.2, coeffs=[],
-                                      ns_precision=ns_precision)
+    emas = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    w_gpu, m_gpu, o_gpu, e_gpu = gu.gpu_step(mats, grads, moms, lr=0.1, momentum=0.5, wd=0.2, coeffs=[],
+                                             ns_precision=ns_precision, emas=emas, ema_decay=0.75)
+    gu.check_fused_ema(emas, w_gpu, e_gpu, 0.75)
     for i in range(len(shapes)):
         _, u = om.momentum_update(moms[i], grads[i], gu.f32(0.5), True)
         assert gu.rel_frob(o_gpu[i], om.orthogonalize(u, [], True)) <= tol
@@ -36,8 +38,8 @@ def test_zero_gradient_and_zero_rows():
     z = np.zeros((96, 160), np.float32)
     g1 = rng.standard_normal((96, 160)).astype(np.float32)
     g1[[3, 50, 95]] = 0.0
-    w_gpu, m_gpu, o_gpu = gu.gpu_step([w0, w0.copy()], [z, g1], [z.copy(), z.copy()], lr=0.1, momentum=0.9,
-                                      wd=0.5, coeffs=STD)
+    w_gpu, m_gpu, o_gpu, _ = gu.gpu_step([w0, w0.copy()], [z, g1], [z.copy(), z.copy()], lr=0.1, momentum=0.9,
+                                         wd=0.5, coeffs=STD)
     assert np.all(o_gpu[0] == 0) and np.all(m_gpu[0] == 0)
     assert gu.rel_max(w_gpu[0], (1 - gu.f32(0.1) * gu.f32(0.5)) * w0.astype(np.float64)) <= gu.ELEM_TOL
     assert np.all(o_gpu[1][[3, 50, 95]] == 0)
@@ -59,10 +61,11 @@ def test_deterministic_and_workspace_contents_do_not_matter():
         P = [gu.dev(p) for p in st["params"]]
         M = [gu.dev(m) for m in st["moms"]]
         O = [torch.empty_like(p) for p in P]
+        E = [gu.dev(e) for e in wl.make_independent_ema(w, 12)]
         ms.muon_step(P, [gu.dev(g) for g in grads], M, lr=w.lr, momentum=w.momentum, weight_decay=w.weight_decay,
-                     coeffs=STD, update_outs=O, workspace=ws)
+                     coeffs=STD, update_outs=O, emas=E, ema_decay=w.ema_decay, workspace=ws)
         torch.cuda.synchronize()
-        outs.append([gu.host(t) for t in P + M + O])
+        outs.append([gu.host(t) for t in P + M + O + E])
     for other in outs[1:]:
         for a, b in zip(outs[0], other):
             assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
@@ -91,7 +94,10 @@ def test_many_tensors_and_shape_groups():
     grads = [rng.standard_normal(s).astype(np.float32) for s in shapes]
     moms = [np.zeros(s, np.float32) for s in shapes]
     coeffs = wl.coeff_table(wl.workload(4), 3).tolist()
-    w_gpu, m_gpu, o_gpu = gu.gpu_step(mats, grads, moms, lr=0.02, momentum=0.95, wd=0.1, coeffs=coeffs)
+    emas = [rng.standard_normal(s).astype(np.float32) if i % 3 else None for i, s in enumerate(shapes)]
+    w_gpu, m_gpu, o_gpu, e_gpu = gu.gpu_step(mats, grads, moms, lr=0.02, momentum=0.95, wd=0.1, coeffs=coeffs,
+                                             emas=emas, ema_decay=0.5)
+    gu.check_fused_ema(emas, w_gpu, e_gpu, 0.5)
     for i, s in enumerate(shapes):
         gu.check_layers(mats[i], grads[i], moms[i], w_gpu[i], m_gpu[i], o_gpu[i], lr=0.02, momentum=0.95, wd=0.1,
                         coeffs=coeffs, nesterov=True, row_norm=True, ns_tol=gu.NS_TOL_BF16, label=f"{i} {s}")
@@ -123,8 +129,15 @@ def test_maximum_sizes_on_a_known_spectrum(rows, cols):
     P = torch.zeros_like(G)
     M = torch.zeros_like(G)
     O = torch.empty_like(G)
-    ms.muon_step([P], [G], [M], lr=1.0, momentum=0.0, weight_decay=0.0, coeffs=STD, row_norm=False, update_outs=[O])
+    E = torch.zeros_like(G)
+    ms.muon_step([P], [G], [M], lr=1.0, momentum=0.0, weight_decay=0.0, coeffs=STD, row_norm=False, update_outs=[O],
+                 emas=[E], ema_decay=0.5)
     torch.cuda.synchronize()
+    # W' = -s*O from W = 0 and E = 0: E' = 0.5*W' exactly, over every element
+    s = max(1.0, rows / cols) ** 0.5
+    assert torch.equal(E, 0.5 * P)
+    assert float((P + np.float32(s) * O).abs().max()) <= 1e-6 * float(O.abs().max())
+    del E
     v32 = vals.float().double().numpy()
     x0 = v32 / (np.sqrt(np.sum(v32 * v32)) + 1e-7)
     want = np.array([om.newton_schulz(np.array([[x]]), STD)[0, 0] for x in x0])
@@ -173,7 +186,10 @@ def test_more_matrices_than_the_fused_apply_table():
     mats = [rng.standard_normal(s).astype(np.float32) for s in shapes]
     grads = [rng.standard_normal(s).astype(np.float32) for s in shapes]
     moms = [rng.standard_normal(s).astype(np.float32) for s in shapes]
-    w_gpu, m_gpu, o_gpu = gu.gpu_step(mats, grads, moms, lr=0.03, momentum=0.9, wd=0.1, coeffs=STD)
+    emas = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    w_gpu, m_gpu, o_gpu, e_gpu = gu.gpu_step(mats, grads, moms, lr=0.03, momentum=0.9, wd=0.1, coeffs=STD,
+                                             emas=emas, ema_decay=0.9965)
+    gu.check_fused_ema(emas, w_gpu, e_gpu, 0.9965)
     for i in range(0, 80, 7):
         gu.check_layers(mats[i], grads[i], moms[i], w_gpu[i], m_gpu[i], o_gpu[i], lr=0.03, momentum=0.9, wd=0.1,
                         coeffs=STD, nesterov=True, row_norm=True, ns_tol=gu.NS_TOL_BF16, label=f"{i}")

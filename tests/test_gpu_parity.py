@@ -27,9 +27,13 @@ def _run_workload(cfg, seed, o_sample=None):
     nm = len(w.matrices)
     mats, moms = st["params"][:nm], st["moms"]
     grads = wl.make_grads(w, seed, 0)
-    w_gpu, m_gpu, o_gpu = gu.gpu_step(mats, grads, moms, lr=w.lr, momentum=w.momentum, wd=w.weight_decay,
-                                      coeffs=coeffs.tolist(), nesterov=w.nesterov, row_norm=w.row_norm,
-                                      ns_precision=w.ns_precision)
+    # workloads without an EMA still run the fused EMA at the pages' decay
+    decay = w.ema_decay if w.ema_decay is not None else 0.9965
+    e_in = wl.make_independent_ema(w, seed + 1)[:nm]
+    w_gpu, m_gpu, o_gpu, e_gpu = gu.gpu_step(mats, grads, moms, lr=w.lr, momentum=w.momentum, wd=w.weight_decay,
+                                             coeffs=coeffs.tolist(), nesterov=w.nesterov, row_norm=w.row_norm,
+                                             ns_precision=w.ns_precision, emas=e_in, ema_decay=decay)
+    e_worst = gu.check_fused_ema(e_in, w_gpu, e_gpu, decay, label=w.name)
     tol = gu.NS_TOL_BF16 if w.ns_precision == 0 else gu.NS_TOL_FP32
     if o_sample is None:
         o_sample = range(nm)
@@ -41,7 +45,7 @@ def _run_workload(cfg, seed, o_sample=None):
         if e is not None:
             errs[w.matrices[i][0]] = e
     gu.say(f"[parity] workload {cfg} seed {seed} NS errors: " +
-           ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+           ", ".join(f"{k}={v:.2e}" for k, v in errs.items()) + f"; fused EMA worst {e_worst:.2e}")
     return w, st, w_gpu
 
 
@@ -89,6 +93,8 @@ def test_full_model_1024d_with_ema():
 def test_structured_gradients_ten_steps():
     """Rank-8 + noise gradients, drawn 4-step table, momentum and EMA carried over 10 steps.
 
+    The matrices' EMA advances inside the step, the other tensors' in ema_update.
+
     Each step is checked layer by layer against the oracle fed the GPU's state
     from the step before (the momentum chain is exact fp32, the NS error is
     re-measured every step on sampled matrices).  The drift of W after ten
@@ -116,8 +122,9 @@ def test_structured_gradients_ten_steps():
         e_in = [gu.host(e) for e in E]
         G = [gu.dev(g) for g in grads]
         ms.muon_step(P[:nm], G, M, lr=w.lr, momentum=w.momentum, weight_decay=w.weight_decay,
-                     coeffs=coeffs.tolist(), nesterov=True, row_norm=True, update_outs=O)
-        ms.ema_update(E, P, w.ema_decay)
+                     coeffs=coeffs.tolist(), nesterov=True, row_norm=True, update_outs=O,
+                     emas=E[:nm], ema_decay=w.ema_decay)
+        ms.ema_update(E[nm:], P[nm:], w.ema_decay)
         torch.cuda.synchronize()
         w_out = [gu.host(p) for p in P[:nm]]
         worst = 0.0
@@ -149,8 +156,8 @@ def test_compensated_mode_one_layer():
     grads = wl.make_grads(w, wl.PRIMARY_SEED, 0)
     coeffs = wl.coeff_table(w, wl.PRIMARY_SEED)
     mats, moms = st["params"], st["moms"]
-    w_gpu, m_gpu, o_gpu = gu.gpu_step(mats, grads, moms, lr=w.lr, momentum=w.momentum, wd=w.weight_decay,
-                                      coeffs=coeffs.tolist(), ns_precision=2)
+    w_gpu, m_gpu, o_gpu, _ = gu.gpu_step(mats, grads, moms, lr=w.lr, momentum=w.momentum, wd=w.weight_decay,
+                                         coeffs=coeffs.tolist(), ns_precision=2)
     errs = []
     for i in range(len(mats)):
         errs.append(gu.check_layers(mats[i], grads[i], moms[i], w_gpu[i], m_gpu[i], o_gpu[i], lr=w.lr,
@@ -169,9 +176,14 @@ def test_ragged_shapes(ns_precision, nesterov, row_norm):
     grads = [rng.standard_normal((r, c)).astype(np.float32) for _, r, c in shapes]
     moms = [(0.5 * rng.standard_normal((r, c))).astype(np.float32) for _, r, c in shapes]
     coeffs = wl.coeff_table(wl.workload(4), 5).tolist()
+    # every other matrix carries an EMA shadow (vector and scalar, row and column epilogues)
+    emas = [rng.standard_normal((r, c)).astype(np.float32) if i % 2 == 0 else None
+            for i, (_, r, c) in enumerate(shapes)]
     gu.say(f"[parity] ragged shapes prec={ns_precision} nesterov={nesterov} row_norm={row_norm}")
-    w_gpu, m_gpu, o_gpu = gu.gpu_step(mats, grads, moms, lr=0.05, momentum=0.9, wd=0.1, coeffs=coeffs,
-                                      nesterov=nesterov, row_norm=row_norm, ns_precision=ns_precision)
+    w_gpu, m_gpu, o_gpu, e_gpu = gu.gpu_step(mats, grads, moms, lr=0.05, momentum=0.9, wd=0.1, coeffs=coeffs,
+                                             nesterov=nesterov, row_norm=row_norm, ns_precision=ns_precision,
+                                             emas=emas, ema_decay=0.9)
+    gu.check_fused_ema(emas, w_gpu, e_gpu, 0.9, label="ragged")
     tol = {0: gu.NS_TOL_BF16, 1: gu.NS_TOL_FP32, 2: gu.NS_TOL_BF16X3}[ns_precision]
     for i, (nm, r, c) in enumerate(shapes):
         gu.check_layers(mats[i], grads[i], moms[i], w_gpu[i], m_gpu[i], o_gpu[i], lr=0.05, momentum=0.9, wd=0.1,

@@ -39,6 +39,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=1337)
+    ap.add_argument("--rotate", type=int, default=2, help="independent state copies used in turn (MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -46,13 +47,16 @@ def parse():
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter files of this bench and of "
                          "--calibrate-copy into profiles/hbm_traffic.json, then exit (no GPU needed)")
+    ap.add_argument("--summarize-mfma", metavar="MOPS_CSV",
+                    help="turn a rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 counter "
+                         "file of this bench into profiles/mfma_counters.json, then exit (no GPU needed)")
     return ap.parse_args()
 
 
 def _kernel_key(name: str) -> str:
     """Library kernel symbol -> the name the profiling hook reports."""
     import re
-    m = re.search(r"ns_kernel<(\d), (\d), (true|false), (true|false)>", name)
+    m = re.search(r"ns_(?:sym_)?kernel<(\d), (\d), (true|false)(?:, (true|false))?>", name)
     if m:
         phase, prec, comp, fuse = int(m.group(1)), int(m.group(2)), m.group(3) == "true", m.group(4) == "true"
         base = ["ns_gram", "ns_square", "ns_update", "ns_update"][phase]
@@ -105,6 +109,35 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, cop
     print(json.dumps(out, indent=1))
 
 
+def summarize_mfma(csv_path):
+    """Executed MFMA flops per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16 / _F32, 512 flops per count)."""
+    kernels = {}
+    for counter in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32"):
+        for k, v in _per_dispatch(csv_path, counter).items():
+            if k == "copy":
+                continue
+            kernels.setdefault(k, {})[counter] = v
+    out = {"source_hash": source_hash(),
+           "kernels": {k: dict(v, flops_per_launch=512.0 * sum(v.values())) for k, v in sorted(kernels.items())}}
+    path = os.path.join(ROOT, "profiles", "mfma_counters.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def mfma_counter_flops(kernel: str):
+    """Executed MFMA flops per launch from the committed counter summary, if it matches these sources."""
+    path = os.path.join(ROOT, "profiles", "mfma_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    if data.get("source_hash") != source_hash():
+        return None
+    k = data.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("flops_per_launch")
+
+
 def calibrate_copy(mib: int) -> None:
     """A plain copy of known size: the reference for scaling FETCH_SIZE / WRITE_SIZE counters."""
     import torch
@@ -118,16 +151,16 @@ def calibrate_copy(mib: int) -> None:
     print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 5}), flush=True)
 
 
-def kernel_model(w):
-    """Algorithmic work of each kernel: flops and HBM bytes.
+def kernel_model(w, fused=True):
+    """Algorithmic work of each kernel per step: flops and HBM bytes.
 
-    NS kernels: per launch (one launch per iteration, every launch the same).
-    prep, apply and ema: per step (they may be split into several launches by
-    tensor-table chunking).  Bytes count each operand once at its stored width:
-    X is a bf16 hi + lo pair (4 B), A and B are bf16 (hi + lo for A), weights,
-    gradients, momenta and EMA shadows are fp32.  The matrices' EMA rides on
-    the weight apply (fused into the last NS update, or the apply kernel);
-    the ema kernel covers the other parameters.
+    The NS phases run once per iteration (split over the lanes' launches); the
+    last update carries the weight apply when `fused`, else the apply kernel
+    does.  Per launch figures are these totals divided by the launches per
+    step.  Bytes count each operand once at its stored width: X is a bf16
+    hi + lo pair (4 B), A and B are bf16 (hi + lo for A), weights, gradients,
+    momenta and EMA shadows are fp32.  The matrices' EMA rides on the weight
+    apply; the ema kernel covers the other parameters.
     """
     gram_f = sq_f = 0.0
     gram_b = sq_b = upd_b = upda_b = 0.0
@@ -141,15 +174,20 @@ def kernel_model(w):
         upd_b += 8.0 * m * n + 2.0 * m * m       # read X hi + lo and B; write X hi + lo
         upda_b += 20.0 * m * n + 2.0 * m * m     # read X hi + lo and B; read + write W and E
         elems += r * c
-    return {
-        "ns_gram_bf16": {"per": "launch", "flops": gram_f, "bytes": gram_b},      # A = X X^T
-        "ns_square_bf16": {"per": "launch", "flops": sq_f, "bytes": sq_b},        # B = b A + c A A
-        "ns_update_bf16": {"per": "launch", "flops": gram_f, "bytes": upd_b},     # X <- a X + B X
-        "ns_update_apply_bf16": {"per": "launch", "flops": gram_f, "bytes": upda_b},  # last X, then W', E'
-        "prep": {"per": "step", "flops": 0.0, "bytes": 16.0 * elems},   # read G, M; write M, X0 hi + lo
-        "apply": {"per": "step", "flops": 0.0, "bytes": 20.0 * elems},  # read W, E, X hi + lo; write W, E
-        "ema": {"per": "step", "flops": 0.0, "bytes": 12.0 * (w.n_params - elems)},  # read E, P; write E
+    k = w.ns_steps
+    plain_updates = k - 1 if fused else k
+    model = {
+        "ns_gram_bf16": {"flops": k * gram_f, "bytes": k * gram_b},                        # A = X X^T
+        "ns_square_bf16": {"flops": k * sq_f, "bytes": k * sq_b},                          # B = b A + c A A
+        "ns_update_bf16": {"flops": plain_updates * gram_f, "bytes": plain_updates * upd_b},  # X <- a X + B X
+        "prep": {"flops": 0.0, "bytes": 16.0 * elems},                   # read G, M; write M, X0 hi + lo
+        "ema": {"flops": 0.0, "bytes": 12.0 * (w.n_params - elems)},     # read E, P; write E
     }
+    if fused:
+        model["ns_update_apply_bf16"] = {"flops": gram_f, "bytes": upda_b}  # last X, then W' and E'
+    else:
+        model["apply"] = {"flops": 0.0, "bytes": 20.0 * elems}           # read W, E, X hi + lo; write W, E
+    return model
 
 
 def source_hash() -> str:
@@ -179,19 +217,17 @@ def cpu_baseline(w, seed, target_s):
     import numpy as np
     import oracle.muon as om
     import workloads as wl
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    from threadpoolctl import threadpool_info, threadpool_limits
+    pools = threadpool_info()
+    threads = max([d.get("num_threads", 1) for d in pools] or [1])
+    blas = ", ".join(sorted({f"{d.get('internal_api')} {d.get('version')}" for d in pools})) or "unknown"
     st = wl.make_state(w, seed)
     grads = wl.make_grads(w, seed, 0)
     coeffs = wl.coeff_table(w, seed).astype(np.float64)
     f = lambda x: float(np.float32(x))
     nm = len(w.matrices)
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
+
+    def one_step():
         new_w = []
         for i in range(nm):
             wn, _, _ = om.muon_step_matrix(st["params"][i], grads[i], st["moms"][i], lr=f(w.lr), mu=f(w.momentum),
@@ -200,13 +236,23 @@ def cpu_baseline(w, seed, target_s):
         post = new_w + st["params"][nm:]
         for e, p in zip(st["ema"], post):
             om.ema_update(e, p, f(w.ema_decay))
+
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        one_step()
         reps += 1
         el = time.perf_counter() - t0
         if el >= target_s or reps >= 20:
             break
+    with threadpool_limits(limits=1):
+        t1 = time.perf_counter()
+        one_step()
+        el1 = time.perf_counter() - t1
     return {"value": reps / el, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{reps} full step(s) of the float64 NumPy oracle on the same workload "
-                      f"(66 matrices + EMA over {w.n_params:,} params), {el:.1f} s"}
+                      f"(66 matrices + EMA over {w.n_params:,} params), {el:.1f} s",
+            "blas": blas, "single_thread": {"value": 1.0 / el1, "unit": "steps/s", "sample": f"1 step, {el1:.1f} s"}}
 
 
 def main():
@@ -221,6 +267,9 @@ def main():
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
         return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
+        return
     import numpy as np
     import torch
     import muon_optimizer_step_amd as ms
@@ -229,25 +278,37 @@ def main():
     w = wl.workload(WORKLOAD)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    st = wl.make_state(w, args.seed)
-    grads = wl.make_grads(w, args.seed, 0)
     coeffs = wl.coeff_table(w, args.seed).tolist()
     nm = len(w.matrices)
-    P = [torch.from_numpy(p).to(dev) for p in st["params"]]
-    G = [torch.from_numpy(g).to(dev) for g in grads]
-    M = [torch.from_numpy(m).to(dev) for m in st["moms"]]
-    E = [torch.from_numpy(e).to(dev) for e in st["ema"]]
-    del st, grads
-    step_muon = ms.PreparedMuonStep(P[:nm], G, M, emas=E[:nm])
-    step_ema = ms.PreparedEma(E[nm:], P[nm:])
+    # args.rotate independent copies of the whole state (seeds seed, seed + 1, ...),
+    # used in turn, so that no step finds the previous step's tensors in the
+    # 256 MB MALL.  One workspace serves all of them (the steps are serial on
+    # one stream).
+    states = []
+    workspace = None
+    for r in range(args.rotate):
+        st = wl.make_state(w, args.seed + r)
+        grads = wl.make_grads(w, args.seed + r, 0)
+        P = [torch.from_numpy(p).to(dev) for p in st["params"]]
+        G = [torch.from_numpy(g).to(dev) for g in grads]
+        M = [torch.from_numpy(m).to(dev) for m in st["moms"]]
+        E = [torch.from_numpy(e).to(dev) for e in st["ema"]]
+        del st, grads
+        muon = ms.PreparedMuonStep(P[:nm], G, M, emas=E[:nm], workspace=workspace)
+        workspace = muon.workspace
+        states.append((muon, ms.PreparedEma(E[nm:], P[nm:])))
     stream = torch.cuda.current_stream(dev)
+    turn = [0]
 
     def step():
+        step_muon, step_ema = states[turn[0] % len(states)]
+        turn[0] += 1
         step_muon(lr=w.lr, momentum=w.momentum, weight_decay=w.weight_decay, coeffs=coeffs,
                   ema_decay=w.ema_decay, stream=stream)
         step_ema(w.ema_decay, stream=stream)
 
-    print(f"[bench] workload {w.name}: {nm} matrices, {w.n_params:,} params, warmup {args.warmup}", flush=True)
+    print(f"[bench] workload {w.name}: {nm} matrices, {w.n_params:,} params, {args.rotate} state copies, "
+          f"warmup {args.warmup}", flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -258,6 +319,19 @@ def main():
     elapsed = time.perf_counter() - t0
     value = args.steps / elapsed
     print(f"[bench] timed {args.steps} steps in {elapsed * 1e3:.1f} ms", flush=True)
+
+    # Spread of single steps: an event pair around each step on the caller's
+    # stream (the lanes join it before the step's last kernel).
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per_step = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    pct = lambda q: per_step[min(len(per_step) - 1, int(q * len(per_step)))]
+    spread = {"p10": round(1e3 / pct(0.9), 2), "p50": round(1e3 / pct(0.5), 2), "p90": round(1e3 / pct(0.1), 2),
+              "unit": "steps/s", "from": f"{args.steps} single steps timed with HIP events"}
 
     # Per-kernel durations: HIP events around every launch, on the launch stream.
     ms.profile_read(reset=True)
@@ -270,7 +344,7 @@ def main():
     prof_elapsed = time.perf_counter() - tp0
     ms.profile_enable(False)
     prof = ms.profile_read(reset=True)
-    model = kernel_model(w)
+    model = kernel_model(w, fused="ns_update_apply_bf16" in prof)
     kernels = {}
     for name, (count, total_ms) in prof.items():
         step_s = total_ms * 1e-3 / args.steps
@@ -278,9 +352,9 @@ def main():
         entry = {"launches_per_step": lps, "avg_us": total_ms / max(count, 1) * 1e3, "ms_per_step": step_s * 1e3}
         if name in model:
             mm = model[name]
-            scale = lps if mm["per"] == "launch" else 1.0
-            entry["flops_per_step"] = mm["flops"] * scale
-            entry["bytes_per_step"] = mm["bytes"] * scale
+            entry["flops_per_step"] = mm["flops"]
+            entry["bytes_per_step"] = mm["bytes"]
+            entry["bytes_per_launch"] = mm["bytes"] / lps
             if mm["flops"] > 0:
                 entry["tflops"] = entry["flops_per_step"] / step_s / 1e12
             entry["gbs"] = entry["bytes_per_step"] / step_s / 1e9
@@ -298,6 +372,10 @@ def main():
     ns_ms = sum(kernels[k]["ms_per_step"] for k in ns_names)
     ns_flops = sum(kernels[k].get("flops_per_step", 0.0) for k in ns_names)
     ns_tflops = ns_flops / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else None
+    # executed MFMA work (counters: compensation products and symmetry savings included)
+    counted = [mfma_counter_flops(k) for k in ns_names]
+    ns_counted = (sum(c * kernels[k]["launches_per_step"] for c, k in zip(counted, ns_names))
+                  if counted and all(c is not None for c in counted) else None)
     traffic = traffic_for(dom)
 
     out = {
@@ -316,16 +394,24 @@ def main():
         "config": {"workload": f"{w.name}: muon_step over 66 matrices (11 layers x Q/K/V/O/up/down at d=512), "
                                f"5 NS steps bf16, EMA over all {w.n_params:,} fp32 params "
                                f"(matrices inside the step, {len(w.extras)} other tensors in ema_update)",
-                   "matrices": nm, "params": w.n_params, "ns_steps": w.ns_steps, "seed": args.seed},
+                   "matrices": nm, "params": w.n_params, "ns_steps": w.ns_steps, "seed": args.seed,
+                   "state_copies": args.rotate},
         "roofline": {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": round(d["bytes_per_launch"]),
+                     "avg_launch_us": round(d["avg_us"], 3),
                      "mfma_frac": round(d.get("tflops", 0.0) / BF16_PEAK_TFLOPS, 4),
                      "hbm_frac": round(d["gbs"] / HBM_PEAK_GBS, 4)},
-        "ns": {"tflops_algorithmic": round(ns_tflops, 2) if ns_tflops else None,
+        "ns": {"tflops_over_summed_kernel_time": round(ns_tflops, 2) if ns_tflops else None,
                "frac_of_bf16_peak": round(ns_tflops / BF16_PEAK_TFLOPS, 4) if ns_tflops else None,
-               "ms_per_step": round(ns_ms, 4)},
+               "summed_kernel_ms_per_step": round(ns_ms, 4),
+               "tflops_over_step_time": round(ns_flops / elapsed * args.steps / 1e12, 2),
+               "executed_flops_per_step": ns_counted,
+               "executed_tflops_over_summed_kernel_time":
+                   round(ns_counted / (ns_ms * 1e-3) / 1e12, 2) if ns_counted and ns_ms > 0 else None},
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
+        "steps_per_s_spread": spread,
         "ms_per_step_with_events": round(prof_elapsed / args.steps * 1e3, 4),
         "cpu_baseline": None,
     }

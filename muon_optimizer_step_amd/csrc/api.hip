@@ -95,11 +95,15 @@ hipError_t timed_launch(const char* name, hipStream_t s, F launch) {
 }
 
 // ------------------------------------------------------------- NS lanes
-// Shape groups are independent NS problems.  The groups are spread over up to
+// The matrices are independent NS problems.  Their parts (shape groups, split
+// where one would overfill a lane) are spread over up to
 // kLanes streams (the caller's stream and internal non-blocking streams of
 // default priority), forked from and joined back into the caller's stream with
 // events, so that short chains (small matrices) fill the compute units the
 // long ones leave idle.  Nothing waits on the host.
+#ifndef NS_SPLIT_GROUPS
+#define NS_SPLIT_GROUPS 0
+#endif
 #ifndef NS_LANES
 #define NS_LANES 2
 #endif
@@ -334,47 +338,73 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
     const size_t xe = prec == kNsBf16 ? 2 : 4;                           // bytes per X element
     hipError_t err = hipSuccess;
 
-    // ---- lanes: shape groups are independent NS problems.  Groups go to lanes
-    // longest first onto the least loaded lane (by NS flops); each lane runs
-    // prep -> frob -> NS iterations -> apply for its own matrices on its own
-    // stream, so short chains fill the compute units the long ones leave idle.
+    // ---- lanes: the matrices are independent NS problems.  Shape groups go
+    // to lanes longest first onto the least loaded lane (by NS flops); a group
+    // that would overfill its lane is split at a slot boundary into parts on
+    // several lanes.  Each lane runs prep -> frob -> NS iterations -> apply for
+    // its own matrices on its own stream, so short chains fill the compute
+    // units the long ones leave idle.
     const int ngroups = (int)p.groups.size();
-    const int nlanes = std::min(kLanes, ngroups);
-    std::vector<int> lane_of(ngroups, 0);
+    struct Part {
+        int group, s0, s1;  // slots [s0, s1) of the group
+        int lane;
+    };
+    std::vector<Part> parts;
     {
+        std::vector<double> per(ngroups);  // NS flops of one matrix
         std::vector<std::pair<double, int>> work;
+        double total = 0.0;
         for (int g = 0; g < ngroups; ++g) {
             const Group& G = p.groups[g];
-            work.push_back({(double)G.count * (4.0 * G.M * G.M * G.N + 2.0 * G.M * G.M * (double)G.M), g});
+            per[g] = 4.0 * G.M * G.M * (double)G.N + 2.0 * G.M * G.M * (double)G.M;
+            work.push_back({per[g] * G.count, g});
+            total += per[g] * G.count;
         }
         std::sort(work.begin(), work.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
-        std::vector<double> load(nlanes, 0.0);
+        std::vector<double> load(kLanes, 0.0);
+        const double target = total / kLanes;
         for (const auto& wg : work) {
-            const int l = (int)(std::min_element(load.begin(), load.end()) - load.begin());
-            lane_of[wg.second] = l;
-            load[l] += wg.first;
+            const int g = wg.second;
+            const int count = p.groups[g].count;
+            for (int s0 = 0; s0 < count;) {
+                const int l = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+                int take = count - s0;
+                if (NS_SPLIT_GROUPS && load[l] + take * per[g] > 1.05 * target) {
+                    const int fit = (int)((target - load[l]) / per[g]);
+                    if (fit >= 1 && fit < take) take = fit;
+                }
+                parts.push_back({g, s0, s0 + take, l});
+                load[l] += take * per[g];
+                s0 += take;
+            }
         }
     }
-    // NS launch sets: (lane, compensated?, up to kMaxGroups groups)
+    int nlanes = 1;
+    for (const Part& pt : parts) nlanes = std::max(nlanes, pt.lane + 1);
+    // lane of every tensor
+    std::vector<int> tensor_lane(n, 0);
+    for (const Part& pt : parts)
+        for (int sl = pt.s0; sl < pt.s1; ++sl) tensor_lane[p.members[pt.group][sl]] = pt.lane;
+    // NS launch sets: (lane, compensated?, up to kMaxGroups parts)
     struct NsLaunchSet {
         int lane, comp;
-        std::vector<int> groups;
+        std::vector<int> parts;
     };
     std::vector<NsLaunchSet> sets;
     for (int l = 0; l < nlanes; ++l)
         for (int comp = 0; comp < 2; ++comp) {
-            std::vector<int> gl;
-            for (int g = 0; g < ngroups; ++g)
-                if (lane_of[g] == l && (int)p.groups[g].comp == comp) gl.push_back(g);
-            for (size_t g0 = 0; g0 < gl.size(); g0 += kMaxGroups)
-                sets.push_back({l, comp, std::vector<int>(gl.begin() + g0, gl.begin() + std::min(gl.size(), g0 + kMaxGroups))});
+            std::vector<int> pl;
+            for (int q = 0; q < (int)parts.size(); ++q)
+                if (parts[q].lane == l && (int)p.groups[parts[q].group].comp == comp) pl.push_back(q);
+            for (size_t q0 = 0; q0 < pl.size(); q0 += kMaxGroups)
+                sets.push_back({l, comp, std::vector<int>(pl.begin() + q0, pl.begin() + std::min(pl.size(), q0 + kMaxGroups))});
         }
     // The weight update runs inside the last NS update launch when every launch
     // holds at most kMaxFused matrices.
     bool fuse = ns_steps > 0;
     for (const NsLaunchSet& ls : sets) {
         int cnt = 0;
-        for (int g : ls.groups) cnt += p.groups[g].count;
+        for (int q : ls.parts) cnt += parts[q].s1 - parts[q].s0;
         if (cnt > kMaxFused) fuse = false;
     }
     const float keep = 1.0f - lr * weight_decay;
@@ -404,15 +434,16 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
         if (err != hipSuccess) return fail(MUON_ERR_HIP, "lane fork failed: %s", hipGetErrorString(err));
     }
 
-    for (int lane = 0; lane < nlanes; ++lane) {
-        hipStream_t ls_stream = lane_stream[lane];
-        std::vector<int> mine;  // this lane's tensors, in call order
-        for (int i = 0; i < n; ++i)
-            if (lane_of[p.group_of[i]] == lane) mine.push_back(i);
-        const int nm = (int)mine.size();
+    // Each lane's tensors, in call order.
+    std::vector<std::vector<int>> mine(nlanes);
+    for (int i = 0; i < n; ++i) mine[tensor_lane[i]].push_back(i);
 
-        // ---- prep: momentum, row norm, X0 (short side first, zero padded), in
-        // evenly sized launches of at most kPrepChunk tensors
+    // ---- prep: momentum, row norm, X0 (short side first, zero padded), in
+    // evenly sized launches of at most kPrepChunk tensors
+    auto enqueue_prep = [&](int lane) -> int {
+        hipStream_t ls_stream = lane_stream[lane];
+        const std::vector<int>& my = mine[lane];
+        const int nm = (int)my.size();
         const int prep_launches = (nm + kPrepChunk - 1) / kPrepChunk;
         const int prep_take = (nm + prep_launches - 1) / prep_launches;
         for (int c0 = 0; c0 < nm;) {
@@ -424,7 +455,7 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
             int blocks = 0;
             size_t lds = 0;
             for (int k = 0; k < prep_take && c0 < nm; ++k, ++c0) {
-                const int i = mine[c0];
+                const int i = my[c0];
                 const muon_tensor_t& x = tensors[i];
                 const Group& G = p.groups[p.group_of[i]];
                 PrepTensor& T = a.t[a.n++];
@@ -454,15 +485,21 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
             err = timed_launch("prep", ls_stream, [&] { return launch_prep(a, prec, blocks, lds, ls_stream); });
             if (err != hipSuccess) return fail(MUON_ERR_HIP, "prep launch failed: %s", hipGetErrorString(err));
         }
+        return MUON_OK;
+    };
 
-        // ---- Frobenius scales
+    // ---- Frobenius scales
+    auto enqueue_frob = [&](int lane) -> int {
+        hipStream_t ls_stream = lane_stream[lane];
+        const std::vector<int>& my = mine[lane];
+        const int nm = (int)my.size();
         for (int c0 = 0; c0 < nm; c0 += kFrobChunk) {
             FrobArgs a;
             memset(&a, 0, sizeof(a));
             a.rowsq = rowsq;
             a.scale = reinterpret_cast<float*>(ws + p.scale_base);
             for (int c = c0; c < std::min(nm, c0 + kFrobChunk); ++c) {
-                const int i = mine[c];
+                const int i = my[c];
                 const Group& G = p.groups[p.group_of[i]];
                 a.rowsq_off[a.n] = (int)p.rowsq_off[i];
                 a.rows[a.n] = tensors[i].rows;
@@ -472,70 +509,80 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
             err = timed_launch("frob", ls_stream, [&] { return launch_frob(a, ls_stream); });
             if (err != hipSuccess) return fail(MUON_ERR_HIP, "frob launch failed: %s", hipGetErrorString(err));
         }
+        return MUON_OK;
+    };
 
-        // ---- Newton-Schulz iterations: one launch per phase per launch set
-        for (int k = 0; k < ns_steps; ++k) {
-            for (int phase = kGram; phase <= kUpdate; ++phase) {
-                for (const NsLaunchSet& ls : sets) {
-                    if (ls.lane != lane) continue;
-                    NsArgs a;
-                    memset(&a, 0, sizeof(a));
-                    a.src = k & 1;
-                    a.first = (k == 0);
-                    a.a = ns_coeffs[3 * k + 0];
-                    a.b = ns_coeffs[3 * k + 1];
-                    a.c = ns_coeffs[3 * k + 2];
-                    a.fuse_apply = fuse && phase == kUpdate && k == ns_steps - 1;
-                    a.keep = keep;
-                    a.decay = ema_decay;
-                    a.one_minus_decay = 1.0f - ema_decay;
-                    int jobs = 0, napply = 0;
-                    for (int gi : ls.groups) {
-                        const Group& G = p.groups[gi];
-                        NsGroup& D = a.g[a.ngroups++];
-                        for (int b = 0; b < 2; ++b) {
-                            D.x[b] = ws + G.x_off[b];
-                            D.xl[b] = ws + G.xl_off[b];
-                        }
-                        D.a_hi = ws + G.ah_off;
-                        D.a_lo = ws + G.al_off;
-                        D.b = ws + G.b_off;
-                        D.b_lo = ws + G.bl_off;
-                        D.scale = reinterpret_cast<const float*>(ws + p.scale_base) + G.scale_begin;
-                        D.count = G.count;
-                        D.M = G.M;
-                        D.N = G.N;
-                        D.job_begin = jobs;
-                        D.apply_begin = napply;
-                        if (a.fuse_apply) {
-                            for (int ti : p.members[gi]) {
-                                const muon_tensor_t& x = tensors[ti];
-                                FusedApply& F = a.apply[napply++];
-                                F.param = x.param;
-                                F.out = x.update_out;
-                                F.ema = x.ema;
-                                F.rows = x.rows;
-                                F.cols = x.cols;
-                                F.flags = (x.rows > x.cols ? kApplyTransposed : 0) |
-                                          (vec_ok(x) ? kApplyVec : 0);
-                                F.lr_s = lr_scale(x);
-                            }
-                        }
-                        const int tm = G.M / kTile, tn = G.N / kTile;
-                        jobs += G.count * (phase == kUpdate ? tm * tn : tm * (tm + 1) / 2);
-                    }
-                    a.total_jobs = jobs;
-                    const bool comp = ls.comp != 0;
-                    const char* name = ns_kernel_name(phase, prec, comp, a.fuse_apply != 0);
-                    err = timed_launch(name, ls_stream, [&] { return launch_ns(a, phase, prec, comp, ls_stream); });
-                    if (err != hipSuccess) return fail(MUON_ERR_HIP, "%s launch failed: %s", name, hipGetErrorString(err));
+    // ---- one Newton-Schulz phase of iteration k: one launch per launch set
+    auto enqueue_ns = [&](int lane, int k, int phase) -> int {
+        hipStream_t ls_stream = lane_stream[lane];
+        for (const NsLaunchSet& ls : sets) {
+            if (ls.lane != lane) continue;
+            NsArgs a;
+            memset(&a, 0, sizeof(a));
+            a.src = k & 1;
+            a.first = (k == 0);
+            a.a = ns_coeffs[3 * k + 0];
+            a.b = ns_coeffs[3 * k + 1];
+            a.c = ns_coeffs[3 * k + 2];
+            a.fuse_apply = fuse && phase == kUpdate && k == ns_steps - 1;
+            a.keep = keep;
+            a.decay = ema_decay;
+            a.one_minus_decay = 1.0f - ema_decay;
+            int jobs = 0, napply = 0;
+            for (int q : ls.parts) {
+                const Part& pt = parts[q];
+                const Group& G = p.groups[pt.group];
+                const int count = pt.s1 - pt.s0;
+                const size_t xslot = (size_t)G.M * G.N * xe, aslot = (size_t)G.M * G.M * xe;
+                NsGroup& D = a.g[a.ngroups++];
+                for (int b = 0; b < 2; ++b) {
+                    D.x[b] = ws + G.x_off[b] + pt.s0 * xslot;
+                    D.xl[b] = ws + G.xl_off[b] + pt.s0 * xslot;
                 }
+                D.a_hi = ws + G.ah_off + pt.s0 * aslot;
+                D.a_lo = ws + G.al_off + pt.s0 * aslot;
+                D.b = ws + G.b_off + pt.s0 * aslot;
+                D.b_lo = ws + G.bl_off + pt.s0 * aslot;
+                D.scale = reinterpret_cast<const float*>(ws + p.scale_base) + G.scale_begin + pt.s0;
+                D.count = count;
+                D.M = G.M;
+                D.N = G.N;
+                D.job_begin = jobs;
+                D.apply_begin = napply;
+                if (a.fuse_apply) {
+                    for (int sl = pt.s0; sl < pt.s1; ++sl) {
+                        const int ti = p.members[pt.group][sl];
+                        const muon_tensor_t& x = tensors[ti];
+                        FusedApply& F = a.apply[napply++];
+                        F.param = x.param;
+                        F.out = x.update_out;
+                        F.ema = x.ema;
+                        F.rows = x.rows;
+                        F.cols = x.cols;
+                        F.flags = (x.rows > x.cols ? kApplyTransposed : 0) | (vec_ok(x) ? kApplyVec : 0);
+                        F.lr_s = lr_scale(x);
+                    }
+                }
+                const int tm = G.M / kTile, tn = G.N / kTile;
+                jobs += count * (phase == kUpdate ? tm * tn : tm * (tm + 1) / 2);
             }
+            a.total_jobs = jobs;
+            const bool comp = ls.comp != 0;
+            const char* name = ns_kernel_name(phase, prec, comp, a.fuse_apply != 0);
+            err = timed_launch(name, ls_stream, [&] { return launch_ns(a, phase, prec, comp, ls_stream); });
+            if (err != hipSuccess) return fail(MUON_ERR_HIP, "%s launch failed: %s", name, hipGetErrorString(err));
         }
+        return MUON_OK;
+    };
 
-        // ---- apply: W' = (1 - lr wd) W - lr s O (unless the last NS update did it)
+    // ---- apply: W' = (1 - lr wd) W - lr s O and the EMA (unless the last NS
+    // update did it)
+    auto enqueue_apply = [&](int lane) -> int {
+        hipStream_t ls_stream = lane_stream[lane];
+        const std::vector<int>& my = mine[lane];
+        const int nm = (int)my.size();
         const int final_buf = ns_steps & 1;
-        for (int c0 = 0; c0 < nm && !fuse; c0 += kApplyChunk) {
+        for (int c0 = 0; c0 < nm; c0 += kApplyChunk) {
             ApplyArgs a;
             memset(&a, 0, sizeof(a));
             a.keep = keep;
@@ -545,7 +592,7 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
             int blocks = 0;
             size_t lds = 0;
             for (int c = c0; c < std::min(nm, c0 + kApplyChunk); ++c) {
-                const int i = mine[c];
+                const int i = my[c];
                 const muon_tensor_t& x = tensors[i];
                 const Group& G = p.groups[p.group_of[i]];
                 ApplyTensor& T = a.t[a.n++];
@@ -575,7 +622,22 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
             err = timed_launch("apply", ls_stream, [&] { return launch_apply(a, prec, blocks, lds, ls_stream); });
             if (err != hipSuccess) return fail(MUON_ERR_HIP, "apply launch failed: %s", hipGetErrorString(err));
         }
-    }
+        return MUON_OK;
+    };
+
+    // Enqueue stage by stage across the lanes, so every lane has work queued
+    // early even when the host is only just ahead of the GPU.
+    for (int lane = 0; lane < nlanes; ++lane)
+        if ((rc = enqueue_prep(lane))) return rc;
+    for (int lane = 0; lane < nlanes; ++lane)
+        if ((rc = enqueue_frob(lane))) return rc;
+    for (int k = 0; k < ns_steps; ++k)
+        for (int phase = kGram; phase <= kUpdate; ++phase)
+            for (int lane = 0; lane < nlanes; ++lane)
+                if ((rc = enqueue_ns(lane, k, phase))) return rc;
+    if (!fuse)
+        for (int lane = 0; lane < nlanes; ++lane)
+            if ((rc = enqueue_apply(lane))) return rc;
 
     if (L) {
         for (int l = 1; l < nlanes && err == hipSuccess; ++l) {

@@ -21,10 +21,12 @@
 // groups, or every group on request, run compensated (~1e-4).  The fp32
 // precision runs the same phases on fp32 MFMA (v_mfma_f32_32x32x2_f32).
 //
-// Tiling.  One workgroup (4 wave64s, 2 x 2) per 128 x 128 output tile, 64 x 64
-// per wave as 2 x 2 v_mfma_f32_32x32x16_bf16 accumulators.  K is staged
-// through LDS 128 bytes per row at a time (64 bf16 or 32 fp32) with the next
-// stage's global loads in flight during the MFMAs.  A and B are symmetric:
+// Tiling.  One workgroup per 128 x 128 output tile, 64 x 64 per wave as 2 x 2
+// v_mfma_f32_32x32x16_bf16 accumulators: 4 wave64s (2 x 2) for the update, and
+// two such groups splitting the K stages for the Gram and square, whose few
+// (upper-triangle) tiles would otherwise leave one wave per SIMD.  K is staged
+// through LDS 128 or 256 bytes per row at a time with the next stage's global
+// loads in flight during the MFMAs.  A and B are symmetric:
 // only tiles with ti <= tj are computed and each is written twice (as is and
 // mirrored).  Epilogues go through LDS so that every global access is 16
 // bytes wide.  All work of one phase for every matrix of every shape group is
@@ -55,6 +57,9 @@
 #ifndef NS_TRANSPOSE_READ
 #define NS_TRANSPOSE_READ 1  // bf16 update reads X through ds_read_b64_tr_b16
 #endif
+#ifndef NS_SYM_KGROUPS
+#define NS_SYM_KGROUPS 1     // Gram and square run with two K groups per workgroup
+#endif
 
 namespace muon {
 
@@ -77,6 +82,7 @@ static_assert(kStageBytes <= 2 * Stage<128>::kSlot, "epilogue staging must fit i
 // K bytes per LDS stage: 256 for the bf16 base Gram, whose long contraction
 // gains from fewer, larger stages (two 128-row slots still fit 2 workgroups per
 // CU), 128 otherwise.
+
 constexpr int ns_stage_bytes(int phase, int precision, bool comp) {
     return (precision == kNsBf16 && !comp && NS_WIDE_STAGE != 0 &&
             (phase == kGram || (phase == kUpdate && NS_WIDE_UPDATE != 0 && NS_TRANSPOSE_READ != 0))) ? 256 : 128;
@@ -112,7 +118,7 @@ struct NtLoader {
     static constexpr int C = RB / 16, Q = RB / 32;
     u32x4 r[Q];
     __device__ inline void load(const uint8_t* base, size_t ld_bytes, int kbyte) {
-        const int t = threadIdx.x;
+        const int t = threadIdx.x % 256;
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             const uint8_t* p = base + (size_t)(t / C + (256 / C) * q) * ld_bytes + kbyte + (t % C) * 16;
@@ -120,7 +126,7 @@ struct NtLoader {
         }
     }
     __device__ inline void store(uint8_t* lds) const {
-        const int t = threadIdx.x;
+        const int t = threadIdx.x % 256;
 #pragma unroll
         for (int q = 0; q < Q; ++q)
             *reinterpret_cast<u32x4*>(lds + (t / C + (256 / C) * q) * Stage<RB>::kPitch + (t % C) * 16) = r[q];
@@ -734,6 +740,241 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
     }
 }
 
+// Gram and square with two K groups per workgroup.  These phases have few
+// output tiles (the upper triangle of m x m), so a launch leaves one wave per
+// SIMD and its LDS and MFMA latencies exposed.  Here 8 waves share a tile:
+// waves 0-3 take the even K stages and waves 4-7 the odd ones, each group
+// with its own LDS stage, so every SIMD holds two waves that interleave.  The
+// two partial accumulators meet in a full-tile fp32 LDS staging buffer
+// (group 0 writes, group 1 adds) before the 512-thread epilogue.
+constexpr int kSymThreads = 2 * kThreads;
+constexpr int kSymStageBytes = kTile * kStagePitch * 4;   // a full tile of fp32
+
+template <int PHASE, int PREC, bool COMP>
+__global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) {
+    static_assert(PHASE == kGram || PHASE == kSquare, "symmetric phases only");
+    typedef typename Elem<PREC>::T T;
+    constexpr bool kSplit = (PREC == kNsBf16) && (PHASE == kSquare || COMP);
+    constexpr int kRB = ns_stage_bytes(PHASE, PREC, COMP);
+    constexpr int kBK = kRB / (int)sizeof(T);
+    constexpr int kSlot = Stage<kRB>::kSlot;
+    constexpr int kStageTiles = kSplit ? 4 : 2;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    Job job;
+    if (!decode_job<PHASE>(args, job)) return;   // uniform over the workgroup
+    const NsGroup& G = args.g[job.g];
+    const int M = G.M, N = G.N;
+    const int tid = threadIdx.x;
+    const int kg = tid / kThreads;                 // K group
+    const int lane = tid % kWave, wave = (tid % kThreads) / kWave;
+    const int wm = wave >> 1, wn = wave & 1;
+    const bool diag = job.ti == job.tj;
+    const size_t xplane = (size_t)job.slot * M * N;
+    const size_t aplane = (size_t)job.slot * M * M;
+
+    auto tile = [&](int which) -> uint8_t* {
+        if (diag && which == 1) which = 0;
+        if (diag && which == 3) which = 2;
+        return lds + (kg * kStageTiles + which) * kSlot;
+    };
+    const uint8_t *ga, *gb, *gal, *gbl;
+    size_t ld_bytes;
+    int K;
+    if (PHASE == kGram) {
+        const T* xh = static_cast<const T*>(G.x[args.src]) + xplane;
+        const T* xl = static_cast<const T*>(G.xl[args.src]) + xplane;
+        ld_bytes = (size_t)N * sizeof(T);
+        ga = reinterpret_cast<const uint8_t*>(xh + (size_t)job.ti * kTile * N);
+        gb = reinterpret_cast<const uint8_t*>(xh + (size_t)job.tj * kTile * N);
+        gal = reinterpret_cast<const uint8_t*>(xl + (size_t)job.ti * kTile * N);
+        gbl = reinterpret_cast<const uint8_t*>(xl + (size_t)job.tj * kTile * N);
+        K = N;
+    } else {
+        const T* ah = static_cast<const T*>(G.a_hi) + aplane;
+        const T* al = static_cast<const T*>(G.a_lo) + aplane;
+        ld_bytes = (size_t)M * sizeof(T);
+        ga = reinterpret_cast<const uint8_t*>(ah + (size_t)job.ti * kTile * M);
+        gb = reinterpret_cast<const uint8_t*>(ah + (size_t)job.tj * kTile * M);
+        gal = reinterpret_cast<const uint8_t*>(al + (size_t)job.ti * kTile * M);
+        gbl = reinterpret_cast<const uint8_t*>(al + (size_t)job.tj * kTile * M);
+        K = M;
+    }
+
+    floatx16 acc[2][2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+    NtLoader<kRB> la, lb, lal, lbl;
+    auto issue = [&](int kt) {
+        const int kbyte = kt * kRB;
+        la.load(ga, ld_bytes, kbyte);
+        if (kSplit) lal.load(gal, ld_bytes, kbyte);
+        if (!diag) {
+            lb.load(gb, ld_bytes, kbyte);
+            if (kSplit) lbl.load(gbl, ld_bytes, kbyte);
+        }
+    };
+    auto commit = [&]() {
+        la.store(tile(0));
+        if (kSplit) lal.store(tile(2));
+        if (!diag) {
+            lb.store(tile(1));
+            if (kSplit) lbl.store(tile(3));
+        }
+    };
+    auto compute = [&]() {
+        const uint8_t* t_a = tile(0);
+        const uint8_t* t_b = tile(1);
+        const uint8_t* t_al = tile(2);
+        const uint8_t* t_bl = tile(3);
+#pragma unroll
+        for (int kc = 0; kc < kRB / 32; ++kc) {
+            u32x4 fa[2], fb[2];
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) fa[mi] = lds_frag<kRB>(t_a, wm * 64 + mi * 32 + lane % 32, kc, lane);
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni) fb[ni] = lds_frag<kRB>(t_b, wn * 64 + ni * 32 + lane % 32, kc, lane);
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni) mfma_chunk<PREC>(acc[mi][ni], fa[mi], fb[ni]);
+            if (kSplit) {
+                u32x4 fal[2], fbl[2];
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi) fal[mi] = lds_frag<kRB>(t_al, wm * 64 + mi * 32 + lane % 32, kc, lane);
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni) fbl[ni] = lds_frag<kRB>(t_bl, wn * 64 + ni * 32 + lane % 32, kc, lane);
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < 2; ++ni) {
+                        mfma_chunk<PREC>(acc[mi][ni], fa[mi], fbl[ni]);
+                        mfma_chunk<PREC>(acc[mi][ni], fal[mi], fb[ni]);
+                    }
+            }
+        }
+    };
+
+    // Group g takes the K stages kt = 2j + g.  The groups run half a step
+    // apart: in half-step h, group 0 stores stage h (h even) into its LDS slot
+    // or computes stage h - 1 (h odd), and group 1 stores stage h (h odd) or
+    // computes stage h - 1 (h even), so one group's LDS stores and load waits
+    // overlap the other group's MFMAs.  A barrier ends every half-step; a
+    // group's store and the reads of that slot are always a half-step apart.
+    const int nk = K / kBK;
+    if (kg < nk) issue(kg);
+    __syncthreads();
+    for (int h = 0; h <= nk; ++h) {
+        if ((h & 1) == kg) {
+            if (h < nk) {                       // stage h: registers -> LDS, next loads
+                commit();
+                if (h + 2 < nk) issue(h + 2);
+            }
+        } else if (h > 0 && h - 1 < nk) {       // stage h - 1 of this group
+            compute();
+        }
+        __syncthreads();
+    }
+
+    // ------------------------------------------------------- epilogue
+    // thread tid -> rows tid/16 + 32p (p < 4) of the tile, columns 8*(tid%16) .. +7
+    const int lc = 8 * (tid % 16);
+    constexpr bool kPreA = (PHASE == kSquare) && (PREC == kNsBf16) && (NS_PREFETCH_XL != 0);
+    u32x4 a_pre[4][2];
+    if constexpr (kPreA) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const size_t idx = aplane + (size_t)(job.ti * kTile + tid / 16 + 32 * p) * M + job.tj * kTile + lc;
+            a_pre[p][0] = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(G.a_hi) + idx);
+            a_pre[p][1] = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(G.a_lo) + idx);
+        }
+    }
+    float* stage = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        __syncthreads();
+        if (kg == pass) {
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = wm * 64 + mi * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+                        const int col = wn * 64 + ni * 32 + (lane % 32);
+                        float& dst = stage[row * kStagePitch + col];
+                        dst = pass == 0 ? acc[mi][ni][r] : dst + acc[mi][ni][r];
+                    }
+        }
+    }
+    __syncthreads();
+    const float s = G.scale[job.slot];
+    const float sc = args.first ? s * s : 1.0f;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int lr = tid / 16 + 32 * p;
+        float* sp = stage + lr * kStagePitch + lc;
+        float v[8];
+        {
+            const floatx4 a = *reinterpret_cast<const floatx4*>(sp);
+            const floatx4 b = *reinterpret_cast<const floatx4*>(sp + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
+        }
+        const size_t idx = (size_t)(job.ti * kTile + lr) * M + job.tj * kTile + lc;
+        if (PHASE == kGram) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] *= sc;
+            store8<PREC>(static_cast<T*>(G.a_hi) + aplane, static_cast<T*>(G.a_lo) + aplane, idx, v);
+        } else {
+            float ah[8], al[8];
+            if constexpr (kPreA) {
+                unpack8(a_pre[p][0], ah);
+                unpack8(a_pre[p][1], al);
+            } else {
+                load8<PREC>(static_cast<const T*>(G.a_hi) + aplane, idx, ah);
+                if constexpr (PREC == kNsBf16) load8<PREC>(static_cast<const T*>(G.a_lo) + aplane, idx, al);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float a = (PREC == kNsBf16) ? ah[e] + al[e] : ah[e];
+                v[e] = fmaf(args.b, a, args.c * v[e]);
+            }
+            store8<PREC>(static_cast<T*>(G.b) + aplane, COMP ? static_cast<T*>(G.b_lo) + aplane : nullptr, idx, v);
+        }
+        if (!diag) {
+            floatx4 a, b;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { a[e] = v[e]; b[e] = v[4 + e]; }
+            *reinterpret_cast<floatx4*>(sp) = a;
+            *reinterpret_cast<floatx4*>(sp + 4) = b;
+        }
+    }
+    if (!diag) {
+        __syncthreads();
+        // mirrored tile: output row tj*128 + c, columns ti*128 + 8*chunk .. +7
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int chunk = tid % 16;
+            const int c = tid / 16 + 32 * p;
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = stage[(chunk * 8 + e) * kStagePitch + c];
+            const size_t idx = (size_t)(job.tj * kTile + c) * M + job.ti * kTile + chunk * 8;
+            if (PHASE == kGram)
+                store8<PREC>(static_cast<T*>(G.a_hi) + aplane, static_cast<T*>(G.a_lo) + aplane, idx, v);
+            else
+                store8<PREC>(static_cast<T*>(G.b) + aplane, COMP ? static_cast<T*>(G.b_lo) + aplane : nullptr,
+                             idx, v);
+        }
+    }
+}
+
 size_t ns_lds_bytes(int phase, int precision, bool comp) {
     const bool split = precision == kNsBf16 && (phase == kSquare || comp);
     const int stages = (split || NS_DOUBLE_BUFFER == 0) ? 1 : 2;
@@ -755,8 +996,31 @@ hipError_t launch_one(const NsArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+size_t ns_sym_lds_bytes(int phase, int precision, bool comp) {
+    const bool split = precision == kNsBf16 && (phase == kSquare || comp);
+    const int slot = ns_stage_bytes(phase, precision, comp) == 256 ? Stage<256>::kSlot : Stage<128>::kSlot;
+    return std::max((size_t)2 * (split ? 4 : 2) * slot, (size_t)kSymStageBytes);
+}
+
+template <int PHASE, int PREC, bool COMP>
+hipError_t launch_sym(const NsArgs& a, hipStream_t s) {
+    const size_t lds = ns_sym_lds_bytes(PHASE, PREC, COMP);
+    if (lds > 65536) {
+        static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&ns_sym_kernel<PHASE, PREC, COMP>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (attr != hipSuccess) return attr;
+    }
+    const int grid = (a.total_jobs + kXcds - 1) / kXcds * kXcds;
+    ns_sym_kernel<PHASE, PREC, COMP><<<grid, kSymThreads, lds, s>>>(a);
+    return hipGetLastError();
+}
+
 template <int PHASE>
 hipError_t launch_phase(const NsArgs& a, int precision, bool comp, hipStream_t s) {
+    if (NS_SYM_KGROUPS) {
+        if (precision == kNsFp32) return launch_sym<PHASE, kNsFp32, false>(a, s);
+        return comp ? launch_sym<PHASE, kNsBf16, true>(a, s) : launch_sym<PHASE, kNsBf16, false>(a, s);
+    }
     if (precision == kNsFp32) return launch_one<PHASE, kNsFp32, false, false>(a, s);
     return comp ? launch_one<PHASE, kNsBf16, true, false>(a, s) : launch_one<PHASE, kNsBf16, false, false>(a, s);
 }

@@ -63,7 +63,7 @@ def test_deterministic_and_workspace_contents_do_not_matter():
         O = [torch.empty_like(p) for p in P]
         E = [gu.dev(e) for e in wl.make_independent_ema(w, 12)]
         ms.muon_step(P, [gu.dev(g) for g in grads], M, lr=w.lr, momentum=w.momentum, weight_decay=w.weight_decay,
-                     coeffs=STD, update_outs=O, emas=E, ema_decay=w.ema_decay, workspace=ws)
+                     coeffs=STD, update_outs=O, emas=E, ema_decay=0.9965, workspace=ws)
         torch.cuda.synchronize()
         outs.append([gu.host(t) for t in P + M + O + E])
     for other in outs[1:]:

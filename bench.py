@@ -41,6 +41,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=1337)
     ap.add_argument("--rotate", type=int, default=2, help="independent state copies used in turn (MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true", help="skip the steps/s of the other workloads")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (counter calibration) and exit")
@@ -255,6 +256,55 @@ def cpu_baseline(w, seed, target_s):
             "blas": blas, "single_thread": {"value": 1.0 / el1, "unit": "steps/s", "sample": f"1 step, {el1:.1f} s"}}
 
 
+def time_other_config(cfg, steps, warmup, seed):
+    """Steps/s of one more workload (the parity configs), same method as the main line, no profiling."""
+    import torch
+    import muon_optimizer_step_amd as ms
+    import workloads as wl
+    w = wl.workload(cfg)
+    dev = torch.device("cuda:0")
+    nm = len(w.matrices)
+    st = wl.make_state(w, seed)
+    coeffs = wl.coeff_table(w, seed).tolist()
+    P = [torch.from_numpy(p).to(dev) for p in st["params"]]
+    M = [torch.from_numpy(m).to(dev) for m in st["moms"]]
+    E = [torch.from_numpy(e).to(dev) for e in st["ema"]] if w.ema_decay is not None else None
+    # the multi-step workload draws a fresh gradient every step: two sets used in turn
+    gsets = [[torch.from_numpy(g).to(dev) for g in wl.make_grads(w, seed, k)] for k in range(2 if w.steps > 1 else 1)]
+    del st
+    runs, workspace = [], None
+    for G in gsets:
+        muon = ms.PreparedMuonStep(P[:nm], G, M, ns_precision=w.ns_precision, emas=E[:nm] if E else None,
+                                   workspace=workspace)
+        workspace = muon.workspace
+        runs.append(muon)
+    ema = ms.PreparedEma(E[nm:], P[nm:]) if E and len(E) > nm else None
+    stream = torch.cuda.current_stream(dev)
+    decay = w.ema_decay if w.ema_decay is not None else 0.0
+
+    def step(i):
+        runs[i % len(runs)](lr=w.lr, momentum=w.momentum, weight_decay=w.weight_decay, coeffs=coeffs,
+                            nesterov=w.nesterov, row_norm=w.row_norm, ema_decay=decay, stream=stream)
+        if ema is not None:
+            ema(decay, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) / steps
+    ns_flops = w.ns_steps * sum(4.0 * min(r, c) ** 2 * max(r, c) + 2.0 * min(r, c) ** 3 for _, r, c in w.matrices)
+    out = {"workload": w.name, "steps_per_s": round(1.0 / el, 2), "ms_per_step": round(el * 1e3, 4),
+           "ns_precision": ["bf16", "fp32"][w.ns_precision], "matrices": nm, "params": w.n_params,
+           "ns_algorithmic_tflops_over_step_time": round(ns_flops / el / 1e12, 2)}
+    del P, M, E, gsets, runs, ema, workspace
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -415,6 +465,16 @@ def main():
         "ms_per_step_with_events": round(prof_elapsed / args.steps * 1e3, 4),
         "cpu_baseline": None,
     }
+    if not args.no_other_configs:
+        # the other workloads (parity cases), each on its own; steps/s only
+        del states, workspace
+        torch.cuda.empty_cache()
+        others = {}
+        for cfg in (0, 1, 3, 4):
+            print(f"[bench] workload {cfg}", flush=True)
+            r = time_other_config(cfg, steps=max(20, args.steps // 4), warmup=5, seed=args.seed)
+            others[r.pop("workload")] = r
+        out["other_workloads"] = others
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", flush=True)
         out["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_seconds)

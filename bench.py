@@ -339,23 +339,42 @@ def main():
     for r in range(args.rotate):
         st = wl.make_state(w, args.seed + r)
         grads = wl.make_grads(w, args.seed + r, 0)
+        ad = wl.make_adamw_state(w, args.seed + r)
         P = [torch.from_numpy(p).to(dev) for p in st["params"]]
         G = [torch.from_numpy(g).to(dev) for g in grads]
         M = [torch.from_numpy(m).to(dev) for m in st["moms"]]
         E = [torch.from_numpy(e).to(dev) for e in st["ema"]]
-        del st, grads
+        AG, AM, AV = ([torch.from_numpy(x).to(dev) for x in ad[k]] for k in ("grads", "exp_avg", "exp_avg_sq"))
+        del st, grads, ad
         muon = ms.PreparedMuonStep(P[:nm], G, M, emas=E[:nm], workspace=workspace)
         workspace = muon.workspace
-        states.append((muon, ms.PreparedEma(E[nm:], P[nm:])))
+        states.append((muon, ms.PreparedEma(E[nm:], P[nm:]), ms.PreparedAdamW(P[nm:], AG, AM, AV, emas=E[nm:])))
     stream = torch.cuda.current_stream(dev)
     turn = [0]
 
     def step():
-        step_muon, step_ema = states[turn[0] % len(states)]
+        step_muon, step_ema, _ = states[turn[0] % len(states)]
         turn[0] += 1
         step_muon(lr=w.lr, momentum=w.momentum, weight_decay=w.weight_decay, coeffs=coeffs,
                   ema_decay=w.ema_decay, stream=stream)
         step_ema(w.ema_decay, stream=stream)
+
+    hp = wl.ADAMW_HPARAMS
+
+    def adamw_only():
+        _, _, step_adamw = states[turn[0] % len(states)]
+        turn[0] += 1
+        step_adamw(lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"], weight_decay=hp["weight_decay"],
+                   step=hp["step"], ema_decay=w.ema_decay, stream=stream)
+
+    def full_step():
+        # the whole optimizer step: Muon on the matrices, AdamW on the rest, EMA on everything
+        step_muon, _, step_adamw = states[turn[0] % len(states)]
+        turn[0] += 1
+        step_muon(lr=w.lr, momentum=w.momentum, weight_decay=w.weight_decay, coeffs=coeffs,
+                  ema_decay=w.ema_decay, stream=stream)
+        step_adamw(lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"], weight_decay=hp["weight_decay"],
+                   step=hp["step"], ema_decay=w.ema_decay, stream=stream)
 
     print(f"[bench] workload {w.name}: {nm} matrices, {w.n_params:,} params, {args.rotate} state copies, "
           f"warmup {args.warmup}", flush=True)
@@ -465,6 +484,40 @@ def main():
         "ms_per_step_with_events": round(prof_elapsed / args.steps * 1e3, 4),
         "cpu_baseline": None,
     }
+    # AdamW on the 121 non-matrix tensors (with their EMA fused), alone and
+    # inside the whole optimizer step
+    for _ in range(5):
+        adamw_only()
+    torch.cuda.synchronize()
+    ms.profile_read(reset=True)
+    ms.profile_enable(True)
+    for _ in range(args.steps):
+        adamw_only()
+    torch.cuda.synchronize()
+    ms.profile_enable(False)
+    aprof = ms.profile_read(reset=True)["adamw"]
+    extra_elems = w.n_params - sum(r * c for _, r, c in w.matrices)
+    a_bytes = 36.0 * extra_elems   # read p, g, m, v, e; write p, m, v, e
+    a_us = aprof[1] / aprof[0] * 1e3
+    for _ in range(5):
+        full_step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        full_step()
+    torch.cuda.synchronize()
+    full_el = (time.perf_counter() - t0) / args.steps
+    out["adamw"] = {"tensors": len(w.extras), "elements": extra_elems, "hyperparameters": hp,
+                    "launches_per_call": aprof[0] / args.steps, "avg_launch_us": round(a_us, 3),
+                    "us_per_call": round(aprof[1] / args.steps * 1e3, 3),
+                    "algorithmic_bytes_per_call": a_bytes,
+                    "gbs": round(a_bytes / (aprof[1] / args.steps * 1e-3) / 1e9, 1),
+                    "frac_of_hbm_peak": round(a_bytes / (aprof[1] / args.steps * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    out["full_optimizer_step"] = {"steps_per_s": round(1.0 / full_el, 2), "ms_per_step": round(full_el * 1e3, 4),
+                                  "what": "muon_step on the 66 matrices (EMA fused) + adamw_step on the 121 other "
+                                          "tensors (EMA fused)"}
+    print(f"[bench] adamw {out['adamw']['us_per_call']} us per call; full optimizer step "
+          f"{out['full_optimizer_step']['steps_per_s']} steps/s", flush=True)
     if not args.no_other_configs:
         # the other workloads (parity cases), each on its own; steps/s only
         del states, workspace

@@ -20,7 +20,8 @@
  *   for k < ns_steps, (a,b,c) = coeffs[k]:  A = X X^T;  X <- a X + (b A + c A A) X
  *   O = X (transposed back);  s = sqrt(max(1, rows/cols))
  *   W' = (1 - lr*wd) W - lr*s*O
- * and the EMA  E' = d*E + (1 - d)*P  over any list of fp32 tensors.
+ * and the EMA  E' = d*E + (1 - d)*P  over any list of fp32 tensors; AdamW for
+ * the parameters that are not Muon matrices (adamw_step below).
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers to contiguous fp32 data on the
@@ -122,6 +123,40 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
  *   1 <= n <= MUON_MAX_TENSORS. */
 int ema_update(float* const* ema, const float* const* params, const int64_t* numel, int32_t n,
                float decay, void* stream);
+
+/* One fp32 tensor of the AdamW update (any shape, numel elements, contiguous).
+ * param, exp_avg and exp_avg_sq are updated in place; grad is read only.  ema is
+ * optional (NULL to skip): when set, the tensor's weight EMA is advanced on the
+ * updated parameter in the same pass (ema = d*ema + (1-d)*param').  None of the
+ * buffers of any tensor of a call may overlap. */
+typedef struct adamw_tensor_t {
+    float* param;
+    const float* grad;
+    float* exp_avg;
+    float* exp_avg_sq;
+    float* ema;
+    int64_t numel;
+} adamw_tensor_t;
+
+/* AdamW over n fp32 tensors: the optimizer of the embeddings and scalar
+ * parameters ("Record: L_ParallelResiduals_UNetSkips_DepthRecur_Muon_ 1.0901"
+ * (PR #1893), "Architecture and training stack", Optimizer row, which names
+ * AdamW and gives no equations).  Per element, with t = step:
+ *   p <- (1 - lr*wd) p
+ *   m <- beta1 m + (1 - beta1) g;   v <- beta2 v + (1 - beta2) g^2
+ *   p <- p - lr * (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
+ * then, where ema is set, ema <- ema_decay*ema + (1 - ema_decay)*p.
+ *   tensors     host array of n descriptors, 1 <= n <= MUON_MAX_TENSORS; tensors
+ *               with numel == 0 are skipped (their pointers may be NULL).
+ *   lr, weight_decay  finite.   beta1, beta2  in [0, 1).   eps  finite, >= 0
+ *               (eps == 0 with a zero second moment gives NaN, as the formula does).
+ *   step        >= 1, the count of AdamW steps including this one.
+ *   ema_decay   finite, in [0, 1] (checked on every call).
+ * Pointers are device pointers, 4-byte aligned (16-byte alignment takes the
+ * vector path).  Validated on the host before anything is enqueued; enqueued
+ * on stream, never synchronises, allocates nothing. */
+int adamw_step(const adamw_tensor_t* tensors, int32_t n, float lr, float beta1, float beta2, float eps,
+               float weight_decay, int32_t step, float ema_decay, void* stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* muon_last_error(void);

@@ -1,4 +1,4 @@
-"""MI355X (gfx950) Muon optimizer step and weight EMA.
+"""MI355X (gfx950) Muon optimizer step, weight EMA and AdamW for the other parameters.
 
 Thin Python binding over the C ABI of libmuonstep.so (include/muonstep.h):
 it only turns torch tensors into device pointers plus the current HIP stream.
@@ -9,6 +9,6 @@ from ._lib import (  # noqa: F401
     MUON_NS_BF16, MUON_NS_FP32, MUON_NS_BF16X3, MuonError, LIB_PATH, load,
 )
 from .api import (  # noqa: F401
-    muon_step, ema_update, workspace_size, profile_enable, profile_read, version,
-    PreparedMuonStep, PreparedEma,
+    muon_step, ema_update, adamw_step, workspace_size, profile_enable, profile_read, version,
+    PreparedMuonStep, PreparedEma, PreparedAdamW,
 )

@@ -33,6 +33,17 @@ class MuonTensor(ctypes.Structure):
     ]
 
 
+class AdamWTensor(ctypes.Structure):
+    _fields_ = [
+        ("param", ctypes.c_void_p),
+        ("grad", ctypes.c_void_p),
+        ("exp_avg", ctypes.c_void_p),
+        ("exp_avg_sq", ctypes.c_void_p),
+        ("ema", ctypes.c_void_p),
+        ("numel", ctypes.c_int64),
+    ]
+
+
 class MuonError(RuntimeError):
     def __init__(self, code: int, message: str):
         super().__init__(f"muonstep error {code}: {message}")
@@ -64,6 +75,10 @@ def load() -> ctypes.CDLL:
     f.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_int64),
                   ctypes.c_int32, ctypes.c_float, ctypes.c_void_p]
     f.restype = ctypes.c_int
+    f = lib.adamw_step
+    f.argtypes = [ctypes.POINTER(AdamWTensor), ctypes.c_int32, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                  ctypes.c_float, ctypes.c_float, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p]
+    f.restype = ctypes.c_int
     lib.muon_last_error.argtypes = []
     lib.muon_last_error.restype = ctypes.c_char_p
     lib.muon_version.argtypes = []
@@ -88,6 +103,15 @@ def tensor_table(entries) -> "ctypes.Array[MuonTensor]":
     arr = (MuonTensor * max(1, len(entries)))()
     for i, (p, g, m, o, e, r, c) in enumerate(entries):
         arr[i] = MuonTensor(p, g, m, o, e, r, c)
+    return arr
+
+
+def adamw_table(entries) -> "ctypes.Array[AdamWTensor]":
+    """entries: iterable of (param, grad, exp_avg, exp_avg_sq, ema, numel) with int pointers."""
+    entries = list(entries)
+    arr = (AdamWTensor * max(1, len(entries)))()
+    for i, e in enumerate(entries):
+        arr[i] = AdamWTensor(*e)
     return arr
 
 

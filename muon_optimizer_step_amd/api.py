@@ -133,6 +133,62 @@ def ema_update(emas, params, decay: float, stream=None) -> None:
     _lib.check(rc)
 
 
+def _adamw_entries(params, grads, exp_avgs, exp_avg_sqs, emas):
+    n = len(params)
+    if len(grads) != n or len(exp_avgs) != n or len(exp_avg_sqs) != n:
+        raise ValueError("params, grads, exp_avgs and exp_avg_sqs must have the same length")
+    emas = emas if emas is not None else [None] * n
+    if len(emas) != n:
+        raise ValueError("emas must have one entry per parameter")
+    entries = []
+    for i, (p, g, m, v, e) in enumerate(zip(params, grads, exp_avgs, exp_avg_sqs, emas)):
+        for t, nm in ((p, "params"), (g, "grads"), (m, "exp_avgs"), (v, "exp_avg_sqs")):
+            _check_tensor(t, f"{nm}[{i}]")
+            if t.numel() != p.numel():
+                raise ValueError(f"{nm}[{i}] has {t.numel()} elements, params[{i}] {p.numel()}")
+        if e is not None:
+            _check_tensor(e, f"emas[{i}]")
+            if e.numel() != p.numel():
+                raise ValueError(f"emas[{i}] has {e.numel()} elements, params[{i}] {p.numel()}")
+        entries.append((p.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr(),
+                        e.data_ptr() if e is not None else 0, p.numel()))
+    return entries
+
+
+def adamw_step(params, grads, exp_avgs, exp_avg_sqs, *, lr: float, betas=(0.9, 0.999), eps: float = 1e-8,
+               weight_decay: float = 0.01, step: int, emas=None, ema_decay: float = 0.0, stream=None) -> None:
+    """AdamW over lists of fp32 tensors of any shape (params and both moments updated in place).
+
+    step counts the AdamW steps including this one (>= 1).  emas: optional list
+    of tensors (or None entries) advanced as ema = d*ema + (1-d)*param' with
+    d = ema_decay.
+    """
+    lib = _lib.load()
+    entries = _adamw_entries(params, grads, exp_avgs, exp_avg_sqs, emas)
+    table = _lib.adamw_table(entries)
+    device = params[0].device if params else None
+    rc = lib.adamw_step(table, len(entries), float(lr), float(betas[0]), float(betas[1]), float(eps),
+                        float(weight_decay), int(step), float(ema_decay), _stream_handle(stream, device))
+    _lib.check(rc)
+
+
+class PreparedAdamW:
+    """adamw_step with the tensor table marshalled once."""
+
+    def __init__(self, params, grads, exp_avgs, exp_avg_sqs, emas=None):
+        self._keep = (list(params), list(grads), list(exp_avgs), list(exp_avg_sqs), emas)
+        entries = _adamw_entries(params, grads, exp_avgs, exp_avg_sqs, emas)
+        self.n = len(entries)
+        self.table = _lib.adamw_table(entries)
+        self.device = params[0].device
+
+    def __call__(self, *, lr, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01, step, ema_decay=0.0, stream=None):
+        rc = _lib.load().adamw_step(self.table, self.n, float(lr), float(betas[0]), float(betas[1]), float(eps),
+                                    float(weight_decay), int(step), float(ema_decay),
+                                    _stream_handle(stream, self.device))
+        _lib.check(rc)
+
+
 def profile_enable(enable: bool = True) -> None:
     _lib.check(_lib.load().muon_profile_enable(int(bool(enable))))
 

@@ -272,6 +272,11 @@ int validate_pointers(const muon_tensor_t* t, int32_t n) {
     return check_overlaps(spans, "muon_step");
 }
 
+// Streaming tensors (EMA, AdamW): at most 2^30 workgroups per launch, so a
+// single tensor may hold at most this many elements (4 Ti elements; far above
+// any device memory).
+constexpr int64_t kMaxStreamElems = ((int64_t)1 << 30) * 1024;
+
 }  // namespace
 }  // namespace muon
 
@@ -658,6 +663,9 @@ int ema_update(float* const* ema, const float* const* params, const int64_t* num
     std::vector<Span> spans;
     for (int i = 0; i < n; ++i) {
         if (numel[i] < 0) return fail(MUON_ERR_INVALID_ARG, "numel[%d] = %lld is negative", i, (long long)numel[i]);
+        if (numel[i] > kMaxStreamElems)
+            return fail(MUON_ERR_UNSUPPORTED, "numel[%d] = %lld beyond %lld", i, (long long)numel[i],
+                        (long long)kMaxStreamElems);
         if (numel[i] == 0) continue;
         if (!ema[i] || !params[i]) return fail(MUON_ERR_INVALID_ARG, "tensor %d: NULL pointer", i);
         if (reinterpret_cast<uintptr_t>(ema[i]) % 4 || reinterpret_cast<uintptr_t>(params[i]) % 4)
@@ -694,6 +702,84 @@ int ema_update(float* const* ema, const float* const* params, const int64_t* num
         if (a.n == 0) continue;
         hipError_t err = timed_launch("ema", s, [&] { return launch_ema(a, (int)blocks, s); });
         if (err != hipSuccess) return fail(MUON_ERR_HIP, "ema launch failed: %s", hipGetErrorString(err));
+    }
+    return MUON_OK;
+}
+
+int adamw_step(const adamw_tensor_t* tensors, int32_t n, float lr, float beta1, float beta2, float eps,
+               float weight_decay, int32_t step, float ema_decay, void* stream) {
+    if (!tensors) return fail(MUON_ERR_INVALID_ARG, "tensors is NULL");
+    if (n <= 0 || n > MUON_MAX_TENSORS) return fail(MUON_ERR_INVALID_ARG, "n = %d outside [1, %d]", n, MUON_MAX_TENSORS);
+    if (!std::isfinite(lr) || !std::isfinite(weight_decay) || !std::isfinite(eps))
+        return fail(MUON_ERR_INVALID_ARG, "lr, weight_decay and eps must be finite");
+    if (eps < 0.f) return fail(MUON_ERR_INVALID_ARG, "eps must be >= 0");
+    if (!(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f))
+        return fail(MUON_ERR_INVALID_ARG, "beta1 and beta2 must be in [0, 1)");
+    if (step < 1) return fail(MUON_ERR_INVALID_ARG, "step = %d must be >= 1", step);
+    if (!std::isfinite(ema_decay) || ema_decay < 0.f || ema_decay > 1.f)
+        return fail(MUON_ERR_INVALID_ARG, "ema_decay must be finite and in [0, 1]");
+    std::vector<Span> spans;
+    for (int i = 0; i < n; ++i) {
+        const adamw_tensor_t& x = tensors[i];
+        if (x.numel < 0) return fail(MUON_ERR_INVALID_ARG, "tensor %d: numel = %lld is negative", i, (long long)x.numel);
+        if (x.numel > kMaxStreamElems)
+            return fail(MUON_ERR_UNSUPPORTED, "tensor %d: numel = %lld beyond %lld", i, (long long)x.numel,
+                        (long long)kMaxStreamElems);
+        if (x.numel == 0) continue;
+        if (!x.param || !x.grad || !x.exp_avg || !x.exp_avg_sq)
+            return fail(MUON_ERR_INVALID_ARG, "tensor %d: param, grad, exp_avg and exp_avg_sq must be non-NULL", i);
+        const void* ptrs[5] = {x.param, x.grad, x.exp_avg, x.exp_avg_sq, x.ema};
+        const size_t bytes = (size_t)x.numel * sizeof(float);
+        for (int k = 0; k < 5; ++k) {
+            if (!ptrs[k]) continue;
+            const uintptr_t lo = reinterpret_cast<uintptr_t>(ptrs[k]);
+            if (lo % sizeof(float)) return fail(MUON_ERR_INVALID_ARG, "tensor %d: pointer %d is not 4-byte aligned", i, k);
+            spans.push_back({lo, lo + bytes, i});
+        }
+    }
+    int rc = check_overlaps(spans, "adamw_step");
+    if (rc) return rc;
+    // bias corrections in double, folded into two fp32 factors
+    const double bc1 = 1.0 - std::pow((double)beta1, (double)step);
+    const double bc2 = 1.0 - std::pow((double)beta2, (double)step);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int i = 0;
+    while (i < n) {
+        AdamArgs a;
+        memset(&a, 0, sizeof(a));
+        a.keep = 1.0f - lr * weight_decay;
+        a.beta1 = beta1;
+        a.one_minus_beta1 = 1.0f - beta1;
+        a.beta2 = beta2;
+        a.one_minus_beta2 = 1.0f - beta2;
+        a.step_size = (float)((double)lr / bc1);
+        a.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
+        a.eps = eps;
+        a.decay = ema_decay;
+        a.one_minus_decay = 1.0f - ema_decay;
+        int64_t blocks = 0;
+        for (; i < n && a.n < kAdamChunk; ++i) {
+            const adamw_tensor_t& x = tensors[i];
+            if (x.numel == 0) continue;
+            const int64_t nb = (x.numel + kAdamElemsPerBlock - 1) / kAdamElemsPerBlock;
+            if (blocks + nb > (int64_t)1 << 30) break;
+            AdamTensor& T = a.t[a.n++];
+            T.param = x.param;
+            T.grad = x.grad;
+            T.m = x.exp_avg;
+            T.v = x.exp_avg_sq;
+            T.ema = x.ema;
+            T.numel = x.numel;
+            T.block_begin = (int)blocks;
+            T.vec = 1;
+            const void* ptrs[5] = {x.param, x.grad, x.exp_avg, x.exp_avg_sq, x.ema};
+            for (int k = 0; k < 5; ++k)
+                if (reinterpret_cast<uintptr_t>(ptrs[k]) % 16) T.vec = 0;
+            blocks += nb;
+        }
+        if (a.n == 0) continue;
+        hipError_t err = timed_launch("adamw", s, [&] { return launch_adamw(a, (int)blocks, s); });
+        if (err != hipSuccess) return fail(MUON_ERR_HIP, "adamw launch failed: %s", hipGetErrorString(err));
     }
     return MUON_OK;
 }

@@ -431,6 +431,74 @@ __global__ __launch_bounds__(kEmaThreads) void ema_kernel(const EmaArgs a) {
     }
 }
 
+// AdamW on one element: decoupled decay of the pre-update parameter, moment
+// updates, bias-corrected step (the host folds 1/(1 - beta1^t) into step_size
+// and 1/sqrt(1 - beta2^t) into inv_sqrt_bc2).
+__device__ inline float adamw_elem(const AdamArgs& a, float p, float g, float& m, float& v) {
+    m = fmaf(a.beta1, m, a.one_minus_beta1 * g);
+    v = fmaf(a.beta2, v, a.one_minus_beta2 * (g * g));
+    const float denom = fmaf(sqrtf(v), a.inv_sqrt_bc2, a.eps);
+    return fmaf(-a.step_size, m / denom, a.keep * p);
+}
+
+// AdamW (then the EMA on the updated parameter, where one is given) over a
+// chunk of kAdamElemsPerBlock elements of one tensor.  Streaming: every
+// operand is read and written once, with 16-byte non-temporal accesses.
+__global__ __launch_bounds__(kAdamThreads) void adamw_kernel(const AdamArgs a) {
+    const int ti = find_tensor(a.t, a.n, blockIdx.x);
+    const AdamTensor& T = a.t[ti];
+    const int64_t base = (int64_t)(blockIdx.x - T.block_begin) * kAdamElemsPerBlock;
+    const int64_t end = min(base + (int64_t)kAdamElemsPerBlock, T.numel);
+    const float d = a.decay, omd = a.one_minus_decay;
+    if (T.vec && end - base == kAdamElemsPerBlock) {
+        floatx4* p4 = reinterpret_cast<floatx4*>(T.param + base);
+        const floatx4* g4 = reinterpret_cast<const floatx4*>(T.grad + base);
+        floatx4* m4 = reinterpret_cast<floatx4*>(T.m + base);
+        floatx4* v4 = reinterpret_cast<floatx4*>(T.v + base);
+        floatx4* e4 = T.ema ? reinterpret_cast<floatx4*>(T.ema + base) : nullptr;
+        floatx4 pv[2], gv[2], mv[2], vv[2], ev[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int j = threadIdx.x + k * kAdamThreads;
+            pv[k] = __builtin_nontemporal_load(p4 + j);
+            gv[k] = __builtin_nontemporal_load(g4 + j);
+            mv[k] = __builtin_nontemporal_load(m4 + j);
+            vv[k] = __builtin_nontemporal_load(v4 + j);
+            if (e4) ev[k] = __builtin_nontemporal_load(e4 + j);
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int j = threadIdx.x + k * kAdamThreads;
+            floatx4 pn, mn, vn;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float m = mv[k][e], v = vv[k][e];
+                pn[e] = adamw_elem(a, pv[k][e], gv[k][e], m, v);
+                mn[e] = m;
+                vn[e] = v;
+            }
+            __builtin_nontemporal_store(pn, p4 + j);
+            __builtin_nontemporal_store(mn, m4 + j);
+            __builtin_nontemporal_store(vn, v4 + j);
+            if (e4) {
+                floatx4 en;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) en[e] = fmaf(d, ev[k][e], omd * pn[e]);
+                __builtin_nontemporal_store(en, e4 + j);
+            }
+        }
+        return;
+    }
+    for (int64_t i = base + threadIdx.x; i < end; i += kAdamThreads) {
+        float m = T.m[i], v = T.v[i];
+        const float p = adamw_elem(a, T.param[i], T.grad[i], m, v);
+        T.param[i] = p;
+        T.m[i] = m;
+        T.v[i] = v;
+        if (T.ema) T.ema[i] = fmaf(d, T.ema[i], omd * p);
+    }
+}
+
 }  // namespace
 
 template <typename K>
@@ -483,6 +551,11 @@ hipError_t launch_apply(const ApplyArgs& a, int precision, int blocks, size_t ld
 
 hipError_t launch_ema(const EmaArgs& a, int blocks, hipStream_t s) {
     ema_kernel<<<blocks, kEmaThreads, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_adamw(const AdamArgs& a, int blocks, hipStream_t s) {
+    adamw_kernel<<<blocks, kAdamThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -136,7 +136,33 @@ struct EmaArgs {
 constexpr int kEmaThreads = 256;
 constexpr int kEmaElemsPerBlock = kEmaThreads * 4 * 4;  // float4 x 4 per thread
 
+// AdamW over a chunk of tensors (one workgroup per kAdamElemsPerBlock elements)
+constexpr int kAdamChunk = 64;
+struct AdamTensor {
+    float* param;
+    const float* grad;
+    float* m;
+    float* v;
+    float* ema;          // nullable
+    int64_t numel;
+    int block_begin;
+    int vec;             // every pointer 16-byte aligned
+};
+struct AdamArgs {
+    AdamTensor t[kAdamChunk];
+    int n;
+    float keep;          // 1 - lr*wd
+    float beta1, one_minus_beta1, beta2, one_minus_beta2;
+    float step_size;     // lr / (1 - beta1^t)
+    float inv_sqrt_bc2;  // 1 / sqrt(1 - beta2^t)
+    float eps;
+    float decay, one_minus_decay;
+};
+constexpr int kAdamThreads = 256;
+constexpr int kAdamElemsPerBlock = kAdamThreads * 4 * 2;  // float4 x 2 per thread
+
 static_assert(sizeof(PrepArgs) <= 4096, "prep kernel arguments exceed 4 KiB");
+static_assert(sizeof(AdamArgs) <= 4096, "AdamW kernel arguments exceed 4 KiB");
 static_assert(sizeof(FrobArgs) <= 4096, "frob kernel arguments exceed 4 KiB");
 static_assert(sizeof(NsArgs) <= 4096, "NS kernel arguments exceed 4 KiB");
 static_assert(sizeof(ApplyArgs) <= 4096, "apply kernel arguments exceed 4 KiB");
@@ -148,6 +174,7 @@ hipError_t launch_frob(const FrobArgs& a, hipStream_t s);
 hipError_t launch_ns(const NsArgs& a, int phase, int precision, bool compensated, hipStream_t s);
 hipError_t launch_apply(const ApplyArgs& a, int precision, int blocks, size_t lds_bytes, hipStream_t s);
 hipError_t launch_ema(const EmaArgs& a, int blocks, hipStream_t s);
+hipError_t launch_adamw(const AdamArgs& a, int blocks, hipStream_t s);
 
 const char* ns_kernel_name(int phase, int precision, bool compensated, bool fused_apply);
 

@@ -298,6 +298,59 @@ def check_page_hyperparameters():
     assert w3.n_params == 131_717_212  # the same list at double width (a reading)
 
 
+def check_adamw_hand_values(m):
+    """AdamW values derived by hand (the update of the non-matrix parameters)."""
+    # Step 1 from zero moments: the bias corrections make m_hat = g and v_hat = g^2, so
+    # p' = (1 - lr wd) p - lr g / (|g| + eps).  lr 0.1, wd 0.5, eps 0.5, beta1 0.9, beta2 0.99:
+    #   p = 1,    g = 2:    0.95 - 0.1 * 2 / 2.5   = 0.87
+    #   p = -2,   g = 0.5: -1.9  - 0.1 * 0.5 / 1.0 = -1.95
+    #   p = 0.5,  g = 0:    0.475
+    p, g = np.array([1.0, -2.0, 0.5]), np.array([2.0, 0.5, 0.0])
+    pn, mn, vn = m.adamw_update(p, g, np.zeros(3), np.zeros(3), lr=0.1, beta1=0.9, beta2=0.99, eps=0.5,
+                                wd=0.5, step=1)
+    assert np.allclose(pn, [0.87, -1.95, 0.475], rtol=1e-14, atol=1e-15)
+    assert np.allclose(mn, [0.2, 0.05, 0.0], rtol=1e-14, atol=0)          # (1 - beta1) g
+    assert np.allclose(vn, [0.04, 0.0025, 0.0], rtol=1e-13, atol=0)       # (1 - beta2) g^2
+    # A zero gradient at step 2 (beta1 0.5, beta2 0.75, eps 0, wd 0): m' = 0.15, v' = 0.03,
+    # m_hat = 0.15 / 0.75 = 0.2, v_hat = 0.03 / 0.4375 = 0.0685714..., sqrt = 0.2618614682831909,
+    # p' = 1 - 0.1 * 0.2 / 0.2618614682831909 = 0.9236237384174026
+    pn, mn, vn = m.adamw_update([1.0], [0.0], [0.3], [0.04], lr=0.1, beta1=0.5, beta2=0.75, eps=0.0, wd=0.0,
+                                step=2)
+    assert np.allclose(mn, [0.15], rtol=1e-15) and np.allclose(vn, [0.03], rtol=1e-15)
+    assert np.allclose(pn, [0.9236237384174026], rtol=1e-14)
+    # weight decay only (zero gradient, zero moments): p' = (1 - lr wd) p exactly
+    pn, _, _ = m.adamw_update([3.0], [0.0], [0.0], [0.0], lr=0.2, beta1=0.9, beta2=0.999, eps=1e-8, wd=0.25,
+                              step=5)
+    assert pn[0] == 3.0 * 0.95
+
+
+def check_adamw_against_torch(m):
+    """torch.optim.AdamW (CPU, float64, single-tensor loop), from zero state over 4 steps, three settings."""
+    import torch
+    settings = [dict(lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01),
+                dict(lr=0.05, betas=(0.8, 0.95), eps=1e-6, weight_decay=0.1),
+                dict(lr=0.3, betas=(0.5, 0.6), eps=1e-3, weight_decay=0.0)]
+    for k, st in enumerate(settings):
+        rng = np.random.default_rng(100 + k)
+        p0 = rng.standard_normal((7, 5))
+        tp = torch.tensor(p0, dtype=torch.float64, requires_grad=True)
+        opt = torch.optim.AdamW([tp], foreach=False, **st)
+        p, mm, vv = p0.copy(), np.zeros_like(p0), np.zeros_like(p0)
+        for t in range(1, 5):
+            g = rng.standard_normal(p0.shape) * (0.1 if t % 2 else 3.0)
+            tp.grad = torch.tensor(g, dtype=torch.float64)
+            opt.step()
+            p, mm, vv = m.adamw_update(p, g, mm, vv, lr=st["lr"], beta1=st["betas"][0], beta2=st["betas"][1],
+                                       eps=st["eps"], wd=st["weight_decay"], step=t)
+            state = opt.state[tp]
+            assert np.allclose(p, tp.detach().numpy(), rtol=1e-12, atol=1e-14), (k, t)
+            assert np.allclose(mm, state["exp_avg"].numpy(), rtol=1e-12, atol=1e-14), (k, t)
+            assert np.allclose(vv, state["exp_avg_sq"].numpy(), rtol=1e-12, atol=1e-14), (k, t)
+
+
+ADAMW_CHECKS = [check_adamw_hand_values, check_adamw_against_torch]
+
+
 ALL_ORACLE_CHECKS = [
     check_ns_svd_closed_form, check_ns_order_of_table, check_ns_invariants,
     check_ns_fixed_band, check_ns_special_cases, check_momentum, check_row_normalize,

@@ -29,7 +29,7 @@ def _declared_functions():
 
 def test_header_declares_the_abi():
     names = _declared_functions()
-    assert names == sorted(["muon_workspace_size", "muon_step", "ema_update", "muon_last_error",
+    assert names == sorted(["muon_workspace_size", "muon_step", "ema_update", "adamw_step", "muon_last_error",
                             "muon_version", "muon_profile_enable", "muon_profile_read"])
 
 
@@ -52,6 +52,7 @@ def test_header_constants_match_binding():
         assert m, name
         assert int(m.group(1)) == getattr(_lib, name), name
     assert ctypes.sizeof(_lib.MuonTensor) == 48
+    assert ctypes.sizeof(_lib.AdamWTensor) == 48
 
 
 # Fake, well-separated device addresses: validation only compares them.
@@ -192,3 +193,58 @@ def test_profile_read_without_events():
     lib = _lib.load()
     assert lib.muon_profile_enable(0) == 0
     assert lib.muon_profile_read(None, None, None, 0, 1) == 0
+
+
+def _adam_t(i, numel, ema=False):
+    span = 1 << 30
+    p = BASE + 5 * i * span
+    return (p, p + span, p + 2 * span, p + 3 * span, (p + 4 * span) if ema else 0, numel)
+
+
+def _adam_call(entries, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.01, step=10, ema_decay=0.99, n=None):
+    lib = _lib.load()
+    table = _lib.adamw_table(entries)
+    rc = lib.adamw_step(table, len(entries) if n is None else n, lr, b1, b2, eps, wd, step, ema_decay, None)
+    return rc, lib.muon_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(n=0), _lib.MUON_ERR_INVALID_ARG, "n = 0"),
+    (dict(n=_lib.MUON_MAX_TENSORS + 1), _lib.MUON_ERR_INVALID_ARG, "outside"),
+    (dict(lr=float("nan")), _lib.MUON_ERR_INVALID_ARG, "finite"),
+    (dict(wd=float("inf")), _lib.MUON_ERR_INVALID_ARG, "finite"),
+    (dict(eps=-1e-8), _lib.MUON_ERR_INVALID_ARG, "eps"),
+    (dict(b1=1.0), _lib.MUON_ERR_INVALID_ARG, "beta1"),
+    (dict(b2=-0.5), _lib.MUON_ERR_INVALID_ARG, "beta1 and beta2"),
+    (dict(b2=float("nan")), _lib.MUON_ERR_INVALID_ARG, "beta1 and beta2"),
+    (dict(step=0), _lib.MUON_ERR_INVALID_ARG, "step"),
+    (dict(ema_decay=1.01), _lib.MUON_ERR_INVALID_ARG, "ema_decay"),
+])
+def test_adamw_rejects_bad_arguments(kw, code, msg):
+    rc, err = _adam_call([_adam_t(0, 1000, ema=True), _adam_t(1, 7)], **kw)
+    assert rc == code and msg in err, (rc, err)
+
+
+def test_adamw_rejects_bad_tensors():
+    p, g, m, v, e, k = _adam_t(0, 4096, ema=True)
+    assert _adam_call([(p, g, m, v, e, -1)])[0] == _lib.MUON_ERR_INVALID_ARG
+    assert _adam_call([(p, g, m, v, e, 1 << 41)])[0] == _lib.MUON_ERR_UNSUPPORTED
+    rc, err = _adam_call([(p, 0, m, v, e, k)])
+    assert rc == _lib.MUON_ERR_INVALID_ARG and "non-NULL" in err
+    rc, err = _adam_call([(p, g, m + 2, v, e, k)])
+    assert rc == _lib.MUON_ERR_INVALID_ARG and "aligned" in err
+    rc, err = _adam_call([(p, g, m, m + 64, e, k)])          # second moment overlaps the first
+    assert rc == _lib.MUON_ERR_UNSUPPORTED and "overlap" in err
+    rc, err = _adam_call([(p, g, m, v, p + 4, k)])           # ema overlaps the parameter
+    assert rc == _lib.MUON_ERR_UNSUPPORTED and "overlap" in err
+    q = _adam_t(1, 4096)
+    rc, err = _adam_call([(p, g, m, v, e, k), (q[0], g + 1024, q[2], q[3], 0, k)])  # two tensors share a grad
+    assert rc == _lib.MUON_ERR_UNSUPPORTED and "tensors 0 and 1" in err
+
+
+def test_streaming_entry_points_reject_huge_tensors():
+    lib = _lib.load()
+    e = (ctypes.c_void_p * 1)(BASE)
+    p = (ctypes.c_void_p * 1)(BASE + (1 << 44))
+    ne = (ctypes.c_int64 * 1)(1 << 41)
+    assert lib.ema_update(e, p, ne, 1, 0.5, None) == _lib.MUON_ERR_UNSUPPORTED

@@ -12,6 +12,7 @@ import types
 
 import pytest
 
+import oracle.adamw as oa
 import oracle.muon as om
 from tests import oracle_checks as oc
 
@@ -52,16 +53,32 @@ MUTANTS = {
 }
 
 
-def _mutant_module(old: str, new: str) -> types.ModuleType:
-    src = inspect.getsource(om)
+# The AdamW oracle (non-matrix parameters), checked by its own pins.
+ADAMW_MUTANTS = {
+    "adamw_no_bias_correction_m": ("m_hat = m_new / (1.0 - beta1 ** step)", "m_hat = m_new"),
+    "adamw_no_bias_correction_v": ("v_hat = v_new / (1.0 - beta2 ** step)", "v_hat = v_new"),
+    "adamw_step_counted_from_zero": ("(1.0 - beta1 ** step)", "(1.0 - beta1 ** (step + 1))"),
+    "adamw_eps_inside_sqrt": ("(np.sqrt(v_hat) + eps)", "np.sqrt(v_hat + eps)"),
+    "adamw_coupled_weight_decay": ("decayed = (1.0 - lr * wd) * p", "decayed = p\n    g = g + wd * p"),
+    "adamw_wd_without_lr": ("decayed = (1.0 - lr * wd) * p", "decayed = (1.0 - wd) * p"),
+    "adamw_wd_after_update": ("p_new = decayed - lr * m_hat / (np.sqrt(v_hat) + eps)",
+                              "p_new = (1.0 - lr * wd) * (p - lr * m_hat / (np.sqrt(v_hat) + eps))"),
+    "adamw_second_moment_not_squared": ("(1.0 - beta2) * (g * g)", "(1.0 - beta2) * g"),
+    "adamw_betas_swapped": ("m_new = beta1 * m + (1.0 - beta1) * g", "m_new = beta2 * m + (1.0 - beta2) * g"),
+    "adamw_update_sign": ("p_new = decayed - lr * m_hat", "p_new = decayed + lr * m_hat"),
+}
+
+
+def _mutant_module(old: str, new: str, base=om) -> types.ModuleType:
+    src = inspect.getsource(base)
     assert src.count(old) >= 1, f"mutation site not found: {old!r}"
     mod = types.ModuleType("oracle_mutant")
     exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
     return mod
 
 
-def _caught(mod) -> bool:
-    for check in oc.ALL_ORACLE_CHECKS:
+def _caught(mod, checks=oc.ALL_ORACLE_CHECKS) -> bool:
+    for check in checks:
         try:
             check(mod)
         except Exception:
@@ -80,3 +97,16 @@ def test_unmutated_copy_passes():
     mod = types.ModuleType("oracle_copy")
     exec(compile(src, "oracle_copy", "exec"), mod.__dict__)
     assert not _caught(mod)
+
+
+@pytest.mark.parametrize("name", sorted(ADAMW_MUTANTS))
+def test_adamw_mutant_is_caught(name):
+    old, new = ADAMW_MUTANTS[name]
+    assert _caught(_mutant_module(old, new, oa), oc.ADAMW_CHECKS), f"mutant {name} survived every pin"
+
+
+def test_unmutated_adamw_copy_passes():
+    src = inspect.getsource(oa)
+    mod = types.ModuleType("oracle_copy")
+    exec(compile(src, "oracle_copy", "exec"), mod.__dict__)
+    assert not _caught(mod, oc.ADAMW_CHECKS)

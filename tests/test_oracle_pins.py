@@ -2,6 +2,7 @@
 
 import pytest
 
+import oracle.adamw as oa
 import oracle.muon as om
 from tests import oracle_checks as oc
 
@@ -13,3 +14,8 @@ def test_oracle_pin(check):
 
 def test_page_hyperparameters():
     oc.check_page_hyperparameters()
+
+
+@pytest.mark.parametrize("check", oc.ADAMW_CHECKS, ids=lambda f: f.__name__)
+def test_adamw_oracle_pin(check):
+    check(oa)

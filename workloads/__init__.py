@@ -193,6 +193,28 @@ def make_grads(w: Workload, seed: int, step: int = 0) -> List[np.ndarray]:
     return out
 
 
+# AdamW on the non-matrix parameters ("Architecture and training stack", Optimizer
+# row, PR #1893, names the optimizer and nothing else).  Reading: the library
+# defaults of torch.optim.AdamW; the step counter is past the first steps so
+# that both bias corrections are live (0.9^1000 is negligible, 0.999^1000 is not).
+ADAMW_HPARAMS = {"lr": 1e-3, "beta1": 0.9, "beta2": 0.999, "eps": 1e-8, "weight_decay": 0.01, "step": 1000}
+
+
+def make_adamw_state(w: Workload, seed: int, step: int = 0):
+    """Gradients and AdamW moments of the non-matrix parameters (float32).
+
+    exp_avg ~ N(0, grad_std^2); exp_avg_sq is the square of an independent
+    N(0, grad_std^2) draw (non-negative, as the second moment always is).
+    """
+    grads, m1, m2 = [], [], []
+    for j, (_, shape) in enumerate(w.extras):
+        rng = _rng(seed, 0xADA, step, j)
+        grads.append(_normal32(rng, shape, w.grad_std))
+        m1.append(_normal32(rng, shape, w.grad_std))
+        m2.append(np.square(_normal32(rng, shape, w.grad_std)))
+    return {"grads": grads, "exp_avg": m1, "exp_avg_sq": m2}
+
+
 def make_independent_ema(w: Workload, seed: int) -> List[np.ndarray]:
     """EMA shadows drawn independently of the weights (so no element is trivial)."""
     out = []

@@ -77,6 +77,11 @@ template <int RB> struct Stage {
 };
 constexpr int kStagePitch = kTile + 4;      // fp32 epilogue staging row pitch
 constexpr int kStageBytes = 64 * kStagePitch * 4;  // half a tile (64 rows) of fp32
+// Column of element (row, col) in the fp32 staging buffer: aligned 8-column
+// blocks are permuted per group of 8 rows, so the transposed (column) reads of
+// the mirror and tall-apply passes, 8 rows x 8 columns per wave, hit 64
+// distinct banks; rows keep their 8-column blocks contiguous and 16-byte aligned.
+__device__ inline int stage_col(int row, int col) { return col ^ (((row >> 3) & 7) << 3); }
 static_assert(kStageBytes <= 2 * Stage<128>::kSlot, "epilogue staging must fit in the operand LDS");
 
 // K bytes per LDS stage: 256 for the bf16 base Gram, whose long contraction
@@ -627,7 +632,7 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
                     for (int r = 0; r < 16; ++r) {
                         const int row = mi * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
                         const int col = wn * 64 + ni * 32 + (lane % 32);
-                        stage[row * kStagePitch + col] = acc[mi][ni][r];
+                        stage[row * kStagePitch + stage_col(row, col)] = acc[mi][ni][r];
                     }
         }
         __syncthreads();
@@ -637,7 +642,7 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
         for (int p = 0; p < 4; ++p) {
             const int lr = t / 16 + 16 * p;
             const int lc = 8 * (t % 16);
-            float* sp = stage + lr * kStagePitch + lc;
+            float* sp = stage + lr * kStagePitch + stage_col(lr, lc);
             float v[8];
             {
                 const floatx4 a = *reinterpret_cast<const floatx4*>(sp);
@@ -714,7 +719,7 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
                 if (wr < F.rows && wc < F.cols) {
                     float v[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = stage[(chunk * 8 + e) * kStagePitch + c];
+                    for (int e = 0; e < 8; ++e) v[e] = stage[(chunk * 8 + e) * kStagePitch + stage_col(chunk * 8 + e, c)];
                     apply8(F, (size_t)wr * F.cols + wc, F.cols - wc, v, args.keep, args.decay, args.one_minus_decay);
                 }
             }
@@ -728,7 +733,7 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
                 const int c = t / 8 + 32 * p;
                 float v[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = stage[(chunk * 8 + e) * kStagePitch + c];
+                for (int e = 0; e < 8; ++e) v[e] = stage[(chunk * 8 + e) * kStagePitch + stage_col(chunk * 8 + e, c)];
                 const size_t idx = (size_t)(job.tj * kTile + c) * M + row_base + chunk * 8;
                 if (PHASE == kGram)
                     store8<PREC>(static_cast<T*>(G.a_hi) + aplane, static_cast<T*>(G.a_lo) + aplane, idx, v);
@@ -907,7 +912,7 @@ __global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) 
                     for (int r = 0; r < 16; ++r) {
                         const int row = wm * 64 + mi * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
                         const int col = wn * 64 + ni * 32 + (lane % 32);
-                        float& dst = stage[row * kStagePitch + col];
+                        float& dst = stage[row * kStagePitch + stage_col(row, col)];
                         dst = pass == 0 ? acc[mi][ni][r] : dst + acc[mi][ni][r];
                     }
         }
@@ -918,7 +923,7 @@ __global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) 
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int lr = tid / 16 + 32 * p;
-        float* sp = stage + lr * kStagePitch + lc;
+        float* sp = stage + lr * kStagePitch + stage_col(lr, lc);
         float v[8];
         {
             const floatx4 a = *reinterpret_cast<const floatx4*>(sp);
@@ -957,14 +962,16 @@ __global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) 
     }
     if (!diag) {
         __syncthreads();
-        // mirrored tile: output row tj*128 + c, columns ti*128 + 8*chunk .. +7
+        // mirrored tile: output row tj*128 + c, columns ti*128 + 8*chunk .. +7.  A wave
+        // takes 8 rows c x 8 chunks (8 lanes write one row's 128 contiguous bytes).
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const int chunk = tid % 16;
-            const int c = tid / 16 + 32 * p;
+            const int l = tid % kWave;
+            const int chunk = l % 8 + 8 * (p % 2);
+            const int c = l / 8 + 8 * (tid / kWave) + 64 * (p / 2);
             float v[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = stage[(chunk * 8 + e) * kStagePitch + c];
+            for (int e = 0; e < 8; ++e) v[e] = stage[(chunk * 8 + e) * kStagePitch + stage_col(chunk * 8 + e, c)];
             const size_t idx = (size_t)(job.tj * kTile + c) * M + job.ti * kTile + chunk * 8;
             if (PHASE == kGram)
                 store8<PREC>(static_cast<T*>(G.a_hi) + aplane, static_cast<T*>(G.a_lo) + aplane, idx, v);

@@ -33,6 +33,8 @@
 // one launch; job indices are remapped so that the tiles of one matrix share
 // an XCD (and its L2).  Workspace dimensions are padded to 128 with zeros,
 // which the iteration keeps at zero, so no loop needs a bounds check.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -754,6 +756,9 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
 // (group 0 writes, group 1 adds) before the 512-thread epilogue.
 constexpr int kSymThreads = 2 * kThreads;
 constexpr int kSymStageBytes = kTile * kStagePitch * 4;   // a full tile of fp32
+// epilogue LDS: the staged tile, then the partial-sum exchange (2 groups x 4
+// waves x 8 chunks x 64 lanes x 16 bytes)
+constexpr int kSymEpilogueBytes = kSymStageBytes + 2 * 4 * 8 * kWave * 16;
 
 template <int PHASE, int PREC, bool COMP>
 __global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) {
@@ -899,24 +904,50 @@ __global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) 
             a_pre[p][1] = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(G.a_lo) + idx);
         }
     }
+    // The two groups hold partial sums of the same tile.  Group g finishes the
+    // 32-row blocks mi = g of every wave: it hands its partial of block 1 - g to
+    // the same wave of the other group through LDS (16-byte chunks in register
+    // order), adds the partial it receives, and stages its finished block.
     float* stage = reinterpret_cast<float*>(lds);
+    u32x4* xbuf = reinterpret_cast<u32x4*>(lds + kSymStageBytes);   // [group][wave][8 chunks][lane]
+    auto send = [&](auto mi_c) {
+        constexpr int mi = decltype(mi_c)::value;
+        u32x4* out = xbuf + ((kg * 4 + wave) * 8) * kWave + lane;
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-        __syncthreads();
-        if (kg == pass) {
+        for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
+            for (int q = 0; q < 4; ++q) {
+                floatx4 v;
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
+                for (int e = 0; e < 4; ++e) v[e] = acc[mi][ni][4 * q + e];
+                out[(ni * 4 + q) * kWave] = __builtin_bit_cast(u32x4, v);
+            }
+    };
+    auto finish = [&](auto mi_c) {
+        constexpr int mi = decltype(mi_c)::value;
+        const u32x4* in = xbuf + (((1 - kg) * 4 + wave) * 8) * kWave + lane;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int row = wm * 64 + mi * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
-                        const int col = wn * 64 + ni * 32 + (lane % 32);
-                        float& dst = stage[row * kStagePitch + stage_col(row, col)];
-                        dst = pass == 0 ? acc[mi][ni][r] : dst + acc[mi][ni][r];
-                    }
-        }
-    }
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const floatx4 v = __builtin_bit_cast(floatx4, in[(ni * 4 + q) * kWave]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[mi][ni][4 * q + e] += v[e];
+            }
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wm * 64 + mi * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+                const int col = wn * 64 + ni * 32 + (lane % 32);
+                stage[row * kStagePitch + stage_col(row, col)] = acc[mi][ni][r];
+            }
+    };
+    if (kg == 0) send(std::integral_constant<int, 1>{});
+    else send(std::integral_constant<int, 0>{});
+    __syncthreads();
+    if (kg == 0) finish(std::integral_constant<int, 0>{});
+    else finish(std::integral_constant<int, 1>{});
     __syncthreads();
     const float s = G.scale[job.slot];
     const float sc = args.first ? s * s : 1.0f;
@@ -1006,7 +1037,7 @@ hipError_t launch_one(const NsArgs& a, hipStream_t s) {
 size_t ns_sym_lds_bytes(int phase, int precision, bool comp) {
     const bool split = precision == kNsBf16 && (phase == kSquare || comp);
     const int slot = ns_stage_bytes(phase, precision, comp) == 256 ? Stage<256>::kSlot : Stage<128>::kSlot;
-    return std::max((size_t)2 * (split ? 4 : 2) * slot, (size_t)kSymStageBytes);
+    return std::max((size_t)2 * (split ? 4 : 2) * slot, (size_t)kSymEpilogueBytes);
 }
 
 template <int PHASE, int PREC, bool COMP>

@@ -334,45 +334,65 @@ __device__ inline void store8(void* hi, void* lo, size_t idx, const float* v) {
 
 // Fused weight update for up to 8 consecutive stored elements starting at idx:
 // W' = keep*W - lr_s*O, the optional copy of O, and the optional weight EMA
-// E' = d*E + (1-d)*W'.
-__device__ inline void apply8(const FusedApply& F, size_t idx, int count, const float* v, float keep, float d,
-                              float omd) {
+// E' = d*E + (1-d)*W'.  apply_load fetches W (and E) early, into registers, so
+// that the epilogue issues every load of a half tile before its first store
+// (a store to W could otherwise alias the next load in the compiler's view and
+// serialise one memory latency per row).
+__device__ inline void apply_load(const FusedApply& F, size_t idx, int count, floatx4* w, floatx4* e) {
+    if (count >= 8 && (F.flags & kApplyVec)) {
+        const floatx4* w4 = reinterpret_cast<const floatx4*>(F.param + idx);
+        w[0] = w4[0];
+        w[1] = w4[1];
+        if (F.ema) {
+            const floatx4* e4 = reinterpret_cast<const floatx4*>(F.ema + idx);
+            e[0] = e4[0];
+            e[1] = e4[1];
+        }
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        if (k < count) {
+            w[k / 4][k % 4] = F.param[idx + k];
+            if (F.ema) e[k / 4][k % 4] = F.ema[idx + k];
+        }
+    }
+}
+
+__device__ inline void apply_store(const FusedApply& F, size_t idx, int count, const float* v, const floatx4* w,
+                                   const floatx4* e, float keep, float d, float omd) {
+    floatx4 wn[2], en[2];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        wn[k / 4][k % 4] = fmaf(-F.lr_s, v[k], keep * w[k / 4][k % 4]);
+        en[k / 4][k % 4] = fmaf(d, e[k / 4][k % 4], omd * wn[k / 4][k % 4]);
+    }
     if (count >= 8 && (F.flags & kApplyVec)) {
         floatx4* w4 = reinterpret_cast<floatx4*>(F.param + idx);
-        floatx4 w0 = w4[0], w1 = w4[1];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            w0[e] = fmaf(-F.lr_s, v[e], keep * w0[e]);
-            w1[e] = fmaf(-F.lr_s, v[4 + e], keep * w1[e]);
-        }
-        w4[0] = w0;
-        w4[1] = w1;
+        w4[0] = wn[0];
+        w4[1] = wn[1];
         if (F.out) {
             floatx4 o0, o1;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { o0[e] = v[e]; o1[e] = v[4 + e]; }
+            for (int k = 0; k < 4; ++k) { o0[k] = v[k]; o1[k] = v[4 + k]; }
             floatx4* o4 = reinterpret_cast<floatx4*>(F.out + idx);
             o4[0] = o0;
             o4[1] = o1;
         }
         if (F.ema) {
             floatx4* e4 = reinterpret_cast<floatx4*>(F.ema + idx);
-            floatx4 e0 = e4[0], e1 = e4[1];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                e0[e] = fmaf(d, e0[e], omd * w0[e]);
-                e1[e] = fmaf(d, e1[e], omd * w1[e]);
-            }
-            e4[0] = e0;
-            e4[1] = e1;
+            e4[0] = en[0];
+            e4[1] = en[1];
         }
         return;
     }
-    for (int e = 0; e < count && e < 8; ++e) {
-        const float w = fmaf(-F.lr_s, v[e], keep * F.param[idx + e]);
-        F.param[idx + e] = w;
-        if (F.out) F.out[idx + e] = v[e];
-        if (F.ema) F.ema[idx + e] = fmaf(d, F.ema[idx + e], omd * w);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        if (k < count) {
+            F.param[idx + k] = wn[k / 4][k % 4];
+            if (F.out) F.out[idx + k] = v[k];
+            if (F.ema) F.ema[idx + k] = en[k / 4][k % 4];
+        }
     }
 }
 
@@ -611,6 +631,21 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
     const int t = threadIdx.x;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+        const int row_base = job.ti * kTile + h * 64;
+        // fused apply: W and E of this half's outputs are in flight while the
+        // accumulators are staged (row pass mapping for stored rows = X rows,
+        // column pass mapping for tall matrices, whose stored W is X^T)
+        floatx4 w_pre[4][2], e_pre[4][2];
+        if constexpr (FUSE) {
+            const FusedApply& F = args.apply[G.apply_begin + job.slot];
+            const bool tall = F.flags & kApplyTransposed;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int wr = tall ? job.tj * kTile + t / 8 + 32 * p : row_base + t / 16 + 16 * p;
+                const int wc = tall ? row_base + 8 * (t % 8) : job.tj * kTile + 8 * (t % 16);
+                if (wr < F.rows && wc < F.cols) apply_load(F, (size_t)wr * F.cols + wc, F.cols - wc, w_pre[p], e_pre[p]);
+            }
+        }
         // the square's epilogue input (A hi and lo of this half) is in flight
         // while the accumulators are staged
         constexpr bool kPreA = (PHASE == kSquare) && (PREC == kNsBf16) && (NS_PREFETCH_XL != 0);
@@ -638,7 +673,6 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
                     }
         }
         __syncthreads();
-        const int row_base = job.ti * kTile + h * 64;
         // row pass: thread -> (row t/16 + 16p, columns 8*(t%16) .. +7)
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
@@ -696,7 +730,9 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
                     // X row = stored row, X column = stored column
                     const FusedApply& F = args.apply[G.apply_begin + job.slot];
                     const int gi = row_base + lr, gj = job.tj * kTile + lc;
-                    if (gi < F.rows) apply8(F, (size_t)gi * F.cols + gj, F.cols - gj, v, args.keep, args.decay, args.one_minus_decay);
+                    if (gi < F.rows && gj < F.cols)
+                        apply_store(F, (size_t)gi * F.cols + gj, F.cols - gj, v, w_pre[p], e_pre[p], args.keep,
+                                    args.decay, args.one_minus_decay);
                 }
             }
             if ((PHASE != kUpdate && !diag) ||
@@ -722,7 +758,8 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
                     float v[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] = stage[(chunk * 8 + e) * kStagePitch + stage_col(chunk * 8 + e, c)];
-                    apply8(F, (size_t)wr * F.cols + wc, F.cols - wc, v, args.keep, args.decay, args.one_minus_decay);
+                    apply_store(F, (size_t)wr * F.cols + wc, F.cols - wc, v, w_pre[p], e_pre[p], args.keep,
+                                args.decay, args.one_minus_decay);
                 }
             }
         }

@@ -124,6 +124,18 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
 int ema_update(float* const* ema, const float* const* params, const int64_t* numel, int32_t n,
                float decay, void* stream);
 
+/* Exchange the contents of ema[i] and params[i] (numel[i] fp32 elements each),
+ * bit for bit: the weight EMA becomes the live parameter set, as the step
+ * before quantization and evaluation needs ("Record: L_ParallelResiduals_
+ * UNetSkips_DepthRecur_Muon_ 1.0901" (PR #1893), "Architecture and training
+ * stack", EMA row: the EMA is applied before quantization); a second call swaps
+ * the training weights back.
+ *   ema, params   host arrays of n device pointers (4-byte aligned), both
+ *                 updated in place; no two buffers of the call may overlap.
+ *   numel         host array of n element counts, each >= 0 (0 is skipped).
+ *   1 <= n <= MUON_MAX_TENSORS.  Same conventions as ema_update. */
+int ema_swap(float* const* ema, float* const* params, const int64_t* numel, int32_t n, void* stream);
+
 /* One fp32 tensor of the AdamW update (any shape, numel elements, contiguous).
  * param, exp_avg and exp_avg_sq are updated in place; grad is read only.  ema is
  * optional (NULL to skip): when set, the tensor's weight EMA is advanced on the

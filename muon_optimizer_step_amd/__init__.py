@@ -9,6 +9,6 @@ from ._lib import (  # noqa: F401
     MUON_NS_BF16, MUON_NS_FP32, MUON_NS_BF16X3, MuonError, LIB_PATH, load,
 )
 from .api import (  # noqa: F401
-    muon_step, ema_update, adamw_step, workspace_size, profile_enable, profile_read, version,
+    muon_step, ema_update, ema_swap, adamw_step, workspace_size, profile_enable, profile_read, version,
     PreparedMuonStep, PreparedEma, PreparedAdamW,
 )

@@ -75,6 +75,10 @@ def load() -> ctypes.CDLL:
     f.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_int64),
                   ctypes.c_int32, ctypes.c_float, ctypes.c_void_p]
     f.restype = ctypes.c_int
+    f = lib.ema_swap
+    f.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_int64),
+                  ctypes.c_int32, ctypes.c_void_p]
+    f.restype = ctypes.c_int
     f = lib.adamw_step
     f.argtypes = [ctypes.POINTER(AdamWTensor), ctypes.c_int32, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                   ctypes.c_float, ctypes.c_float, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p]

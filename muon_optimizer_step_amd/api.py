@@ -189,6 +189,25 @@ class PreparedAdamW:
         _lib.check(rc)
 
 
+def ema_swap(emas, params, stream=None) -> None:
+    """Exchange the contents of emas[i] and params[i] (fp32, same element count), bit for bit."""
+    lib = _lib.load()
+    n = len(emas)
+    if len(params) != n:
+        raise ValueError("emas and params must have the same length")
+    e_ptrs = (ctypes.c_void_p * max(1, n))()
+    p_ptrs = (ctypes.c_void_p * max(1, n))()
+    numel = (ctypes.c_int64 * max(1, n))()
+    for i, (e, p) in enumerate(zip(emas, params)):
+        _check_tensor(e, f"emas[{i}]")
+        _check_tensor(p, f"params[{i}]")
+        if e.numel() != p.numel():
+            raise ValueError(f"tensor {i}: {e.numel()} != {p.numel()} elements")
+        e_ptrs[i], p_ptrs[i], numel[i] = e.data_ptr(), p.data_ptr(), e.numel()
+    device = emas[0].device if n else None
+    _lib.check(lib.ema_swap(e_ptrs, p_ptrs, numel, n, _stream_handle(stream, device)))
+
+
 def profile_enable(enable: bool = True) -> None:
     _lib.check(_lib.load().muon_profile_enable(int(bool(enable))))
 

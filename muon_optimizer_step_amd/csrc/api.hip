@@ -706,6 +706,52 @@ int ema_update(float* const* ema, const float* const* params, const int64_t* num
     return MUON_OK;
 }
 
+int ema_swap(float* const* ema, float* const* params, const int64_t* numel, int32_t n, void* stream) {
+    if (!ema || !params || !numel) return fail(MUON_ERR_INVALID_ARG, "ema, params and numel must be non-NULL");
+    if (n <= 0 || n > MUON_MAX_TENSORS) return fail(MUON_ERR_INVALID_ARG, "n = %d outside [1, %d]", n, MUON_MAX_TENSORS);
+    std::vector<Span> spans;
+    for (int i = 0; i < n; ++i) {
+        if (numel[i] < 0) return fail(MUON_ERR_INVALID_ARG, "numel[%d] = %lld is negative", i, (long long)numel[i]);
+        if (numel[i] > kMaxStreamElems)
+            return fail(MUON_ERR_UNSUPPORTED, "numel[%d] = %lld beyond %lld", i, (long long)numel[i],
+                        (long long)kMaxStreamElems);
+        if (numel[i] == 0) continue;
+        if (!ema[i] || !params[i]) return fail(MUON_ERR_INVALID_ARG, "tensor %d: NULL pointer", i);
+        if (reinterpret_cast<uintptr_t>(ema[i]) % 4 || reinterpret_cast<uintptr_t>(params[i]) % 4)
+            return fail(MUON_ERR_INVALID_ARG, "tensor %d: pointer not 4-byte aligned", i);
+        const uintptr_t e = reinterpret_cast<uintptr_t>(ema[i]);
+        const uintptr_t q = reinterpret_cast<uintptr_t>(params[i]);
+        const size_t bytes = (size_t)numel[i] * sizeof(float);
+        spans.push_back({e, e + bytes, i});
+        spans.push_back({q, q + bytes, i});
+    }
+    int rc = check_overlaps(spans, "ema_swap");
+    if (rc) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int i = 0;
+    while (i < n) {
+        SwapArgs a;
+        memset(&a, 0, sizeof(a));
+        int64_t blocks = 0;
+        for (; i < n && a.n < kEmaChunk; ++i) {
+            if (numel[i] == 0) continue;
+            const int64_t nb = (numel[i] + kEmaElemsPerBlock - 1) / kEmaElemsPerBlock;
+            if (blocks + nb > (int64_t)1 << 30) break;
+            SwapTensor& T = a.t[a.n++];
+            T.a = ema[i];
+            T.b = params[i];
+            T.numel = numel[i];
+            T.block_begin = (int)blocks;
+            T.vec = (reinterpret_cast<uintptr_t>(ema[i]) % 16 == 0) && (reinterpret_cast<uintptr_t>(params[i]) % 16 == 0);
+            blocks += nb;
+        }
+        if (a.n == 0) continue;
+        hipError_t err = timed_launch("swap", s, [&] { return launch_swap(a, (int)blocks, s); });
+        if (err != hipSuccess) return fail(MUON_ERR_HIP, "swap launch failed: %s", hipGetErrorString(err));
+    }
+    return MUON_OK;
+}
+
 int adamw_step(const adamw_tensor_t* tensors, int32_t n, float lr, float beta1, float beta2, float eps,
                float weight_decay, int32_t step, float ema_decay, void* stream) {
     if (!tensors) return fail(MUON_ERR_INVALID_ARG, "tensors is NULL");

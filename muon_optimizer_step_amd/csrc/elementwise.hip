@@ -431,6 +431,35 @@ __global__ __launch_bounds__(kEmaThreads) void ema_kernel(const EmaArgs a) {
     }
 }
 
+// Exchange a chunk of kEmaElemsPerBlock elements of two buffers (bit for bit).
+__global__ __launch_bounds__(kEmaThreads) void swap_kernel(const SwapArgs a) {
+    const int ti = find_tensor(a.t, a.n, blockIdx.x);
+    const SwapTensor& T = a.t[ti];
+    const int64_t base = (int64_t)(blockIdx.x - T.block_begin) * kEmaElemsPerBlock;
+    const int64_t end = min(base + (int64_t)kEmaElemsPerBlock, T.numel);
+    if (T.vec && end - base == kEmaElemsPerBlock) {
+        floatx4* a4 = reinterpret_cast<floatx4*>(T.a + base);
+        floatx4* b4 = reinterpret_cast<floatx4*>(T.b + base);
+        floatx4 av[4], bv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            av[k] = __builtin_nontemporal_load(a4 + threadIdx.x + k * kEmaThreads);
+            bv[k] = __builtin_nontemporal_load(b4 + threadIdx.x + k * kEmaThreads);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            __builtin_nontemporal_store(bv[k], a4 + threadIdx.x + k * kEmaThreads);
+            __builtin_nontemporal_store(av[k], b4 + threadIdx.x + k * kEmaThreads);
+        }
+        return;
+    }
+    for (int64_t i = base + threadIdx.x; i < end; i += kEmaThreads) {
+        const float x = T.a[i];
+        T.a[i] = T.b[i];
+        T.b[i] = x;
+    }
+}
+
 // AdamW on one element: decoupled decay of the pre-update parameter, moment
 // updates, bias-corrected step (the host folds 1/(1 - beta1^t) into step_size
 // and 1/sqrt(1 - beta2^t) into inv_sqrt_bc2).
@@ -551,6 +580,11 @@ hipError_t launch_apply(const ApplyArgs& a, int precision, int blocks, size_t ld
 
 hipError_t launch_ema(const EmaArgs& a, int blocks, hipStream_t s) {
     ema_kernel<<<blocks, kEmaThreads, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_swap(const SwapArgs& a, int blocks, hipStream_t s) {
+    swap_kernel<<<blocks, kEmaThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -136,6 +136,19 @@ struct EmaArgs {
 constexpr int kEmaThreads = 256;
 constexpr int kEmaElemsPerBlock = kEmaThreads * 4 * 4;  // float4 x 4 per thread
 
+// Swap of two fp32 buffers per tensor (the EMA swap-in), same chunking as the EMA
+struct SwapTensor {
+    float* a;
+    float* b;
+    int64_t numel;
+    int block_begin;
+    int vec;             // both pointers 16-byte aligned
+};
+struct SwapArgs {
+    SwapTensor t[kEmaChunk];
+    int n;
+};
+
 // AdamW over a chunk of tensors (one workgroup per kAdamElemsPerBlock elements)
 constexpr int kAdamChunk = 64;
 struct AdamTensor {
@@ -163,6 +176,7 @@ constexpr int kAdamElemsPerBlock = kAdamThreads * 4 * 2;  // float4 x 2 per thre
 
 static_assert(sizeof(PrepArgs) <= 4096, "prep kernel arguments exceed 4 KiB");
 static_assert(sizeof(AdamArgs) <= 4096, "AdamW kernel arguments exceed 4 KiB");
+static_assert(sizeof(SwapArgs) <= 4096, "swap kernel arguments exceed 4 KiB");
 static_assert(sizeof(FrobArgs) <= 4096, "frob kernel arguments exceed 4 KiB");
 static_assert(sizeof(NsArgs) <= 4096, "NS kernel arguments exceed 4 KiB");
 static_assert(sizeof(ApplyArgs) <= 4096, "apply kernel arguments exceed 4 KiB");
@@ -175,6 +189,7 @@ hipError_t launch_ns(const NsArgs& a, int phase, int precision, bool compensated
 hipError_t launch_apply(const ApplyArgs& a, int precision, int blocks, size_t lds_bytes, hipStream_t s);
 hipError_t launch_ema(const EmaArgs& a, int blocks, hipStream_t s);
 hipError_t launch_adamw(const AdamArgs& a, int blocks, hipStream_t s);
+hipError_t launch_swap(const SwapArgs& a, int blocks, hipStream_t s);
 
 const char* ns_kernel_name(int phase, int precision, bool compensated, bool fused_apply);
 

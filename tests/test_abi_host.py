@@ -29,8 +29,8 @@ def _declared_functions():
 
 def test_header_declares_the_abi():
     names = _declared_functions()
-    assert names == sorted(["muon_workspace_size", "muon_step", "ema_update", "adamw_step", "muon_last_error",
-                            "muon_version", "muon_profile_enable", "muon_profile_read"])
+    assert names == sorted(["muon_workspace_size", "muon_step", "ema_update", "ema_swap", "adamw_step",
+                            "muon_last_error", "muon_version", "muon_profile_enable", "muon_profile_read"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -248,3 +248,22 @@ def test_streaming_entry_points_reject_huge_tensors():
     p = (ctypes.c_void_p * 1)(BASE + (1 << 44))
     ne = (ctypes.c_int64 * 1)(1 << 41)
     assert lib.ema_update(e, p, ne, 1, 0.5, None) == _lib.MUON_ERR_UNSUPPORTED
+
+
+def test_ema_swap_rejects_bad_arguments():
+    lib = _lib.load()
+    n = 2
+    e = (ctypes.c_void_p * n)(BASE, BASE + (1 << 30))
+    p = (ctypes.c_void_p * n)(BASE + (2 << 30), BASE + (3 << 30))
+    ne = (ctypes.c_int64 * n)(100, 200)
+
+    def call(e=e, p=p, ne=ne, n=n):
+        return lib.ema_swap(e, p, ne, n, None), lib.muon_last_error().decode()
+
+    assert call(n=0)[0] == _lib.MUON_ERR_INVALID_ARG
+    assert call(ne=(ctypes.c_int64 * n)(100, -1))[0] == _lib.MUON_ERR_INVALID_ARG
+    assert call(ne=(ctypes.c_int64 * n)(100, 1 << 41))[0] == _lib.MUON_ERR_UNSUPPORTED
+    rc, err = call(p=(ctypes.c_void_p * n)(BASE + 64, BASE + (3 << 30)))   # param 0 inside ema 0
+    assert rc == _lib.MUON_ERR_UNSUPPORTED and "overlap" in err
+    assert call(e=(ctypes.c_void_p * n)(0, BASE + (1 << 30)))[0] == _lib.MUON_ERR_INVALID_ARG
+    assert call(p=(ctypes.c_void_p * n)(BASE + (2 << 30) + 1, BASE + (3 << 30)))[0] == _lib.MUON_ERR_INVALID_ARG

@@ -193,3 +193,28 @@ def test_more_matrices_than_the_fused_apply_table():
     for i in range(0, 80, 7):
         gu.check_layers(mats[i], grads[i], moms[i], w_gpu[i], m_gpu[i], o_gpu[i], lr=0.03, momentum=0.9, wd=0.1,
                         coeffs=STD, nesterov=True, row_norm=True, ns_tol=gu.NS_TOL_BF16, label=f"{i}")
+
+
+def test_ema_swap_is_an_exact_exchange():
+    """ema_swap exchanges the buffers bit for bit (vector and scalar paths, many tensors); twice is identity."""
+    import torch
+    import muon_optimizer_step_amd as ms
+    rng = np.random.default_rng(31)
+    sizes = [4096 * 3, 1, 4095, 4097, 512, 92] + [int(x) for x in rng.integers(1, 9000, size=130)]
+    total = sum(sizes) + 3 * len(sizes)
+    flat_e = torch.from_numpy(rng.standard_normal(total).astype(np.float32)).cuda()
+    flat_p = torch.from_numpy(rng.standard_normal(total).astype(np.float32)).cuda()
+    E, P, pos = [], [], 0
+    for i, k in enumerate(sizes):
+        off = pos + (i % 3)          # some tensors start off the 16-byte grid
+        E.append(flat_e[off:off + k])
+        P.append(flat_p[off:off + k])
+        pos += k + 3
+    e0 = [x.clone() for x in E]
+    p0 = [x.clone() for x in P]
+    ms.ema_swap(E, P)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(E, p0)) and all(torch.equal(a, b) for a, b in zip(P, e0))
+    ms.ema_swap(E, P)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(E, e0)) and all(torch.equal(a, b) for a, b in zip(P, p0))

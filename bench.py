@@ -349,6 +349,8 @@ def main():
         muon = ms.PreparedMuonStep(P[:nm], G, M, emas=E[:nm], workspace=workspace)
         workspace = muon.workspace
         states.append((muon, ms.PreparedEma(E[nm:], P[nm:]), ms.PreparedAdamW(P[nm:], AG, AM, AV, emas=E[nm:])))
+        if r == 0:
+            swap_lists = (E, P)
     stream = torch.cuda.current_stream(dev)
     turn = [0]
 
@@ -516,6 +518,24 @@ def main():
     out["full_optimizer_step"] = {"steps_per_s": round(1.0 / full_el, 2), "ms_per_step": round(full_el * 1e3, 4),
                                   "what": "muon_step on the 66 matrices (EMA fused) + adamw_step on the 121 other "
                                           "tensors (EMA fused)"}
+    # EMA swap-in over all 187 tensors (read and write both buffers: 16 B per parameter)
+    sw_e, sw_p = swap_lists
+    for _ in range(3):
+        ms.ema_swap(sw_e, sw_p, stream=stream)
+    torch.cuda.synchronize()
+    ms.profile_read(reset=True)
+    ms.profile_enable(True)
+    for _ in range(args.steps):
+        ms.ema_swap(sw_e, sw_p, stream=stream)
+    torch.cuda.synchronize()
+    ms.profile_enable(False)
+    sprof = ms.profile_read(reset=True)["swap"]
+    sw_us = sprof[1] / args.steps * 1e3
+    sw_bytes = 16.0 * w.n_params
+    out["ema_swap"] = {"tensors": len(sw_e), "elements": w.n_params, "us_per_call": round(sw_us, 3),
+                       "launches_per_call": sprof[0] / args.steps, "algorithmic_bytes_per_call": sw_bytes,
+                       "gbs": round(sw_bytes / (sw_us * 1e-6) / 1e9, 1),
+                       "frac_of_hbm_peak": round(sw_bytes / (sw_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     print(f"[bench] adamw {out['adamw']['us_per_call']} us per call; full optimizer step "
           f"{out['full_optimizer_step']['steps_per_s']} steps/s", flush=True)
     if not args.no_other_configs:

@@ -60,7 +60,13 @@
 #define NS_TRANSPOSE_READ 1  // bf16 update reads X through ds_read_b64_tr_b16
 #endif
 #ifndef NS_SYM_KGROUPS
-#define NS_SYM_KGROUPS 1     // Gram and square run with two K groups per workgroup
+#define NS_SYM_KGROUPS 1     // Gram and square run with two K groups per workgroup ...
+#endif
+#ifndef NS_SYM_MIN_K_GRAM
+#define NS_SYM_MIN_K_GRAM 0  // ... when the launch's longest contraction is at least this
+#endif
+#ifndef NS_SYM_MIN_K_SQUARE
+#define NS_SYM_MIN_K_SQUARE 0
 #endif
 
 namespace muon {
@@ -1092,7 +1098,11 @@ hipError_t launch_sym(const NsArgs& a, hipStream_t s) {
 
 template <int PHASE>
 hipError_t launch_phase(const NsArgs& a, int precision, bool comp, hipStream_t s) {
-    if (NS_SYM_KGROUPS) {
+    // Two K groups pay off on long contractions; short ones keep the 4-wave
+    // kernel, whose smaller LDS lets the other lane's workgroups share the CU.
+    int k_extent = 0;
+    for (int g = 0; g < a.ngroups; ++g) k_extent = std::max(k_extent, PHASE == kGram ? a.g[g].N : a.g[g].M);
+    if (NS_SYM_KGROUPS && k_extent >= (PHASE == kGram ? NS_SYM_MIN_K_GRAM : NS_SYM_MIN_K_SQUARE)) {
         if (precision == kNsFp32) return launch_sym<PHASE, kNsFp32, false>(a, s);
         return comp ? launch_sym<PHASE, kNsBf16, true>(a, s) : launch_sym<PHASE, kNsBf16, false>(a, s);
     }

@@ -158,22 +158,26 @@ def kernel_model(w, fused=True):
     The NS phases run once per iteration (split over the lanes' launches); the
     last update carries the weight apply when `fused`, else the apply kernel
     does.  Per launch figures are these totals divided by the launches per
-    step.  Bytes count each operand once at its stored width: X is a bf16
-    hi + lo pair (4 B), A and B are bf16 (hi + lo for A), weights, gradients,
-    momenta and EMA shadows are fp32.  The matrices' EMA rides on the weight
+    step.  Bytes count each operand once at its stored width: X is a bf16 hi
+    plus a byte lo (3 B; a bf16 lo, 4 B, for compensated groups below a short
+    side of 192), A and B are bf16 (hi + lo for A), weights, gradients, momenta
+    and EMA shadows are fp32.  The matrices' EMA rides on the weight
     apply; the ema kernel covers the other parameters.
     """
     gram_f = sq_f = 0.0
     gram_b = sq_b = upd_b = upda_b = 0.0
     elems = 0
+    prep_b = 0.0
     for _, r, c in w.matrices:
         m, n = min(r, c), max(r, c)
+        xb = 3.0 if m >= 192 else 4.0            # X per element: bf16 hi + byte lo (base) or bf16 lo
         gram_f += 2.0 * m * m * n
         sq_f += 2.0 * m * m * m
         gram_b += 2.0 * m * n + 4.0 * m * m      # read X hi; write A hi + lo
         sq_b += 4.0 * m * m + 2.0 * m * m        # read A hi + lo; write B
-        upd_b += 8.0 * m * n + 2.0 * m * m       # read X hi + lo and B; write X hi + lo
-        upda_b += 20.0 * m * n + 2.0 * m * m     # read X hi + lo and B; read + write W and E
+        upd_b += 2 * xb * m * n + 2.0 * m * m    # read X hi + lo and B; write X hi + lo
+        upda_b += (xb + 16.0) * m * n + 2.0 * m * m  # read X hi + lo and B; read + write W and E
+        prep_b += (12.0 + xb) * r * c            # read G, M; write M', X0 hi + lo
         elems += r * c
     k = w.ns_steps
     plain_updates = k - 1 if fused else k
@@ -181,7 +185,7 @@ def kernel_model(w, fused=True):
         "ns_gram_bf16": {"flops": k * gram_f, "bytes": k * gram_b},                        # A = X X^T
         "ns_square_bf16": {"flops": k * sq_f, "bytes": k * sq_b},                          # B = b A + c A A
         "ns_update_bf16": {"flops": plain_updates * gram_f, "bytes": plain_updates * upd_b},  # X <- a X + B X
-        "prep": {"flops": 0.0, "bytes": 16.0 * elems},                   # read G, M; write M, X0 hi + lo
+        "prep": {"flops": 0.0, "bytes": prep_b},                         # read G, M; write M', X0 hi + lo
         "ema": {"flops": 0.0, "bytes": 12.0 * (w.n_params - elems)},     # read E, P; write E
     }
     if fused:

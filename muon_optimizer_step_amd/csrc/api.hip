@@ -341,6 +341,9 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
     float* rowsq = reinterpret_cast<float*>(ws + p.rowsq_base);
     const int prec = ns_precision == MUON_NS_FP32 ? kNsFp32 : kNsBf16;  // storage precision
     const size_t xe = prec == kNsBf16 ? 2 : 4;                           // bytes per X element
+    // bytes per element of X's lo plane: base-precision bf16 groups keep bytes
+    // (the NS kernels index that plane by element), the compensated ones bf16
+    auto lo_bytes = [&](const Group& G) -> size_t { return prec == kNsBf16 ? (G.comp ? 2 : 1) : xe; };
     hipError_t err = hipSuccess;
 
     // ---- lanes: the matrices are independent NS problems.  Shape groups go
@@ -468,7 +471,7 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
                 T.mom = x.momentum;
                 const size_t slot_off = (size_t)p.slot_of[i] * G.M * G.N * xe;
                 T.xh = ws + G.x_off[0] + slot_off;
-                T.xl = ws + G.xl_off[0] + slot_off;
+                T.xl = ws + G.xl_off[0] + (size_t)p.slot_of[i] * G.M * G.N * lo_bytes(G);
                 T.rowsq = rowsq + p.rowsq_off[i];
                 T.rows = x.rows;
                 T.cols = x.cols;
@@ -477,6 +480,7 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
                 T.n_pad = G.N;
                 T.vec = (x.cols % 4 == 0) && (reinterpret_cast<uintptr_t>(x.grad) % 16 == 0) &&
                         (reinterpret_cast<uintptr_t>(x.momentum) % 16 == 0);
+                T.lo8 = prec == kNsBf16 && !G.comp;
                 T.block_begin = blocks;
                 if (T.transposed) {
                     T.rb = transposed_rb(x.cols);
@@ -542,7 +546,7 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
                 NsGroup& D = a.g[a.ngroups++];
                 for (int b = 0; b < 2; ++b) {
                     D.x[b] = ws + G.x_off[b] + pt.s0 * xslot;
-                    D.xl[b] = ws + G.xl_off[b] + pt.s0 * xslot;
+                    D.xl[b] = ws + G.xl_off[b] + pt.s0 * (size_t)G.M * G.N * lo_bytes(G);
                 }
                 D.a_hi = ws + G.ah_off + pt.s0 * aslot;
                 D.a_lo = ws + G.al_off + pt.s0 * aslot;
@@ -606,7 +610,7 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
                 T.ema = x.ema;
                 const size_t slot_off = (size_t)p.slot_of[i] * G.M * G.N * xe;
                 T.xh = ws + G.x_off[final_buf] + slot_off;
-                T.xl = ws + G.xl_off[final_buf] + slot_off;
+                T.xl = ws + G.xl_off[final_buf] + (size_t)p.slot_of[i] * G.M * G.N * lo_bytes(G);
                 T.scale = reinterpret_cast<const float*>(ws + p.scale_base) + G.scale_begin + p.slot_of[i];
                 T.lr_s = lr_scale(x);
                 T.rows = x.rows;
@@ -614,6 +618,7 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
                 T.n_pad = G.N;
                 T.transposed = x.rows > x.cols;
                 T.vec = vec_ok(x);
+                T.lo8 = prec == kNsBf16 && !G.comp;
                 T.block_begin = blocks;
                 if (T.transposed) {
                     T.rb = transposed_rb(x.cols);

@@ -33,6 +33,27 @@ __device__ inline void split_bf16(float x, bf16& hi, bf16& lo) {
     lo = to_bf16(x - from_bf16(hi));
 }
 
+// Base-precision groups keep the low part of X as one signed byte per element
+// instead of a second bf16: lo = q * 2^(e - 15), e the unbiased exponent of hi
+// and |q| <= 127.  |x - hi| is at most half a bf16 ulp, 2^(e - 8), so q covers
+// it in steps of 2^(e - 15): hi + lo holds x to 2^-16 of its magnitude, as a
+// bf16 pair does, in 3 bytes instead of 4.
+__device__ inline float lo8_step(float hi) {
+    const uint32_t eb = (__builtin_bit_cast(uint32_t, hi) >> 23) & 0xFFu;
+    return eb < 16u ? 0.0f : __builtin_bit_cast(float, (eb - 15u) << 23);
+}
+__device__ inline uint32_t lo8_encode(float x, float hi) {
+    const uint32_t eb = (__builtin_bit_cast(uint32_t, hi) >> 23) & 0xFFu;
+    if (eb < 16u) return 0u;
+    const float inv = __builtin_bit_cast(float, (269u - eb) << 23);  // 2^(15 - e)
+    const float q = fminf(fmaxf(rintf((x - hi) * inv), -127.0f), 127.0f);
+    return (uint32_t)(int32_t)q & 0xFFu;
+}
+__device__ inline float lo8_decode(float hi, uint32_t byte) {
+    const int32_t q = (int32_t)(int8_t)(uint8_t)byte;
+    return fmaf((float)q, lo8_step(hi), hi);
+}
+
 __device__ inline uint32_t bf16_bits(bf16 x) { return (uint32_t)__builtin_bit_cast(uint16_t, x); }
 __device__ inline bf16 bits_bf16(uint32_t b) { return __builtin_bit_cast(bf16, (uint16_t)b); }
 

@@ -33,59 +33,81 @@ __device__ inline float momentum_u(float g, float m, float mu, int nesterov, flo
     return nesterov ? fmaf(mu, m_new, g) : m_new;
 }
 
+// X element stores and loads.  bf16: hi plane plus either a bf16 lo plane or,
+// for base-precision groups (lo8), a byte plane (see lo8_encode); fp32: one plane.
 template <int PREC>
-__device__ inline void store_x(void* xh, void* xl, size_t idx, float v) {
+__device__ inline void store_x(void* xh, void* xl, size_t idx, float v, bool lo8) {
     if (PREC == kNsBf16) {
-        bf16 h, l;
-        split_bf16(v, h, l);
+        const bf16 h = to_bf16(v);
         static_cast<bf16*>(xh)[idx] = h;
-        static_cast<bf16*>(xl)[idx] = l;
+        if (lo8) static_cast<uint8_t*>(xl)[idx] = (uint8_t)lo8_encode(v, from_bf16(h));
+        else static_cast<bf16*>(xl)[idx] = to_bf16(v - from_bf16(h));
     } else {
         static_cast<float*>(xh)[idx] = v;
     }
 }
 
 template <int PREC>
-__device__ inline float load_x(const void* xh, const void* xl, size_t idx) {
+__device__ inline float load_x(const void* xh, const void* xl, size_t idx, bool lo8) {
     if (PREC == kNsBf16) {
-        return from_bf16(static_cast<const bf16*>(xh)[idx]) + from_bf16(static_cast<const bf16*>(xl)[idx]);
+        const float h = from_bf16(static_cast<const bf16*>(xh)[idx]);
+        if (lo8) return lo8_decode(h, static_cast<const uint8_t*>(xl)[idx]);
+        return h + from_bf16(static_cast<const bf16*>(xl)[idx]);
     } else {
         return static_cast<const float*>(xh)[idx];
     }
 }
 
-// Four consecutive X elements (8-byte aligned in bf16, 16 in fp32).
+// Four consecutive X elements (idx a multiple of 4).
 template <int PREC>
-__device__ inline void store_x4(void* xh, void* xl, size_t idx, float4 v) {
+__device__ inline void store_x4(void* xh, void* xl, size_t idx, float4 v, bool lo8) {
     if (PREC == kNsBf16) {
-        bf16 h[4], l[4];
-        split_bf16(v.x, h[0], l[0]);
-        split_bf16(v.y, h[1], l[1]);
-        split_bf16(v.z, h[2], l[2]);
-        split_bf16(v.w, h[3], l[3]);
-        u32x2 ph, pl;
+        const float x[4] = {v.x, v.y, v.z, v.w};
+        bf16 h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = to_bf16(x[e]);
+        u32x2 ph;
         ph.x = bf16_bits(h[0]) | (bf16_bits(h[1]) << 16);
         ph.y = bf16_bits(h[2]) | (bf16_bits(h[3]) << 16);
-        pl.x = bf16_bits(l[0]) | (bf16_bits(l[1]) << 16);
-        pl.y = bf16_bits(l[2]) | (bf16_bits(l[3]) << 16);
         *reinterpret_cast<u32x2*>(static_cast<bf16*>(xh) + idx) = ph;
-        *reinterpret_cast<u32x2*>(static_cast<bf16*>(xl) + idx) = pl;
+        if (lo8) {
+            uint32_t q = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) q |= lo8_encode(x[e], from_bf16(h[e])) << (8 * e);
+            *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(xl) + idx) = q;
+        } else {
+            bf16 l[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) l[e] = to_bf16(x[e] - from_bf16(h[e]));
+            u32x2 pl;
+            pl.x = bf16_bits(l[0]) | (bf16_bits(l[1]) << 16);
+            pl.y = bf16_bits(l[2]) | (bf16_bits(l[3]) << 16);
+            *reinterpret_cast<u32x2*>(static_cast<bf16*>(xl) + idx) = pl;
+        }
     } else {
         *reinterpret_cast<float4*>(static_cast<float*>(xh) + idx) = v;
     }
 }
 
 template <int PREC>
-__device__ inline float4 load_x4(const void* xh, const void* xl, size_t idx) {
+__device__ inline float4 load_x4(const void* xh, const void* xl, size_t idx, bool lo8) {
     if (PREC == kNsBf16) {
         const u32x2 h = *reinterpret_cast<const u32x2*>(static_cast<const bf16*>(xh) + idx);
-        const u32x2 l = *reinterpret_cast<const u32x2*>(static_cast<const bf16*>(xl) + idx);
-        float4 r;
-        r.x = from_bf16(bits_bf16(h.x & 0xFFFFu)) + from_bf16(bits_bf16(l.x & 0xFFFFu));
-        r.y = from_bf16(bits_bf16(h.x >> 16)) + from_bf16(bits_bf16(l.x >> 16));
-        r.z = from_bf16(bits_bf16(h.y & 0xFFFFu)) + from_bf16(bits_bf16(l.y & 0xFFFFu));
-        r.w = from_bf16(bits_bf16(h.y >> 16)) + from_bf16(bits_bf16(l.y >> 16));
-        return r;
+        const float hf[4] = {from_bf16(bits_bf16(h.x & 0xFFFFu)), from_bf16(bits_bf16(h.x >> 16)),
+                             from_bf16(bits_bf16(h.y & 0xFFFFu)), from_bf16(bits_bf16(h.y >> 16))};
+        float r[4];
+        if (lo8) {
+            const uint32_t q = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(xl) + idx);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = lo8_decode(hf[e], q >> (8 * e));
+        } else {
+            const u32x2 l = *reinterpret_cast<const u32x2*>(static_cast<const bf16*>(xl) + idx);
+            r[0] = hf[0] + from_bf16(bits_bf16(l.x & 0xFFFFu));
+            r[1] = hf[1] + from_bf16(bits_bf16(l.x >> 16));
+            r[2] = hf[2] + from_bf16(bits_bf16(l.y & 0xFFFFu));
+            r[3] = hf[3] + from_bf16(bits_bf16(l.y >> 16));
+        }
+        return make_float4(r[0], r[1], r[2], r[3]);
     } else {
         return *reinterpret_cast<const float4*>(static_cast<const float*>(xh) + idx);
     }
@@ -215,18 +237,18 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepArgs a) {
             float rs;
             if (T.vec && T.cols <= 4 * kWave * RV) {
                 rs = process_row_regs<RV>(g, m, T.cols, a.mu, a.nesterov, a.row_norm, lane,
-                                          [&](int j, float4 r) { store_x4<PREC>(T.xh, T.xl, xrow + j, r); });
+                                          [&](int j, float4 r) { store_x4<PREC>(T.xh, T.xl, xrow + j, r, T.lo8); });
                 const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-                for (int j = T.cols + 4 * lane; j < T.n_pad; j += 4 * kWave) store_x4<PREC>(T.xh, T.xl, xrow + j, z);
+                for (int j = T.cols + 4 * lane; j < T.n_pad; j += 4 * kWave) store_x4<PREC>(T.xh, T.xl, xrow + j, z, T.lo8);
             } else {
                 rs = process_row(g, m, T.cols, T.vec, a.mu, a.nesterov, a.row_norm, lane,
-                                 [&](int j, float r) { store_x<PREC>(T.xh, T.xl, xrow + j, r); });
-                for (int j = T.cols + lane; j < T.n_pad; j += kWave) store_x<PREC>(T.xh, T.xl, xrow + j, 0.f);
+                                 [&](int j, float r) { store_x<PREC>(T.xh, T.xl, xrow + j, r, T.lo8); });
+                for (int j = T.cols + lane; j < T.n_pad; j += kWave) store_x<PREC>(T.xh, T.xl, xrow + j, 0.f, T.lo8);
             }
             if (lane == 0) T.rowsq[row] = rs;
         } else {
             const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-            for (int j = 4 * lane; j < T.n_pad; j += 4 * kWave) store_x4<PREC>(T.xh, T.xl, xrow + j, z);
+            for (int j = 4 * lane; j < T.n_pad; j += 4 * kWave) store_x4<PREC>(T.xh, T.xl, xrow + j, z, T.lo8);
         }
         return;
     }
@@ -272,7 +294,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepArgs a) {
                 v.z = lds_rows[(size_t)(rr + 2) * pitch + j];
                 v.w = lds_rows[(size_t)(rr + 3) * pitch + j];
             }
-            store_x4<PREC>(T.xh, T.xl, (size_t)j * ld + row0 + rr, v);
+            store_x4<PREC>(T.xh, T.xl, (size_t)j * ld + row0 + rr, v, T.lo8);
         }
     } else {
         const int items = T.m_pad * rb;
@@ -280,7 +302,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepArgs a) {
             const int j = it / rb;
             const int rr = it - j * rb;
             const float v = (j < T.cols) ? lds_rows[(size_t)rr * pitch + j] : 0.f;
-            store_x<PREC>(T.xh, T.xl, (size_t)j * ld + row0 + rr, v);
+            store_x<PREC>(T.xh, T.xl, (size_t)j * ld + row0 + rr, v, T.lo8);
         }
     }
 }
@@ -329,7 +351,7 @@ __global__ __launch_bounds__(256) void apply_kernel(const ApplyArgs a) {
             float4* o4 = reinterpret_cast<float4*>(out);
             float4* e4 = reinterpret_cast<float4*>(ema);
             for (int j = lane; j < T.cols / 4; j += kWave) {
-                float4 o = load_x4<PREC>(T.xh, T.xl, xrow + 4 * j);
+                float4 o = load_x4<PREC>(T.xh, T.xl, xrow + 4 * j, T.lo8);
                 o.x *= fac; o.y *= fac; o.z *= fac; o.w *= fac;
                 float4 wv = w4[j];
                 wv.x = fmaf(-lr_s, o.x, keep * wv.x);
@@ -349,7 +371,7 @@ __global__ __launch_bounds__(256) void apply_kernel(const ApplyArgs a) {
             }
         } else {
             for (int j = lane; j < T.cols; j += kWave) {
-                const float o = fac * load_x<PREC>(T.xh, T.xl, xrow + j);
+                const float o = fac * load_x<PREC>(T.xh, T.xl, xrow + j, T.lo8);
                 const float wv = fmaf(-lr_s, o, keep * w[j]);
                 w[j] = wv;
                 if (out) out[j] = o;
@@ -370,7 +392,7 @@ __global__ __launch_bounds__(256) void apply_kernel(const ApplyArgs a) {
         for (int it = threadIdx.x; it < items; it += blockDim.x) {
             const int j = it / rq;
             const int rr = 4 * (it - j * rq);
-            const float4 v = load_x4<PREC>(T.xh, T.xl, (size_t)j * ld + row0 + rr);
+            const float4 v = load_x4<PREC>(T.xh, T.xl, (size_t)j * ld + row0 + rr, T.lo8);
             lds_o[(size_t)(rr + 0) * pitch + j] = fac * v.x;
             lds_o[(size_t)(rr + 1) * pitch + j] = fac * v.y;
             lds_o[(size_t)(rr + 2) * pitch + j] = fac * v.z;
@@ -381,7 +403,7 @@ __global__ __launch_bounds__(256) void apply_kernel(const ApplyArgs a) {
         for (int it = threadIdx.x; it < items; it += blockDim.x) {
             const int j = it / rb;
             const int rr = it - j * rb;
-            lds_o[(size_t)rr * pitch + j] = fac * load_x<PREC>(T.xh, T.xl, (size_t)j * ld + row0 + rr);
+            lds_o[(size_t)rr * pitch + j] = fac * load_x<PREC>(T.xh, T.xl, (size_t)j * ld + row0 + rr, T.lo8);
         }
     }
     __syncthreads();

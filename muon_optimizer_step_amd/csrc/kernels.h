@@ -11,7 +11,7 @@
 namespace muon {
 
 constexpr int kMaxGroups = 12;    // NS shape groups per NS launch
-constexpr int kPrepChunk = 52;    // tensors per prep / apply launch
+constexpr int kPrepChunk = 50;    // tensors per prep launch
 constexpr int kFrobChunk = 256;   // matrices per Frobenius-scale launch
 constexpr int kEmaChunk = 112;    // tensors per EMA launch
 constexpr int kRowsPerWaveBlock = 4;  // stored rows per workgroup when no transpose is needed
@@ -32,6 +32,7 @@ struct PrepTensor {
     int rb;          // stored rows per workgroup
     int block_begin; // first workgroup of this tensor
     int vec;         // grad/mom 16-byte aligned and cols % 4 == 0
+    int lo8;         // bf16: the lo plane holds bytes (base-precision group)
 };
 struct PrepArgs {
     PrepTensor t[kPrepChunk];
@@ -109,8 +110,9 @@ struct ApplyTensor {
     int rb;
     int block_begin;
     int vec;             // param/out/ema 16-byte aligned and cols % 4 == 0
+    int lo8;             // bf16: the lo plane holds bytes (base-precision group)
 };
-constexpr int kApplyChunk = 46;    // tensors per apply launch
+constexpr int kApplyChunk = 44;    // tensors per apply launch
 struct ApplyArgs {
     ApplyTensor t[kApplyChunk];
     int n;

@@ -9,11 +9,14 @@
 //     X <- a X + B X       (kUpdate, m x n, contraction over m)
 // with X short-side-first (m <= n).
 //
-// bf16 numerics.  X is kept to ~16 significant bits as two bf16 planes
-// (hi = rne(X), lo = rne(X - hi)); MFMA operands are bf16 and accumulate in
-// fp32.  A is split the same way and A A is formed as hi*hi + hi*lo + lo*hi,
-// because the plain bf16 square loses the small singular directions that the
-// iteration amplifies; the a X term always uses hi + lo.
+// bf16 numerics.  X is kept to ~16 significant bits as hi = rne(X) in bf16
+// plus its remainder: one byte per element in units of 2^-15 of hi's binade
+// for the base groups (lo8_encode), a second bf16 plane for the compensated
+// ones, whose products use it as an MFMA operand.  MFMA operands are bf16 and
+// accumulate in fp32.  A is split into bf16 hi + lo planes and A A is formed
+// as hi*hi + hi*lo + lo*hi, because the plain bf16 square loses the small
+// singular directions that the iteration amplifies; the a X term always uses
+// hi + lo.
 //   base:        A = Xh Xh^T,  B X = Bh Xh
 //   compensated: A = Xh Xh^T + Xh Xl^T + Xl Xh^T,  B X = Bh Xh + Bl Xh + Bh Xl
 // The base products keep the error within 2e-2 of float64 once the short side
@@ -338,6 +341,21 @@ __device__ inline void store8(void* hi, void* lo, size_t idx, const float* v) {
     }
 }
 
+// Store 8 X values as a bf16 hi plane and a byte lo plane (lo8_encode).
+__device__ inline void store8_lo8(void* hi, void* lo, size_t idx, const float* v) {
+    u32x4 wh;
+    u32x2 wl = {0u, 0u};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const bf16 h0 = to_bf16(v[2 * p]), h1 = to_bf16(v[2 * p + 1]);
+        wh[p] = bf16_bits(h0) | (bf16_bits(h1) << 16);
+        wl[p / 2] |= (lo8_encode(v[2 * p], from_bf16(h0)) | (lo8_encode(v[2 * p + 1], from_bf16(h1)) << 8))
+                     << (16 * (p % 2));
+    }
+    *reinterpret_cast<u32x4*>(static_cast<bf16*>(hi) + idx) = wh;
+    *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(lo) + idx) = wl;
+}
+
 // Fused weight update for up to 8 consecutive stored elements starting at idx:
 // W' = keep*W - lr_s*O, the optional copy of O, and the optional weight EMA
 // E' = d*E + (1-d)*W'.  apply_load fetches W (and E) early, into registers, so
@@ -620,8 +638,11 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
     float* stage = reinterpret_cast<float*>(lds);
     // Base bf16 update: the lo plane of X for both halves is fetched before the
     // accumulators are staged, so one memory latency overlaps the LDS work.
+    // Base-precision bf16 updates carry X's low part as bytes (lo8_encode).
+    constexpr bool kLo8 = (PHASE == kUpdate) && (PREC == kNsBf16) && !COMP;
     constexpr bool kPreXl = kKeep && !kSplit && (NS_PREFETCH_XL != 0);
-    u32x4 xl_pre[2][4];
+    static_assert(!kPreXl || kLo8, "the prefetched lo plane is the byte plane");
+    u32x2 xl_pre[2][4];
     if constexpr (kPreXl) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -629,7 +650,7 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
             for (int p = 0; p < 4; ++p) {
                 const size_t idx = xplane + (size_t)(job.ti * kTile + h * 64 + threadIdx.x / 16 + 16 * p) * N +
                                    job.tj * kTile + 8 * (threadIdx.x % 16);
-                xl_pre[h][p] = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(G.xl[src]) + idx);
+                xl_pre[h][p] = *reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(G.xl[src]) + idx);
             }
     }
     const float s = G.scale[job.slot];
@@ -715,23 +736,28 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
                 store8<PREC>(static_cast<T*>(G.b) + aplane, COMP ? static_cast<T*>(G.b_lo) + aplane : nullptr, idx, v);
             } else {
                 const size_t idx = xplane + (size_t)(row_base + lr) * N + job.tj * kTile + lc;
-                float xh[8], xl[8];
-                if constexpr (kKeep) {
-                    unpack8(keep_h[h][p], xh);
-                    if constexpr (kSplit) unpack8(keep_l[h][p], xl);
-                    else if constexpr (kPreXl) unpack8(xl_pre[h][p], xl);
+                float xh[8], xl[8], x[8];
+                if constexpr (kKeep) unpack8(keep_h[h][p], xh);
+                else load8<PREC>(G.x[src], idx, xh);
+                if constexpr (kLo8) {
+                    const u32x2 q = kPreXl ? xl_pre[h][p]
+                                           : *reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(G.xl[src]) + idx);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = lo8_decode(xh[e], q[e / 4] >> (8 * (e % 4)));
+                } else if constexpr (PREC == kNsBf16) {
+                    if constexpr (kKeep && kSplit) unpack8(keep_l[h][p], xl);
                     else load8<PREC>(G.xl[src], idx, xl);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = xh[e] + xl[e];
                 } else {
-                    load8<PREC>(G.x[src], idx, xh);
-                    if constexpr (PREC == kNsBf16) load8<PREC>(G.xl[src], idx, xl);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = xh[e];
                 }
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float x = (PREC == kNsBf16) ? xh[e] + xl[e] : xh[e];
-                    v[e] = sc * fmaf(args.a, x, v[e]);
-                }
+                for (int e = 0; e < 8; ++e) v[e] = sc * fmaf(args.a, x[e], v[e]);
                 if (!FUSE) {
-                    store8<PREC>(G.x[src ^ 1], G.xl[src ^ 1], idx, v);
+                    if constexpr (kLo8) store8_lo8(G.x[src ^ 1], G.xl[src ^ 1], idx, v);
+                    else store8<PREC>(G.x[src ^ 1], G.xl[src ^ 1], idx, v);
                 } else if (!(args.apply[G.apply_begin + job.slot].flags & kApplyTransposed)) {
                     // X row = stored row, X column = stored column
                     const FusedApply& F = args.apply[G.apply_begin + job.slot];

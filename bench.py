@@ -64,7 +64,7 @@ def _kernel_key(name: str) -> str:
         if phase == 2 and fuse:
             base = "ns_update_apply"
         return base + ("_fp32" if prec == 1 else ("_bf16x3" if comp else "_bf16"))
-    for k in ("prep_kernel", "apply_kernel", "ema_kernel", "frob_kernel", "adamw_kernel"):
+    for k in ("prep_kernel", "apply_kernel", "ema_kernel", "frob_kernel", "adamw_kernel", "swap_kernel"):
         if k in name:
             return k.replace("_kernel", "")
     return "copy" if "copyBuffer" in name else name

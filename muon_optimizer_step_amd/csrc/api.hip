@@ -95,15 +95,11 @@ hipError_t timed_launch(const char* name, hipStream_t s, F launch) {
 }
 
 // ------------------------------------------------------------- NS lanes
-// The matrices are independent NS problems.  Their parts (shape groups, split
-// where one would overfill a lane) are spread over up to
-// kLanes streams (the caller's stream and internal non-blocking streams of
+// The matrices are independent NS problems.  Their shape groups are spread
+// over up to kLanes streams (the caller's stream and internal non-blocking streams of
 // default priority), forked from and joined back into the caller's stream with
 // events, so that short chains (small matrices) fill the compute units the
 // long ones leave idle.  Nothing waits on the host.
-#ifndef NS_SPLIT_GROUPS
-#define NS_SPLIT_GROUPS 0
-#endif
 #ifndef NS_LANES
 #define NS_LANES 2
 #endif
@@ -347,9 +343,8 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
     hipError_t err = hipSuccess;
 
     // ---- lanes: the matrices are independent NS problems.  Shape groups go
-    // to lanes longest first onto the least loaded lane (by NS flops); a group
-    // that would overfill its lane is split at a slot boundary into parts on
-    // several lanes.  Each lane runs prep -> frob -> NS iterations -> apply for
+    // to lanes longest first onto the least loaded lane (by NS flops), whole.
+    // Each lane runs prep -> frob -> NS iterations -> apply for
     // its own matrices on its own stream, so short chains fill the compute
     // units the long ones leave idle.
     const int ngroups = (int)p.groups.size();
@@ -361,30 +356,19 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
     {
         std::vector<double> per(ngroups);  // NS flops of one matrix
         std::vector<std::pair<double, int>> work;
-        double total = 0.0;
         for (int g = 0; g < ngroups; ++g) {
             const Group& G = p.groups[g];
             per[g] = 4.0 * G.M * G.M * (double)G.N + 2.0 * G.M * G.M * (double)G.M;
             work.push_back({per[g] * G.count, g});
-            total += per[g] * G.count;
         }
         std::sort(work.begin(), work.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
         std::vector<double> load(kLanes, 0.0);
-        const double target = total / kLanes;
         for (const auto& wg : work) {
             const int g = wg.second;
             const int count = p.groups[g].count;
-            for (int s0 = 0; s0 < count;) {
-                const int l = (int)(std::min_element(load.begin(), load.end()) - load.begin());
-                int take = count - s0;
-                if (NS_SPLIT_GROUPS && load[l] + take * per[g] > 1.05 * target) {
-                    const int fit = (int)((target - load[l]) / per[g]);
-                    if (fit >= 1 && fit < take) take = fit;
-                }
-                parts.push_back({g, s0, s0 + take, l});
-                load[l] += take * per[g];
-                s0 += take;
-            }
+            const int l = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+            parts.push_back({g, 0, count, l});
+            load[l] += count * per[g];
         }
     }
     int nlanes = 1;

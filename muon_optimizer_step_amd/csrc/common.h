@@ -43,11 +43,13 @@ __device__ inline float lo8_step(float hi) {
     return eb < 16u ? 0.0f : __builtin_bit_cast(float, (eb - 15u) << 23);
 }
 __device__ inline uint32_t lo8_encode(float x, float hi) {
+    // straight-line code (a select, not a branch, for the tiny binades)
     const uint32_t eb = (__builtin_bit_cast(uint32_t, hi) >> 23) & 0xFFu;
-    if (eb < 16u) return 0u;
-    const float inv = __builtin_bit_cast(float, (269u - eb) << 23);  // 2^(15 - e)
+    const uint32_t ebc = eb < 16u ? 16u : eb;
+    const float inv = __builtin_bit_cast(float, (269u - ebc) << 23);  // 2^(15 - e)
     const float q = fminf(fmaxf(rintf((x - hi) * inv), -127.0f), 127.0f);
-    return (uint32_t)(int32_t)q & 0xFFu;
+    const uint32_t code = (uint32_t)(int32_t)q & 0xFFu;
+    return eb < 16u ? 0u : code;
 }
 __device__ inline float lo8_decode(float hi, uint32_t byte) {
     const int32_t q = (int32_t)(int8_t)(uint8_t)byte;

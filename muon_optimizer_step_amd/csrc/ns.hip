@@ -41,37 +41,6 @@
 #include "common.h"
 #include "kernels.h"
 
-#ifndef NS_DOUBLE_BUFFER
-#define NS_DOUBLE_BUFFER 0   // 1: base kernels double-buffer their LDS stages (costs occupancy)
-#endif
-#ifndef NS_PREFETCH_XL
-#define NS_PREFETCH_XL 1     // bf16 update / square: fetch the epilogue's inputs before staging
-#endif
-#ifndef NS_UPDATE_COLMAJOR
-#define NS_UPDATE_COLMAJOR 1  // update jobs ordered by X column panel
-#endif
-#ifndef NS_WIDE_UPDATE
-#define NS_WIDE_UPDATE 0     // 1: the bf16 base update stages 256 bytes of K too
-#endif
-#ifndef NS_WIDE_STAGE
-#define NS_WIDE_STAGE 1      // bf16 base kernels stage 256 bytes of K per row
-#endif
-#ifndef NS_KEEP_X
-#define NS_KEEP_X 1          // bf16 update: the epilogue reuses the X rows its K loop loaded last
-#endif
-#ifndef NS_TRANSPOSE_READ
-#define NS_TRANSPOSE_READ 1  // bf16 update reads X through ds_read_b64_tr_b16
-#endif
-#ifndef NS_SYM_KGROUPS
-#define NS_SYM_KGROUPS 1     // Gram and square run with two K groups per workgroup ...
-#endif
-#ifndef NS_SYM_MIN_K_GRAM
-#define NS_SYM_MIN_K_GRAM 0  // ... when the launch's longest contraction is at least this
-#endif
-#ifndef NS_SYM_MIN_K_SQUARE
-#define NS_SYM_MIN_K_SQUARE 0
-#endif
-
 namespace muon {
 
 namespace {
@@ -95,13 +64,10 @@ constexpr int kStageBytes = 64 * kStagePitch * 4;  // half a tile (64 rows) of f
 __device__ inline int stage_col(int row, int col) { return col ^ (((row >> 3) & 7) << 3); }
 static_assert(kStageBytes <= 2 * Stage<128>::kSlot, "epilogue staging must fit in the operand LDS");
 
-// K bytes per LDS stage: 256 for the bf16 base Gram, whose long contraction
-// gains from fewer, larger stages (two 128-row slots still fit 2 workgroups per
-// CU), 128 otherwise.
-
-constexpr int ns_stage_bytes(int phase, int precision, bool comp) {
-    return (precision == kNsBf16 && !comp && NS_WIDE_STAGE != 0 &&
-            (phase == kGram || (phase == kUpdate && NS_WIDE_UPDATE != 0 && NS_TRANSPOSE_READ != 0))) ? 256 : 128;
+// K bytes per LDS stage of the Gram and square: 256 for the bf16 base Gram,
+// whose long contraction gains from fewer, larger stages, 128 otherwise.
+constexpr int ns_sym_stage_bytes(int phase, int precision, bool comp) {
+    return (precision == kNsBf16 && !comp && phase == kGram) ? 256 : 128;
 }
 
 template <int PREC> struct Elem;
@@ -149,39 +115,10 @@ struct NtLoader {
     }
 };
 
-// X[k][j] (j contiguous in memory) staged as LDS[j][k] so that K is contiguous
-// per lane for the MFMA B operand.  bf16: thread t reads 8 k-rows x 4 j
-// (8-byte loads, 256 contiguous bytes per half wave) and transposes in
-// registers with v_perm; fp32: 4 k-rows x 4 j (16-byte loads).
+// fp32 X[k][j] (j contiguous in memory) staged as LDS[j][k] so that K is
+// contiguous per lane for the MFMA B operand: thread t reads 4 k-rows x 4 j
+// (16-byte loads) and transposes in registers.
 template <int PREC> struct TLoader;
-
-template <> struct TLoader<kNsBf16> {
-    u32x2 v[8];
-    __device__ inline void load(const bf16* x, size_t ld, int k0, int j0) {
-        const int t = threadIdx.x;
-        const int jq = t % 32, kb = t / 32;
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-            v[r] = *reinterpret_cast<const u32x2*>(x + (size_t)(k0 + 8 * kb + r) * ld + j0 + 4 * jq);
-    }
-    __device__ inline void store(uint8_t* lds) const {
-        const int t = threadIdx.x;
-        const int jq = t % 32, kb = t / 32;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            // column c of the 8 x 4 block: element c of every k-row, two k per dword
-            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-            u32x4 w;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const uint32_t lo_row = (c < 2) ? v[2 * p].x : v[2 * p].y;
-                const uint32_t hi_row = (c < 2) ? v[2 * p + 1].x : v[2 * p + 1].y;
-                w[p] = __builtin_amdgcn_perm(hi_row, lo_row, sel);
-            }
-            *reinterpret_cast<u32x4*>(lds + (4 * jq + c) * Stage<128>::kPitch + kb * 16) = w;
-        }
-    }
-};
 
 template <> struct TLoader<kNsFp32> {
     floatx4 v[4];
@@ -270,13 +207,8 @@ __device__ inline bool decode_job(const NsArgs& args, Job& j) {
         const int per = tm * tn;
         j.slot = local / per;
         const int t = local - j.slot * per;
-        if (NS_UPDATE_COLMAJOR) {
-            j.tj = t / tm;
-            j.ti = t - j.tj * tm;
-        } else {
-            j.ti = t / tn;
-            j.tj = t - j.ti * tn;
-        }
+        j.tj = t / tm;
+        j.ti = t - j.tj * tm;
     } else {
         const int per = tm * (tm + 1) / 2;
         j.slot = local / per;
@@ -420,73 +352,44 @@ __device__ inline void apply_store(const FusedApply& F, size_t idx, int count, c
     }
 }
 
-template <int PHASE, int PREC, bool COMP, bool FUSE>
-__global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
+// The update X' = s (a X + B X), s the Frobenius scale on the first iteration
+// and 1 after: one 128 x 128 tile of X' per workgroup, 4 waves of 64 x 64.  The
+// rows ti*128 .. +127 of B (K contiguous) are the A operand and the column
+// panel tj*128 .. +127 of X the B operand.  With FUSE, the last iteration
+// writes W' = keep W - lr_s X' (and the EMA) instead of X'.
+template <int PREC, bool COMP, bool FUSE>
+__global__ __launch_bounds__(kThreads, (PREC == kNsBf16 && !COMP && !FUSE) ? 3 : 1) void ns_update_kernel(
+    const NsArgs args) {
     typedef typename Elem<PREC>::T T;
     // operands carry a lo plane (and the MFMAs run hi*hi + hi*lo + lo*hi)
-    constexpr bool kSplit = (PREC == kNsBf16) && (PHASE == kSquare || COMP);
-    constexpr bool kTr = (PHASE == kUpdate) && (PREC == kNsBf16) && (NS_TRANSPOSE_READ != 0);
-    constexpr int kRB = ns_stage_bytes(PHASE, PREC, COMP);   // K bytes per stage per row
-    constexpr int kBK = kRB / (int)sizeof(T);                 // K elements per stage
+    constexpr bool kSplit = (PREC == kNsBf16) && COMP;
+    // bf16 keeps the X tile in its natural [k][j] layout and reads it with
+    // transposing LDS loads; fp32 transposes into LDS
+    constexpr bool kTr = PREC == kNsBf16;
+    constexpr int kRB = 128;                      // K bytes per stage per row
+    constexpr int kBK = kRB / (int)sizeof(T);     // K elements per stage
     constexpr int kSlot = Stage<kRB>::kSlot;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     Job job;
-    if (!decode_job<PHASE>(args, job)) return;
+    if (!decode_job<kUpdate>(args, job)) return;
     const NsGroup& G = args.g[job.g];
     const int M = G.M, N = G.N;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int wm = wave >> 1, wn = wave & 1;
-    const bool diag = (PHASE != kUpdate) && job.ti == job.tj;
-
     const size_t xplane = (size_t)job.slot * M * N;
     const size_t aplane = (size_t)job.slot * M * M;
     const int src = args.src;
+    const int K = M;
 
-    // LDS operand tiles per stage: [0] hi of the A-side rows, [1] hi of the
-    // B-side rows, [2] / [3] the lo planes.  On diagonal tiles both sides are
-    // the same rows.  The bf16 update keeps its X tile in natural [k][j] layout
-    // and reads it with transposing LDS loads.
-    constexpr int kStages = (kSplit || NS_DOUBLE_BUFFER == 0) ? 1 : 2;
-    constexpr int kStageTiles = kSplit ? 4 : 2;
-    auto tile = [&](int stage, int which) -> uint8_t* {
-        if (diag && which == 1) which = 0;
-        if (diag && which == 3) which = 2;
-        return lds + (stage * kStageTiles + which) * kSlot;
-    };
+    // LDS operand tiles: [0] B hi rows, [1] X hi, [2] / [3] their lo planes
+    auto tile = [&](int which) -> uint8_t* { return lds + which * kSlot; };
 
-    const uint8_t *ga = nullptr, *gb = nullptr, *gal = nullptr, *gbl = nullptr;
-    const T *xb = nullptr, *xbl = nullptr;  // update: B-side X planes
-    size_t ld_bytes = 0;
-    int K = 0;
-    if (PHASE == kGram) {
-        const T* xh = static_cast<const T*>(G.x[src]) + xplane;
-        const T* xl = static_cast<const T*>(G.xl[src]) + xplane;
-        ld_bytes = (size_t)N * sizeof(T);
-        ga = reinterpret_cast<const uint8_t*>(xh + (size_t)job.ti * kTile * N);
-        gb = reinterpret_cast<const uint8_t*>(xh + (size_t)job.tj * kTile * N);
-        gal = reinterpret_cast<const uint8_t*>(xl + (size_t)job.ti * kTile * N);
-        gbl = reinterpret_cast<const uint8_t*>(xl + (size_t)job.tj * kTile * N);
-        K = N;
-    } else if (PHASE == kSquare) {
-        const T* ah = static_cast<const T*>(G.a_hi) + aplane;
-        const T* al = static_cast<const T*>(G.a_lo) + aplane;
-        ld_bytes = (size_t)M * sizeof(T);
-        ga = reinterpret_cast<const uint8_t*>(ah + (size_t)job.ti * kTile * M);
-        gb = reinterpret_cast<const uint8_t*>(ah + (size_t)job.tj * kTile * M);
-        gal = reinterpret_cast<const uint8_t*>(al + (size_t)job.ti * kTile * M);
-        gbl = reinterpret_cast<const uint8_t*>(al + (size_t)job.tj * kTile * M);
-        K = M;
-    } else {
-        const T* bh = static_cast<const T*>(G.b) + aplane;
-        const T* bl = static_cast<const T*>(G.b_lo) + aplane;
-        ld_bytes = (size_t)M * sizeof(T);
-        ga = reinterpret_cast<const uint8_t*>(bh + (size_t)job.ti * kTile * M);
-        gal = reinterpret_cast<const uint8_t*>(bl + (size_t)job.ti * kTile * M);
-        xb = static_cast<const T*>(G.x[src]) + xplane;
-        xbl = static_cast<const T*>(G.xl[src]) + xplane;
-        K = M;
-    }
+    const size_t ld_bytes = (size_t)M * sizeof(T);
+    const uint8_t* ga = reinterpret_cast<const uint8_t*>(static_cast<const T*>(G.b) + aplane + (size_t)job.ti * kTile * M);
+    const uint8_t* gal = reinterpret_cast<const uint8_t*>(static_cast<const T*>(G.b_lo) + aplane + (size_t)job.ti * kTile * M);
+    const T* xb = static_cast<const T*>(G.x[src]) + xplane;
+    const T* xbl = static_cast<const T*>(G.xl[src]) + xplane;
 
     floatx16 acc[2][2];
 #pragma unroll
@@ -497,51 +400,38 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
             for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
     // Registers staging one K stage from global memory into LDS.
-    NtLoader<kRB> la[1], lb[1], lal[1], lbl[1];
-    TLoader<PREC> lt[1], ltl[1];
-    XLoader<kBK> lx[1], lxl[1];
-    auto issue = [&](int k0, int set) {
-        const int kbyte = k0 * (int)sizeof(T);
-        la[set].load(ga, ld_bytes, kbyte);
-        if (kSplit) lal[set].load(gal, ld_bytes, kbyte);
-        if (PHASE == kUpdate) {
-            if constexpr (kTr) {
-                lx[set].load(reinterpret_cast<const bf16*>(xb), (size_t)N, k0, job.tj * kTile);
-                if (kSplit) lxl[set].load(reinterpret_cast<const bf16*>(xbl), (size_t)N, k0, job.tj * kTile);
-            } else {
-                lt[set].load(xb, (size_t)N, k0, job.tj * kTile);
-                if (kSplit) ltl[set].load(xbl, (size_t)N, k0, job.tj * kTile);
-            }
-        } else if (!diag) {
-            lb[set].load(gb, ld_bytes, kbyte);
-            if (kSplit) lbl[set].load(gbl, ld_bytes, kbyte);
+    NtLoader<kRB> la, lal;
+    TLoader<kNsFp32> lt;
+    XLoader<kBK> lx, lxl;
+    auto issue = [&](int k0) {
+        la.load(ga, ld_bytes, k0 * (int)sizeof(T));
+        if (kSplit) lal.load(gal, ld_bytes, k0 * (int)sizeof(T));
+        if constexpr (kTr) {
+            lx.load(reinterpret_cast<const bf16*>(xb), (size_t)N, k0, job.tj * kTile);
+            if (kSplit) lxl.load(reinterpret_cast<const bf16*>(xbl), (size_t)N, k0, job.tj * kTile);
+        } else {
+            lt.load(reinterpret_cast<const float*>(xb), (size_t)N, k0, job.tj * kTile);
         }
     };
-    auto commit = [&](int stage, int set) {
-        la[set].store(tile(stage, 0));
-        if (kSplit) lal[set].store(tile(stage, 2));
-        if (PHASE == kUpdate) {
-            if constexpr (kTr) {
-                lx[set].store(tile(stage, 1));
-                if (kSplit) lxl[set].store(tile(stage, 3));
-            } else {
-                lt[set].store(tile(stage, 1));
-                if (kSplit) ltl[set].store(tile(stage, 3));
-            }
-        } else if (!diag) {
-            lb[set].store(tile(stage, 1));
-            if (kSplit) lbl[set].store(tile(stage, 3));
+    auto commit = [&]() {
+        la.store(tile(0));
+        if (kSplit) lal.store(tile(2));
+        if constexpr (kTr) {
+            lx.store(tile(1));
+            if (kSplit) lxl.store(tile(3));
+        } else {
+            lt.store(tile(1));
         }
     };
     auto bfrag = [&](const uint8_t* tb, int ni, int kc) -> u32x4 {
         if constexpr (kTr) return lds_frag_tr(tb, kc * 16, wn * 64 + ni * 32, lane);
         else return lds_frag<kRB>(tb, wn * 64 + ni * 32 + lane % 32, kc, lane);
     };
-    auto compute = [&](int stage) {
-        const uint8_t* t_a = tile(stage, 0);
-        const uint8_t* t_b = tile(stage, 1);
-        const uint8_t* t_al = tile(stage, 2);
-        const uint8_t* t_bl = tile(stage, 3);
+    auto compute = [&]() {
+        const uint8_t* t_a = tile(0);
+        const uint8_t* t_b = tile(1);
+        const uint8_t* t_al = tile(2);
+        const uint8_t* t_bl = tile(3);
 #pragma unroll
         for (int kc = 0; kc < kRB / 32; ++kc) {
             u32x4 fa[2], fb[2];
@@ -570,80 +460,49 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
         }
     };
 
-    // The update's own output rows ti*128 .. +127 of X pass through the K loop
-    // as the B operand.  The K loop of the update starts right after them and
-    // wraps around, so they are its last two stages; the XLoader thread
-    // mapping (row t/16 + 16q, columns 8(t%16)) is the epilogue's row mapping,
-    // so each thread keeps those registers instead of reloading X from HBM.
-    constexpr bool kKeep = kTr && (kStages == 1) && (NS_KEEP_X != 0);
-    constexpr int kOwnStages = kTile / kBK;   // stages holding the tile's own rows (1 or 2)
+    // The tile's own rows ti*128 .. +127 of X pass through the K loop as the B
+    // operand.  With bf16 the K loop starts right after them and wraps around,
+    // so they are its last two stages; the XLoader thread mapping (row t/16 +
+    // 16q, columns 8(t%16)) is the epilogue's row mapping, so each thread keeps
+    // those registers instead of reloading X from HBM.
+    constexpr bool kKeep = kTr;
+    static_assert(!kKeep || kTile == 2 * kBK, "the own rows are the last two stages");
     u32x4 keep_h[2][4], keep_l[2][4];
-    const int nk = K / kBK;
+    const int nk = K / kBK;   // >= 2: K is padded to a multiple of 128
     auto kstart = [&](int kt) -> int {
         if constexpr (kKeep) return ((job.ti + 1) * kTile + kt * kBK) % K;
         else return kt * kBK;
     };
-    auto capture = [&](int kt) {
-        if constexpr (kKeep && kOwnStages == 2) {
-            if (kt == nk - 2) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) { keep_h[0][q] = lx[0].r[q]; if (kSplit) keep_l[0][q] = lxl[0].r[q]; }
-            }
-        }
-    };
-
-    if constexpr (kStages == 2) {
-        // LDS double buffer: one barrier per stage; the global loads of stage
-        // kt+2 are in flight while stage kt+1 waits in LDS and kt computes.
-        issue(kstart(0), 0);
-        commit(0, 0);
-        if (nk > 1) issue(kstart(1), 0);
+    issue(kstart(0));
+    for (int kt = 0; kt < nk; ++kt) {
         __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
-            compute(kt & 1);
-            if (kt + 1 < nk) commit((kt + 1) & 1, 0);
-            if (kt + 2 < nk) issue(kstart(kt + 2), 0);
-            __syncthreads();
-        }
-    } else if (nk > 0) {
-        issue(kstart(0), 0);
-        for (int kt = 0; kt < nk; ++kt) {
-            __syncthreads();
-            commit(0, 0);
-            capture(kt);
-            __syncthreads();
-            if (kt + 1 < nk) issue(kstart(kt + 1), 0);
-            compute(0);
-        }
+        commit();
         if constexpr (kKeep) {
-            // the last stage: rows ti*128 + 64 .. +127, or the whole 128 rows
-            constexpr int base = (kOwnStages == 2) ? 0 : 4;
+            if (kt == nk - 2) {   // rows ti*128 .. +63
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                keep_h[1][q] = lx[0].r[base + q];
-                if (kSplit) keep_l[1][q] = lxl[0].r[base + q];
-                if (kOwnStages == 1) {
-                    keep_h[0][q] = lx[0].r[q];
-                    if (kSplit) keep_l[0][q] = lxl[0].r[q];
-                }
+                for (int q = 0; q < 4; ++q) { keep_h[0][q] = lx.r[q]; if (kSplit) keep_l[0][q] = lxl.r[q]; }
             }
         }
+        __syncthreads();
+        if (kt + 1 < nk) issue(kstart(kt + 1));
+        compute();
+    }
+    if constexpr (kKeep) {   // the last stage: rows ti*128 + 64 .. +127
+#pragma unroll
+        for (int q = 0; q < 4; ++q) { keep_h[1][q] = lx.r[q]; if (kSplit) keep_l[1][q] = lxl.r[q]; }
     }
 
     // ---------------------------------------------------------- epilogue
     // Two passes of 64 rows: the waves holding those rows park their fp32
     // accumulators in LDS, then all threads finish 8 consecutive columns of a
-    // row each with 16-byte global accesses, and symmetric outputs also write
-    // the mirrored tile from the staged columns.
+    // row each with 16-byte global accesses.
     float* stage = reinterpret_cast<float*>(lds);
-    // Base bf16 update: the lo plane of X for both halves is fetched before the
-    // accumulators are staged, so one memory latency overlaps the LDS work.
-    // Base-precision bf16 updates carry X's low part as bytes (lo8_encode).
-    constexpr bool kLo8 = (PHASE == kUpdate) && (PREC == kNsBf16) && !COMP;
-    constexpr bool kPreXl = kKeep && !kSplit && (NS_PREFETCH_XL != 0);
-    static_assert(!kPreXl || kLo8, "the prefetched lo plane is the byte plane");
+    // Base-precision bf16 updates carry X's low part as bytes (lo8_encode);
+    // that plane for both halves is fetched before the accumulators are
+    // staged, so one memory latency overlaps the LDS work.
+    constexpr bool kLo8 = (PREC == kNsBf16) && !COMP;
     u32x2 xl_pre[2][4];
-    if constexpr (kPreXl) {
+    if constexpr (kLo8) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -654,36 +513,24 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
             }
     }
     const float s = G.scale[job.slot];
-    const float sc = (PHASE == kGram) ? (args.first ? s * s : 1.0f) : (args.first ? s : 1.0f);
+    const float sc = args.first ? s : 1.0f;
     const int t = threadIdx.x;
+    const int fslot = G.apply_begin + job.slot;   // fused apply table entry
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+        const bool tall = FUSE && (args.apply[fslot].flags & kApplyTransposed);   // stored W is X^T
         const int row_base = job.ti * kTile + h * 64;
         // fused apply: W and E of this half's outputs are in flight while the
         // accumulators are staged (row pass mapping for stored rows = X rows,
-        // column pass mapping for tall matrices, whose stored W is X^T)
+        // column pass mapping for tall matrices)
         floatx4 w_pre[4][2], e_pre[4][2];
         if constexpr (FUSE) {
-            const FusedApply& F = args.apply[G.apply_begin + job.slot];
-            const bool tall = F.flags & kApplyTransposed;
+            const FusedApply& F = args.apply[fslot];
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 const int wr = tall ? job.tj * kTile + t / 8 + 32 * p : row_base + t / 16 + 16 * p;
                 const int wc = tall ? row_base + 8 * (t % 8) : job.tj * kTile + 8 * (t % 16);
                 if (wr < F.rows && wc < F.cols) apply_load(F, (size_t)wr * F.cols + wc, F.cols - wc, w_pre[p], e_pre[p]);
-            }
-        }
-        // the square's epilogue input (A hi and lo of this half) is in flight
-        // while the accumulators are staged
-        constexpr bool kPreA = (PHASE == kSquare) && (PREC == kNsBf16) && (NS_PREFETCH_XL != 0);
-        u32x4 a_pre[2][4];
-        if constexpr (kPreA) {
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const size_t idx = aplane + (size_t)(job.ti * kTile + h * 64 + threadIdx.x / 16 + 16 * p) * M +
-                                   job.tj * kTile + 8 * (threadIdx.x % 16);
-                a_pre[0][p] = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(G.a_hi) + idx);
-                a_pre[1][p] = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(G.a_lo) + idx);
             }
         }
         __syncthreads();
@@ -713,63 +560,36 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
             }
-            if (PHASE == kGram) {
-                const size_t idx = (size_t)(row_base + lr) * M + job.tj * kTile + lc;
+            const size_t idx = xplane + (size_t)(row_base + lr) * N + job.tj * kTile + lc;
+            float xh[8], xl[8], x[8];
+            if constexpr (kKeep) unpack8(keep_h[h][p], xh);
+            else load8<PREC>(G.x[src], idx, xh);
+            if constexpr (kLo8) {
+                const u32x2 q = xl_pre[h][p];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] *= sc;
-                store8<PREC>(static_cast<T*>(G.a_hi) + aplane, static_cast<T*>(G.a_lo) + aplane, idx, v);
-            } else if (PHASE == kSquare) {
-                const size_t idx = (size_t)(row_base + lr) * M + job.tj * kTile + lc;
-                float ah[8], al[8];
-                if constexpr (kPreA) {
-                    unpack8(a_pre[0][p], ah);
-                    unpack8(a_pre[1][p], al);
-                } else {
-                    load8<PREC>(static_cast<const T*>(G.a_hi) + aplane, idx, ah);
-                    if constexpr (PREC == kNsBf16) load8<PREC>(static_cast<const T*>(G.a_lo) + aplane, idx, al);
-                }
+                for (int e = 0; e < 8; ++e) x[e] = lo8_decode(xh[e], q[e / 4] >> (8 * (e % 4)));
+            } else if constexpr (PREC == kNsBf16) {
+                unpack8(keep_l[h][p], xl);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float a = (PREC == kNsBf16) ? ah[e] + al[e] : ah[e];
-                    v[e] = fmaf(args.b, a, args.c * v[e]);
-                }
-                store8<PREC>(static_cast<T*>(G.b) + aplane, COMP ? static_cast<T*>(G.b_lo) + aplane : nullptr, idx, v);
+                for (int e = 0; e < 8; ++e) x[e] = xh[e] + xl[e];
             } else {
-                const size_t idx = xplane + (size_t)(row_base + lr) * N + job.tj * kTile + lc;
-                float xh[8], xl[8], x[8];
-                if constexpr (kKeep) unpack8(keep_h[h][p], xh);
-                else load8<PREC>(G.x[src], idx, xh);
-                if constexpr (kLo8) {
-                    const u32x2 q = kPreXl ? xl_pre[h][p]
-                                           : *reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(G.xl[src]) + idx);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] = lo8_decode(xh[e], q[e / 4] >> (8 * (e % 4)));
-                } else if constexpr (PREC == kNsBf16) {
-                    if constexpr (kKeep && kSplit) unpack8(keep_l[h][p], xl);
-                    else load8<PREC>(G.xl[src], idx, xl);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] = xh[e] + xl[e];
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] = xh[e];
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = sc * fmaf(args.a, x[e], v[e]);
-                if (!FUSE) {
-                    if constexpr (kLo8) store8_lo8(G.x[src ^ 1], G.xl[src ^ 1], idx, v);
-                    else store8<PREC>(G.x[src ^ 1], G.xl[src ^ 1], idx, v);
-                } else if (!(args.apply[G.apply_begin + job.slot].flags & kApplyTransposed)) {
-                    // X row = stored row, X column = stored column
-                    const FusedApply& F = args.apply[G.apply_begin + job.slot];
-                    const int gi = row_base + lr, gj = job.tj * kTile + lc;
-                    if (gi < F.rows && gj < F.cols)
-                        apply_store(F, (size_t)gi * F.cols + gj, F.cols - gj, v, w_pre[p], e_pre[p], args.keep,
-                                    args.decay, args.one_minus_decay);
-                }
+                for (int e = 0; e < 8; ++e) x[e] = xh[e];
             }
-            if ((PHASE != kUpdate && !diag) ||
-                (PHASE == kUpdate && FUSE && (args.apply[G.apply_begin + job.slot].flags & kApplyTransposed))) {
-                // keep the final value for the mirrored write
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = sc * fmaf(args.a, x[e], v[e]);
+            if constexpr (!FUSE) {
+                if constexpr (kLo8) store8_lo8(G.x[src ^ 1], G.xl[src ^ 1], idx, v);
+                else store8<PREC>(G.x[src ^ 1], G.xl[src ^ 1], idx, v);
+            } else if (!tall) {
+                // X row = stored row, X column = stored column
+                const FusedApply& F = args.apply[fslot];
+                const int gi = row_base + lr, gj = job.tj * kTile + lc;
+                if (gi < F.rows && gj < F.cols)
+                    apply_store(F, (size_t)gi * F.cols + gj, F.cols - gj, v, w_pre[p], e_pre[p], args.keep,
+                                args.decay, args.one_minus_decay);
+            } else {
+                // keep the final value for the column pass
                 floatx4 a, b;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) { a[e] = v[e]; b[e] = v[4 + e]; }
@@ -777,10 +597,10 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
                 *reinterpret_cast<floatx4*>(sp + 4) = b;
             }
         }
-        if (PHASE == kUpdate && FUSE && (args.apply[G.apply_begin + job.slot].flags & kApplyTransposed)) {
+        if (tall) {
             __syncthreads();
             // stored W is X^T: W row tj*128 + c, columns row_base + 8*chunk .. +7
-            const FusedApply& F = args.apply[G.apply_begin + job.slot];
+            const FusedApply& F = args.apply[fslot];
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 const int chunk = t % 8;
@@ -793,24 +613,6 @@ __global__ __launch_bounds__(kThreads) void ns_kernel(const NsArgs args) {
                     apply_store(F, (size_t)wr * F.cols + wc, F.cols - wc, v, w_pre[p], e_pre[p], args.keep,
                                 args.decay, args.one_minus_decay);
                 }
-            }
-        }
-        if (PHASE != kUpdate && !diag) {
-            __syncthreads();
-            // mirror pass: output row tj*128 + c, columns row_base + 8*chunk .. +7
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int chunk = t % 8;
-                const int c = t / 8 + 32 * p;
-                float v[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = stage[(chunk * 8 + e) * kStagePitch + stage_col(chunk * 8 + e, c)];
-                const size_t idx = (size_t)(job.tj * kTile + c) * M + row_base + chunk * 8;
-                if (PHASE == kGram)
-                    store8<PREC>(static_cast<T*>(G.a_hi) + aplane, static_cast<T*>(G.a_lo) + aplane, idx, v);
-                else
-                    store8<PREC>(static_cast<T*>(G.b) + aplane, COMP ? static_cast<T*>(G.b_lo) + aplane : nullptr,
-                                 idx, v);
             }
         }
     }
@@ -834,7 +636,7 @@ __global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) 
     static_assert(PHASE == kGram || PHASE == kSquare, "symmetric phases only");
     typedef typename Elem<PREC>::T T;
     constexpr bool kSplit = (PREC == kNsBf16) && (PHASE == kSquare || COMP);
-    constexpr int kRB = ns_stage_bytes(PHASE, PREC, COMP);
+    constexpr int kRB = ns_sym_stage_bytes(PHASE, PREC, COMP);
     constexpr int kBK = kRB / (int)sizeof(T);
     constexpr int kSlot = Stage<kRB>::kSlot;
     constexpr int kStageTiles = kSplit ? 4 : 2;
@@ -906,7 +708,48 @@ __global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) 
             if (kSplit) lbl.store(tile(3));
         }
     };
+    // bf16 base: the fragments of chunk kc + 2 are read while the MFMAs of
+    // chunk kc run.  The scheduling groups (one fragment read after each MFMA)
+    // keep the compiler from moving the reads next to the MFMAs that use them.
+    auto compute_ahead = [&]() {
+        const uint8_t* t_a = tile(0);
+        const uint8_t* t_b = tile(1);
+        constexpr int kKC = kRB / 32, kDist = 2, kBufs = kDist + 1;
+        static_assert(kKC >= kDist, "at least kDist chunks per stage");
+        u32x4 f[kBufs][4];
+        auto read = [&](int kc, u32x4* d) {
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) d[mi] = lds_frag<kRB>(t_a, wm * 64 + mi * 32 + lane % 32, kc, lane);
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni) d[2 + ni] = lds_frag<kRB>(t_b, wn * 64 + ni * 32 + lane % 32, kc, lane);
+        };
+#pragma unroll
+        for (int kc = 0; kc < kDist; ++kc) read(kc, f[kc]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * kDist, 0);   // DS reads
+#pragma unroll
+        for (int kc = 0; kc < kKC; ++kc) {
+            if (kc + kDist < kKC) read(kc + kDist, f[(kc + kDist) % kBufs]);
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+                    mfma_chunk<PREC>(acc[mi][ni], f[kc % kBufs][mi], f[kc % kBufs][2 + ni]);
+            if (kc + kDist < kKC) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+                }
+            } else {
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            }
+        }
+    };
     auto compute = [&]() {
+        if constexpr (PREC == kNsBf16 && !kSplit) {
+            compute_ahead();
+            return;
+        }
         const uint8_t* t_a = tile(0);
         const uint8_t* t_b = tile(1);
         const uint8_t* t_al = tile(2);
@@ -963,7 +806,7 @@ __global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) 
     // ------------------------------------------------------- epilogue
     // thread tid -> rows tid/16 + 32p (p < 4) of the tile, columns 8*(tid%16) .. +7
     const int lc = 8 * (tid % 16);
-    constexpr bool kPreA = (PHASE == kSquare) && (PREC == kNsBf16) && (NS_PREFETCH_XL != 0);
+    constexpr bool kPreA = (PHASE == kSquare) && (PREC == kNsBf16);
     u32x4 a_pre[4][2];
     if constexpr (kPreA) {
 #pragma unroll
@@ -1082,30 +925,27 @@ __global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) 
     }
 }
 
-size_t ns_lds_bytes(int phase, int precision, bool comp) {
-    const bool split = precision == kNsBf16 && (phase == kSquare || comp);
-    const int stages = (split || NS_DOUBLE_BUFFER == 0) ? 1 : 2;
-    const int slot = ns_stage_bytes(phase, precision, comp) == 256 ? Stage<256>::kSlot : Stage<128>::kSlot;
-    return (size_t)(split ? 4 : 2) * stages * slot;
+size_t ns_update_lds_bytes(int precision, bool comp) {
+    return (size_t)((precision == kNsBf16 && comp) ? 4 : 2) * Stage<128>::kSlot;
 }
 
-template <int PHASE, int PREC, bool COMP, bool FUSE>
-hipError_t launch_one(const NsArgs& a, hipStream_t s) {
-    const size_t lds = ns_lds_bytes(PHASE, PREC, COMP);
+template <int PREC, bool COMP, bool FUSE>
+hipError_t launch_update(const NsArgs& a, hipStream_t s) {
+    const size_t lds = ns_update_lds_bytes(PREC, COMP);
     if (lds > 65536) {
         // more than the default 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU)
-        static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&ns_kernel<PHASE, PREC, COMP, FUSE>),
+        static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&ns_update_kernel<PREC, COMP, FUSE>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (attr != hipSuccess) return attr;
     }
     const int grid = (a.total_jobs + kXcds - 1) / kXcds * kXcds;
-    ns_kernel<PHASE, PREC, COMP, FUSE><<<grid, kThreads, lds, s>>>(a);
+    ns_update_kernel<PREC, COMP, FUSE><<<grid, kThreads, lds, s>>>(a);
     return hipGetLastError();
 }
 
 size_t ns_sym_lds_bytes(int phase, int precision, bool comp) {
     const bool split = precision == kNsBf16 && (phase == kSquare || comp);
-    const int slot = ns_stage_bytes(phase, precision, comp) == 256 ? Stage<256>::kSlot : Stage<128>::kSlot;
+    const int slot = ns_sym_stage_bytes(phase, precision, comp) == 256 ? Stage<256>::kSlot : Stage<128>::kSlot;
     return std::max((size_t)2 * (split ? 4 : 2) * slot, (size_t)kSymEpilogueBytes);
 }
 
@@ -1123,35 +963,24 @@ hipError_t launch_sym(const NsArgs& a, hipStream_t s) {
 }
 
 template <int PHASE>
-hipError_t launch_phase(const NsArgs& a, int precision, bool comp, hipStream_t s) {
-    // Two K groups pay off on long contractions; short ones keep the 4-wave
-    // kernel, whose smaller LDS lets the other lane's workgroups share the CU.
-    int k_extent = 0;
-    for (int g = 0; g < a.ngroups; ++g) k_extent = std::max(k_extent, PHASE == kGram ? a.g[g].N : a.g[g].M);
-    if (NS_SYM_KGROUPS && k_extent >= (PHASE == kGram ? NS_SYM_MIN_K_GRAM : NS_SYM_MIN_K_SQUARE)) {
-        if (precision == kNsFp32) return launch_sym<PHASE, kNsFp32, false>(a, s);
-        return comp ? launch_sym<PHASE, kNsBf16, true>(a, s) : launch_sym<PHASE, kNsBf16, false>(a, s);
-    }
-    if (precision == kNsFp32) return launch_one<PHASE, kNsFp32, false, false>(a, s);
-    return comp ? launch_one<PHASE, kNsBf16, true, false>(a, s) : launch_one<PHASE, kNsBf16, false, false>(a, s);
+hipError_t launch_sym_phase(const NsArgs& a, int precision, bool comp, hipStream_t s) {
+    if (precision == kNsFp32) return launch_sym<PHASE, kNsFp32, false>(a, s);
+    return comp ? launch_sym<PHASE, kNsBf16, true>(a, s) : launch_sym<PHASE, kNsBf16, false>(a, s);
 }
 
-template <>
-hipError_t launch_phase<kUpdate>(const NsArgs& a, int precision, bool comp, hipStream_t s) {
-    if (a.fuse_apply) {
-        if (precision == kNsFp32) return launch_one<kUpdate, kNsFp32, false, true>(a, s);
-        return comp ? launch_one<kUpdate, kNsBf16, true, true>(a, s) : launch_one<kUpdate, kNsBf16, false, true>(a, s);
-    }
-    if (precision == kNsFp32) return launch_one<kUpdate, kNsFp32, false, false>(a, s);
-    return comp ? launch_one<kUpdate, kNsBf16, true, false>(a, s) : launch_one<kUpdate, kNsBf16, false, false>(a, s);
+template <bool FUSE>
+hipError_t launch_update_phase(const NsArgs& a, int precision, bool comp, hipStream_t s) {
+    if (precision == kNsFp32) return launch_update<kNsFp32, false, FUSE>(a, s);
+    return comp ? launch_update<kNsBf16, true, FUSE>(a, s) : launch_update<kNsBf16, false, FUSE>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_ns(const NsArgs& a, int phase, int precision, bool comp, hipStream_t s) {
-    if (phase == kGram) return launch_phase<kGram>(a, precision, comp, s);
-    if (phase == kSquare) return launch_phase<kSquare>(a, precision, comp, s);
-    return launch_phase<kUpdate>(a, precision, comp, s);
+    if (phase == kGram) return launch_sym_phase<kGram>(a, precision, comp, s);
+    if (phase == kSquare) return launch_sym_phase<kSquare>(a, precision, comp, s);
+    return a.fuse_apply ? launch_update_phase<true>(a, precision, comp, s)
+                        : launch_update_phase<false>(a, precision, comp, s);
 }
 
 const char* ns_kernel_name(int phase, int precision, bool comp, bool fused) {

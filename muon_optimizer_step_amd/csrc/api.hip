@@ -3,7 +3,8 @@
 //
 // One muon_step enqueues, on the caller's stream:
 //   prep  (per-row momentum, MuonEq-R row norm, NS input X0 short side first)
-//   frob  (per-matrix Frobenius scale from the per-row sums)
+//   frob  (per-matrix Frobenius scale from the per-row sums; folded into the
+//   first ns_gram unless a launch holds more than kMaxFrobSlots matrices)
 //   for each NS iteration: ns_gram, ns_square, ns_update (all shape groups
 //   batched in one launch per phase)
 //   apply (decoupled weight decay + shape-scaled update)
@@ -393,11 +394,14 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
         }
     // The weight update runs inside the last NS update launch when every launch
     // holds at most kMaxFused matrices.
-    bool fuse = ns_steps > 0;
+    // The first Gram launch computes the Frobenius scales itself (no separate
+    // frob launch) when every launch holds at most kMaxFrobSlots matrices.
+    bool fuse = ns_steps > 0, fold_frob = ns_steps > 0;
     for (const NsLaunchSet& ls : sets) {
         int cnt = 0;
         for (int q : ls.parts) cnt += parts[q].s1 - parts[q].s0;
         if (cnt > kMaxFused) fuse = false;
+        if (cnt > kMaxFrobSlots) fold_frob = false;
     }
     const float keep = 1.0f - lr * weight_decay;
     // 16-byte accesses to the caller's W / O / EMA rows
@@ -521,7 +525,9 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
             a.keep = keep;
             a.decay = ema_decay;
             a.one_minus_decay = 1.0f - ema_decay;
-            int jobs = 0, napply = 0;
+            a.fold_frob = fold_frob && phase == kGram && k == 0;
+            a.rowsq = rowsq;
+            int jobs = 0, napply = 0, nfrob = 0;
             for (int q : ls.parts) {
                 const Part& pt = parts[q];
                 const Group& G = p.groups[pt.group];
@@ -536,12 +542,19 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
                 D.a_lo = ws + G.al_off + pt.s0 * aslot;
                 D.b = ws + G.b_off + pt.s0 * aslot;
                 D.b_lo = ws + G.bl_off + pt.s0 * aslot;
-                D.scale = reinterpret_cast<const float*>(ws + p.scale_base) + G.scale_begin + pt.s0;
+                D.scale = reinterpret_cast<float*>(ws + p.scale_base) + G.scale_begin + pt.s0;
                 D.count = count;
                 D.M = G.M;
                 D.N = G.N;
                 D.job_begin = jobs;
                 D.apply_begin = napply;
+                D.frob_begin = nfrob;
+                if (a.fold_frob) {
+                    for (int sl = pt.s0; sl < pt.s1; ++sl) {
+                        const int ti = p.members[pt.group][sl];
+                        a.frob[nfrob++] = {(int)p.rowsq_off[ti], tensors[ti].rows};
+                    }
+                }
                 if (a.fuse_apply) {
                     for (int sl = pt.s0; sl < pt.s1; ++sl) {
                         const int ti = p.members[pt.group][sl];
@@ -623,8 +636,9 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
     // early even when the host is only just ahead of the GPU.
     for (int lane = 0; lane < nlanes; ++lane)
         if ((rc = enqueue_prep(lane))) return rc;
-    for (int lane = 0; lane < nlanes; ++lane)
-        if ((rc = enqueue_frob(lane))) return rc;
+    if (!fold_frob)
+        for (int lane = 0; lane < nlanes; ++lane)
+            if ((rc = enqueue_frob(lane))) return rc;
     for (int k = 0; k < ns_steps; ++k)
         for (int phase = kGram; phase <= kUpdate; ++phase)
             for (int lane = 0; lane < nlanes; ++lane)

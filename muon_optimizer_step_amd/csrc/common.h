@@ -67,6 +67,24 @@ __device__ inline float wave_sum(float v) {
     return v;
 }
 
+// Frobenius scale 1 / (sqrt(sum of rows[0 .. n)) + eps) over a 512-thread
+// workgroup in a fixed order: thread t sums rows t, t + 512, ...; each wave
+// reduces with wave_sum; thread 0 adds the 8 wave totals in wave order.  The
+// frob kernel and the first Gram launch that folds it in both use this, so the
+// scale is the same bits either way.  red: 8 floats of LDS; every thread of
+// the workgroup must call it; the result is valid in every thread.
+__device__ inline float frob_scale_512(const float* rows, int n, float* red) {
+    float s = 0.f;
+    for (int r = threadIdx.x; r < n; r += 512) s += rows[r];
+    s = wave_sum(s);
+    if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = s;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) t += red[w];
+    return 1.0f / (sqrtf(t) + kEps);
+}
+
 // Remap blockIdx so that consecutive job indices land on the same XCD (blocks
 // are dispatched round-robin over the XCDs).  grid must be a multiple of kXcds.
 __device__ inline int xcd_job_index() {

@@ -308,20 +308,12 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepArgs a) {
 }
 
 // One workgroup per matrix: scale = 1 / (sqrt(sum of the row sums) + eps),
-// summed in a fixed order.
-__global__ __launch_bounds__(256) void frob_kernel(const FrobArgs a) {
-    __shared__ float part[256];
+// summed in the fixed order of frob_scale_512.
+__global__ __launch_bounds__(512) void frob_kernel(const FrobArgs a) {
+    __shared__ float red[8];
     const int i = blockIdx.x;
-    const float* rs = a.rowsq + a.rowsq_off[i];
-    float s = 0.f;
-    for (int r = threadIdx.x; r < a.rows[i]; r += blockDim.x) s += rs[r];
-    part[threadIdx.x] = s;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) a.scale[a.scale_idx[i]] = 1.0f / (sqrtf(part[0]) + kEps);
+    const float s = frob_scale_512(a.rowsq + a.rowsq_off[i], a.rows[i], red);
+    if (threadIdx.x == 0) a.scale[a.scale_idx[i]] = s;
 }
 
 // W' = keep*W - lr_s*O with O = fac*X (fac = Frobenius scale when no NS step ran).
@@ -584,7 +576,7 @@ hipError_t launch_prep(const PrepArgs& a, int precision, int blocks, size_t lds_
 }
 
 hipError_t launch_frob(const FrobArgs& a, hipStream_t s) {
-    frob_kernel<<<a.n, 256, 0, s>>>(a);
+    frob_kernel<<<a.n, 512, 0, s>>>(a);
     return hipGetLastError();
 }
 

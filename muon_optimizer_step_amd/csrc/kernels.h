@@ -66,6 +66,13 @@ struct FusedApply {
 };
 constexpr int kApplyTransposed = 1;  // stored W is X^T
 constexpr int kApplyVec = 2;         // param/out/ema 16-byte aligned and cols % 4 == 0
+// First Gram launch with the Frobenius scale folded in: where each matrix's
+// per-row sums of squares are (one entry per matrix of the launch).
+struct FrobSlot {
+    int off;    // offset into the row-sum array, in floats
+    int rows;   // stored rows
+};
+constexpr int kMaxFrobSlots = kMaxFused * (int)sizeof(FusedApply) / (int)sizeof(FrobSlot);
 
 struct NsGroup {
     void* x[2];      // bf16: hi planes (ping-pong); fp32: X planes.  [count][M][N]
@@ -74,10 +81,11 @@ struct NsGroup {
     void* a_lo;      // bf16: lo of A; fp32: unused
     void* b;         // bf16: hi of B; fp32: B.  [count][M][M]
     void* b_lo;      // bf16: lo of B (written and read by the compensated kernels)
-    const float* scale;  // [count] Frobenius scale of X0
+    float* scale;        // [count] Frobenius scale of X0 (written by a folding first Gram)
     int count, M, N;     // padded, multiples of 128
     int job_begin;
     int apply_begin;     // fused apply: entry of slot 0 in NsArgs::apply
+    int frob_begin;      // folded Frobenius scale: entry of slot 0 in NsArgs::frob
 };
 struct NsArgs {
     NsGroup g[kMaxGroups];
@@ -89,7 +97,12 @@ struct NsArgs {
     int fuse_apply;  // last update: write W' (and O) instead of X
     float keep;      // 1 - lr*wd
     float decay, one_minus_decay;  // weight EMA
-    FusedApply apply[kMaxFused];
+    int fold_frob;         // first Gram: compute the Frobenius scale from the row sums
+    const float* rowsq;    // base of the per-row sums (fold_frob)
+    union {
+        FusedApply apply[kMaxFused];    // last update (fuse_apply)
+        FrobSlot frob[kMaxFrobSlots];   // first Gram (fold_frob)
+    };
 };
 
 enum NsPhase { kGram = 0, kSquare = 1, kUpdate = 2 };

@@ -790,6 +790,16 @@ __global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) 
     // group's store and the reads of that slot are always a half-step apart.
     const int nk = K / kBK;
     if (kg < nk) issue(kg);
+    // First Gram: the Frobenius scale of X0 from the per-row sums of squares,
+    // while the first loads are in flight (every tile of a matrix computes the
+    // same bits; tile (0, 0) stores it for the later phases).  Its 8 floats of
+    // LDS are read before the barrier below, ahead of the first LDS stage.
+    float fscale = 0.f;
+    if (PHASE == kGram && args.first && args.fold_frob) {
+        const FrobSlot fs = args.frob[G.frob_begin + job.slot];
+        fscale = frob_scale_512(args.rowsq + fs.off, fs.rows, reinterpret_cast<float*>(lds));
+        if (job.ti == 0 && job.tj == 0 && tid == 0) G.scale[job.slot] = fscale;
+    }
     __syncthreads();
     for (int h = 0; h <= nk; ++h) {
         if ((h & 1) == kg) {
@@ -861,7 +871,7 @@ __global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) 
     if (kg == 0) finish(std::integral_constant<int, 0>{});
     else finish(std::integral_constant<int, 1>{});
     __syncthreads();
-    const float s = G.scale[job.slot];
+    const float s = (PHASE == kGram && args.first && args.fold_frob) ? fscale : G.scale[job.slot];
     const float sc = args.first ? s * s : 1.0f;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {

@@ -195,6 +195,21 @@ def test_more_matrices_than_the_fused_apply_table():
                         coeffs=STD, nesterov=True, row_norm=True, ns_tol=gu.NS_TOL_BF16, label=f"{i}")
 
 
+def test_more_matrices_than_the_folded_frobenius_table():
+    """400 matrices of one shape in one launch: more than the first Gram's table
+    of row-sum spans (360), so the separate Frobenius-scale launch runs (and the
+    separate apply, past the fused table)."""
+    rng = np.random.default_rng(22)
+    shapes = [(32, 48)] * 400
+    mats = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    grads = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    moms = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    w_gpu, m_gpu, o_gpu, _ = gu.gpu_step(mats, grads, moms, lr=0.02, momentum=0.95, wd=0.0, coeffs=STD)
+    for i in range(0, 400, 37):
+        gu.check_layers(mats[i], grads[i], moms[i], w_gpu[i], m_gpu[i], o_gpu[i], lr=0.02, momentum=0.95, wd=0.0,
+                        coeffs=STD, nesterov=True, row_norm=True, ns_tol=gu.NS_TOL_BF16, label=f"{i}")
+
+
 def test_ema_swap_is_an_exact_exchange():
     """ema_swap exchanges the buffers bit for bit (vector and scalar paths, many tensors); twice is identity."""
     import torch

@@ -683,24 +683,27 @@ int ema_update(float* const* ema, const float* const* params, const int64_t* num
     int rc = check_overlaps(spans, "ema_update");
     if (rc) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // table entries of at most kEmaEntryElems elements, kEmaChunk per launch
     int i = 0;
+    int64_t off = 0;
     while (i < n) {
         EmaArgs a;
         memset(&a, 0, sizeof(a));
         a.decay = decay;
         a.one_minus_decay = 1.0f - decay;
         int64_t blocks = 0;
-        for (; i < n && a.n < kEmaChunk; ++i) {
-            if (numel[i] == 0) continue;
-            const int64_t nb = (numel[i] + kEmaElemsPerBlock - 1) / kEmaElemsPerBlock;
+        while (i < n && a.n < kEmaChunk) {
+            if (off >= numel[i]) { ++i; off = 0; continue; }
+            const int64_t len = std::min(numel[i] - off, kEmaEntryElems);
+            const int64_t nb = (len + kEmaElemsPerBlock - 1) / kEmaElemsPerBlock;
             if (blocks + nb > (int64_t)1 << 30) break;
             EmaTensor& T = a.t[a.n++];
-            T.ema = ema[i];
-            T.param = params[i];
-            T.numel = numel[i];
+            T.ema = ema[i] + off;
+            T.param = params[i] + off;
+            T.numel = (int)len;
             T.block_begin = (int)blocks;
-            T.vec = (reinterpret_cast<uintptr_t>(ema[i]) % 16 == 0) && (reinterpret_cast<uintptr_t>(params[i]) % 16 == 0);
             blocks += nb;
+            off += len;
         }
         if (a.n == 0) continue;
         hipError_t err = timed_launch("ema", s, [&] { return launch_ema(a, (int)blocks, s); });
@@ -731,22 +734,25 @@ int ema_swap(float* const* ema, float* const* params, const int64_t* numel, int3
     int rc = check_overlaps(spans, "ema_swap");
     if (rc) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // table entries of at most kEmaEntryElems elements, kEmaChunk per launch
     int i = 0;
+    int64_t off = 0;
     while (i < n) {
         SwapArgs a;
         memset(&a, 0, sizeof(a));
         int64_t blocks = 0;
-        for (; i < n && a.n < kEmaChunk; ++i) {
-            if (numel[i] == 0) continue;
-            const int64_t nb = (numel[i] + kEmaElemsPerBlock - 1) / kEmaElemsPerBlock;
+        while (i < n && a.n < kEmaChunk) {
+            if (off >= numel[i]) { ++i; off = 0; continue; }
+            const int64_t len = std::min(numel[i] - off, kEmaEntryElems);
+            const int64_t nb = (len + kEmaElemsPerBlock - 1) / kEmaElemsPerBlock;
             if (blocks + nb > (int64_t)1 << 30) break;
             SwapTensor& T = a.t[a.n++];
-            T.a = ema[i];
-            T.b = params[i];
-            T.numel = numel[i];
+            T.a = ema[i] + off;
+            T.b = params[i] + off;
+            T.numel = (int)len;
             T.block_begin = (int)blocks;
-            T.vec = (reinterpret_cast<uintptr_t>(ema[i]) % 16 == 0) && (reinterpret_cast<uintptr_t>(params[i]) % 16 == 0);
             blocks += nb;
+            off += len;
         }
         if (a.n == 0) continue;
         hipError_t err = timed_launch("swap", s, [&] { return launch_swap(a, (int)blocks, s); });

@@ -420,9 +420,10 @@ __global__ __launch_bounds__(kEmaThreads) void ema_kernel(const EmaArgs a) {
     const int ti = find_tensor(a.t, a.n, blockIdx.x);
     const EmaTensor& T = a.t[ti];
     const int64_t base = (int64_t)(blockIdx.x - T.block_begin) * kEmaElemsPerBlock;
-    const int64_t end = min(base + (int64_t)kEmaElemsPerBlock, T.numel);
+    const int64_t end = min(base + (int64_t)kEmaElemsPerBlock, (int64_t)T.numel);
     const float d = a.decay, omd = a.one_minus_decay;
-    if (T.vec && end - base == kEmaElemsPerBlock) {
+    const bool vec = ((reinterpret_cast<uintptr_t>(T.ema) | reinterpret_cast<uintptr_t>(T.param)) & 15) == 0;
+    if (vec && end - base == kEmaElemsPerBlock) {
         floatx4* e4 = reinterpret_cast<floatx4*>(T.ema + base);
         const floatx4* p4 = reinterpret_cast<const floatx4*>(T.param + base);
         floatx4 ev[4], pv[4];
@@ -450,8 +451,9 @@ __global__ __launch_bounds__(kEmaThreads) void swap_kernel(const SwapArgs a) {
     const int ti = find_tensor(a.t, a.n, blockIdx.x);
     const SwapTensor& T = a.t[ti];
     const int64_t base = (int64_t)(blockIdx.x - T.block_begin) * kEmaElemsPerBlock;
-    const int64_t end = min(base + (int64_t)kEmaElemsPerBlock, T.numel);
-    if (T.vec && end - base == kEmaElemsPerBlock) {
+    const int64_t end = min(base + (int64_t)kEmaElemsPerBlock, (int64_t)T.numel);
+    const bool vec = ((reinterpret_cast<uintptr_t>(T.a) | reinterpret_cast<uintptr_t>(T.b)) & 15) == 0;
+    if (vec && end - base == kEmaElemsPerBlock) {
         floatx4* a4 = reinterpret_cast<floatx4*>(T.a + base);
         floatx4* b4 = reinterpret_cast<floatx4*>(T.b + base);
         floatx4 av[4], bv[4];

@@ -13,7 +13,8 @@ namespace muon {
 constexpr int kMaxGroups = 12;    // NS shape groups per NS launch
 constexpr int kPrepChunk = 50;    // tensors per prep launch
 constexpr int kFrobChunk = 256;   // matrices per Frobenius-scale launch
-constexpr int kEmaChunk = 112;    // tensors per EMA launch
+constexpr int kEmaChunk = 144;    // table entries per EMA / swap launch (24 bytes each)
+constexpr int64_t kEmaEntryElems = (int64_t)1 << 30;  // a longer tensor takes several entries
 constexpr int kRowsPerWaveBlock = 4;  // stored rows per workgroup when no transpose is needed
 constexpr size_t kTransposeLdsBytes = 64 * 1024;  // LDS budget of the transposing prep / apply
 
@@ -138,9 +139,8 @@ struct ApplyArgs {
 struct EmaTensor {
     float* ema;
     const float* param;
-    int64_t numel;
+    int numel;           // <= kEmaEntryElems
     int block_begin;
-    int vec;             // both pointers 16-byte aligned
 };
 struct EmaArgs {
     EmaTensor t[kEmaChunk];
@@ -155,9 +155,8 @@ constexpr int kEmaElemsPerBlock = kEmaThreads * 4 * 4;  // float4 x 4 per thread
 struct SwapTensor {
     float* a;
     float* b;
-    int64_t numel;
+    int numel;           // <= kEmaEntryElems
     int block_begin;
-    int vec;             // both pointers 16-byte aligned
 };
 struct SwapArgs {
     SwapTensor t[kEmaChunk];

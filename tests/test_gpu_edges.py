@@ -210,6 +210,33 @@ def test_more_matrices_than_the_folded_frobenius_table():
                         coeffs=STD, nesterov=True, row_norm=True, ns_tol=gu.NS_TOL_BF16, label=f"{i}")
 
 
+def test_ema_and_swap_of_a_tensor_past_2_30_elements():
+    """One tensor of 2^30 + 4099 elements takes two table entries (the split at
+    2^30 elements): the EMA matches the oracle on slices around the split and a
+    float32 device check everywhere; the swap exchanges every element exactly."""
+    import torch
+    import muon_optimizer_step_amd as ms
+    n = (1 << 30) + 4099
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    e = torch.rand(n, device="cuda", generator=gen)
+    p = torch.rand(n, device="cuda", generator=gen)
+    e0 = e.clone()
+    decay = 0.99
+    gu.say(f"[edges] EMA of {n} elements")
+    ms.ema_update([e], [p], decay)
+    torch.cuda.synchronize()
+    for lo, hi in ((0, 4096), ((1 << 30) - 4096, n)):
+        want = om.ema_update(e0[lo:hi].cpu().numpy(), p[lo:hi].cpu().numpy(), gu.f32(decay))
+        assert gu.rel_max(e[lo:hi].cpu().numpy(), want) <= gu.ELEM_TOL, (lo, hi)
+    ref = e0.mul_(decay).add_(p, alpha=1.0 - decay)
+    assert float((e - ref).abs_().max()) <= 1e-6 * float(ref.abs().max())
+    del ref, e0
+    e1, p1 = e.clone(), p.clone()
+    ms.ema_swap([e], [p])
+    torch.cuda.synchronize()
+    assert torch.equal(e, p1) and torch.equal(p, e1)
+
+
 def test_ema_swap_is_an_exact_exchange():
     """ema_swap exchanges the buffers bit for bit (vector and scalar paths, many tensors); twice is identity."""
     import torch

@@ -57,12 +57,14 @@ def parse():
 def _kernel_key(name: str) -> str:
     """Library kernel symbol -> the name the profiling hook reports."""
     import re
-    m = re.search(r"ns_(?:sym_)?kernel<(\d), (\d), (true|false)(?:, (true|false))?>", name)
+    m = re.search(r"ns_sym_kernel<(\d), (\d), (true|false)>", name)
     if m:
-        phase, prec, comp, fuse = int(m.group(1)), int(m.group(2)), m.group(3) == "true", m.group(4) == "true"
-        base = ["ns_gram", "ns_square", "ns_update", "ns_update"][phase]
-        if phase == 2 and fuse:
-            base = "ns_update_apply"
+        phase, prec, comp = int(m.group(1)), int(m.group(2)), m.group(3) == "true"
+        return ["ns_gram", "ns_square"][phase] + ("_fp32" if prec == 1 else ("_bf16x3" if comp else "_bf16"))
+    m = re.search(r"ns_update_kernel<(\d), (true|false), (true|false)>", name)
+    if m:
+        prec, comp, fuse = int(m.group(1)), m.group(2) == "true", m.group(3) == "true"
+        base = "ns_update_apply" if fuse else "ns_update"
         return base + ("_fp32" if prec == 1 else ("_bf16x3" if comp else "_bf16"))
     for k in ("prep_kernel", "apply_kernel", "ema_kernel", "frob_kernel", "adamw_kernel", "swap_kernel"):
         if k in name:

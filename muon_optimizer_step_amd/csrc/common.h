@@ -69,16 +69,35 @@ __device__ inline float wave_sum(float v) {
 
 // Frobenius scale 1 / (sqrt(sum of rows[0 .. n)) + eps) over a 512-thread
 // workgroup in a fixed order: thread t sums rows t, t + 512, ...; each wave
-// reduces with wave_sum; thread 0 adds the 8 wave totals in wave order.  The
-// frob kernel and the first Gram launch that folds it in both use this, so the
-// scale is the same bits either way.  red: 8 floats of LDS; every thread of
-// the workgroup must call it; the result is valid in every thread.
-__device__ inline float frob_scale_512(const float* rows, int n, float* red) {
+// reduces with wave_sum; every thread adds the 8 wave totals in wave order.
+// The frob kernel and the first Gram launch that folds it in both use this,
+// so the scale is the same bits either way.  Split in two so that a caller can
+// put other loads between them: frob_prefetch loads the first 4 rows of the
+// thread, frob_finish adds them (0 for rows past n, which leaves the sum's
+// bits unchanged) and any further rows.  red: 8 floats of LDS; every thread of the
+// workgroup must call frob_finish; the result is valid in every thread.  The
+// caller separates red from later LDS writes with a barrier of its own.
+__device__ inline void frob_prefetch(const float* rows, int n, float v[4]) {
+    // straight-line loads of rows in range (n >= 1; frob_finish drops the
+    // values past n), so the compiler can wait for exactly these loads later
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int r = (int)threadIdx.x + 512 * k;
+        v[k] = rows[r < n ? r : n - 1];
+    }
+}
+__device__ inline float frob_finish(const float* rows, int n, const float v[4], float* red) {
     float s = 0.f;
-    for (int r = threadIdx.x; r < n; r += 512) s += rows[r];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s += ((int)threadIdx.x + 512 * k < n) ? v[k] : 0.f;
+    for (int r = (int)threadIdx.x + 2048; r < n; r += 512) s += rows[r];
     s = wave_sum(s);
     if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = s;
-    __syncthreads();
+    // LDS-only barrier: waits for this wave's LDS write, not for other memory
+    // operations in flight (the caller's direct LDS loads may be)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     float t = 0.f;
 #pragma unroll
     for (int w = 0; w < 8; ++w) t += red[w];

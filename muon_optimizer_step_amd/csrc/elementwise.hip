@@ -308,11 +308,14 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepArgs a) {
 }
 
 // One workgroup per matrix: scale = 1 / (sqrt(sum of the row sums) + eps),
-// summed in the fixed order of frob_scale_512.
+// summed in the fixed order of frob_prefetch / frob_finish.
 __global__ __launch_bounds__(512) void frob_kernel(const FrobArgs a) {
     __shared__ float red[8];
     const int i = blockIdx.x;
-    const float s = frob_scale_512(a.rowsq + a.rowsq_off[i], a.rows[i], red);
+    const float* rs = a.rowsq + a.rowsq_off[i];
+    float v[4];
+    frob_prefetch(rs, a.rows[i], v);
+    const float s = frob_finish(rs, a.rows[i], v, red);
     if (threadIdx.x == 0) a.scale[a.scale_idx[i]] = s;
 }
 

@@ -64,10 +64,40 @@ constexpr int kStageBytes = 64 * kStagePitch * 4;  // half a tile (64 rows) of f
 __device__ inline int stage_col(int row, int col) { return col ^ (((row >> 3) & 7) << 3); }
 static_assert(kStageBytes <= 2 * Stage<128>::kSlot, "epilogue staging must fit in the operand LDS");
 
-// K bytes per LDS stage of the Gram and square: 256 for the bf16 base Gram,
-// whose long contraction gains from fewer, larger stages, 128 otherwise.
-constexpr int ns_sym_stage_bytes(int phase, int precision, bool comp) {
+#ifndef NS_SYM_DMA
+#define NS_SYM_DMA 1   // Gram / square operands loaded straight into LDS (double-buffered)
+#endif
+
+// Direct loads for the phases with two operand tiles per stage (the split
+// phases stage four, which would need 64-byte stages to fit two buffers).
+constexpr bool ns_sym_dma(int phase, int precision, bool comp) {
+    return NS_SYM_DMA != 0 && !(precision == kNsBf16 && (phase == kSquare || comp));
+}
+
+// K bytes per LDS stage of the Gram and square.  Register staging: 256 for the
+// bf16 base Gram, whose long contraction gains from fewer, larger stages, 128
+// otherwise.  Direct loads (two buffers per group): 128.
+constexpr int ns_sym_stage_bytes(int phase, int precision, bool comp, bool dma) {
+    if (dma) return 128;
     return (precision == kNsBf16 && !comp && phase == kGram) ? 256 : 128;
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Explicit waits and a bare barrier for the direct-load K loop: the compiler
+// does not count global_load_lds against later LDS reads, so the loop waits
+// for its own loads (vmcnt) and publishes them with s_barrier.  The empty asm
+// statements with memory clobbers keep LDS accesses on their side.
+template <int N>
+__device__ inline void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ inline void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ inline void barrier_only() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 template <int PREC> struct Elem;
@@ -636,7 +666,8 @@ __global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) 
     static_assert(PHASE == kGram || PHASE == kSquare, "symmetric phases only");
     typedef typename Elem<PREC>::T T;
     constexpr bool kSplit = (PREC == kNsBf16) && (PHASE == kSquare || COMP);
-    constexpr int kRB = ns_sym_stage_bytes(PHASE, PREC, COMP);
+    constexpr bool kDma = ns_sym_dma(PHASE, PREC, COMP);
+    constexpr int kRB = ns_sym_stage_bytes(PHASE, PREC, COMP, kDma);
     constexpr int kBK = kRB / (int)sizeof(T);
     constexpr int kSlot = Stage<kRB>::kSlot;
     constexpr int kStageTiles = kSplit ? 4 : 2;
@@ -689,78 +720,59 @@ __global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) 
         for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+    // zeroed here, ahead of the first operand loads (otherwise the zeros are
+    // rematerialised into registers that still wait for those loads)
+    asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]));
 
-    NtLoader<kRB> la, lb, lal, lbl;
-    auto issue = [&](int kt) {
-        const int kbyte = kt * kRB;
-        la.load(ga, ld_bytes, kbyte);
-        if (kSplit) lal.load(gal, ld_bytes, kbyte);
-        if (!diag) {
-            lb.load(gb, ld_bytes, kbyte);
-            if (kSplit) lbl.load(gbl, ld_bytes, kbyte);
-        }
-    };
-    auto commit = [&]() {
-        la.store(tile(0));
-        if (kSplit) lal.store(tile(2));
-        if (!diag) {
-            lb.store(tile(1));
-            if (kSplit) lbl.store(tile(3));
-        }
-    };
-    // bf16 base: the fragments of chunk kc + 2 are read while the MFMAs of
-    // chunk kc run.  The scheduling groups (one fragment read after each MFMA)
-    // keep the compiler from moving the reads next to the MFMAs that use them.
-    auto compute_ahead = [&]() {
-        const uint8_t* t_a = tile(0);
-        const uint8_t* t_b = tile(1);
-        constexpr int kKC = kRB / 32, kDist = 2, kBufs = kDist + 1;
-        static_assert(kKC >= kDist, "at least kDist chunks per stage");
-        u32x4 f[kBufs][4];
-        auto read = [&](int kc, u32x4* d) {
-#pragma unroll
-            for (int mi = 0; mi < 2; ++mi) d[mi] = lds_frag<kRB>(t_a, wm * 64 + mi * 32 + lane % 32, kc, lane);
-#pragma unroll
-            for (int ni = 0; ni < 2; ++ni) d[2 + ni] = lds_frag<kRB>(t_b, wn * 64 + ni * 32 + lane % 32, kc, lane);
-        };
-#pragma unroll
-        for (int kc = 0; kc < kDist; ++kc) read(kc, f[kc]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4 * kDist, 0);   // DS reads
-#pragma unroll
-        for (int kc = 0; kc < kKC; ++kc) {
-            if (kc + kDist < kKC) read(kc + kDist, f[(kc + kDist) % kBufs]);
-#pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
-                    mfma_chunk<PREC>(acc[mi][ni], f[kc % kBufs][mi], f[kc % kBufs][2 + ni]);
-            if (kc + kDist < kKC) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-                }
-            } else {
-                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-            }
-        }
-    };
-    auto compute = [&]() {
+    // MFMAs of one LDS stage.  frag(t, row, kc) is the lane's 16-byte operand
+    // chunk (K chunk kc of 16 elements) of row `row` of tile t.
+    auto compute_with = [&](auto frag, const uint8_t* t_a, const uint8_t* t_b, const uint8_t* t_al,
+                            const uint8_t* t_bl) {
+        constexpr int kKC = kRB / 32;
         if constexpr (PREC == kNsBf16 && !kSplit) {
-            compute_ahead();
+            // bf16 base: the fragments of chunk kc + 2 are read while the MFMAs
+            // of chunk kc run.  The scheduling groups (one fragment read after
+            // each MFMA) keep the compiler from moving the reads next to the
+            // MFMAs that use them.
+            constexpr int kDist = 2, kBufs = kDist + 1;
+            static_assert(kKC >= kDist, "at least kDist chunks per stage");
+            u32x4 f[kBufs][4];
+            auto read = [&](int kc, u32x4* d) {
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi) d[mi] = frag(t_a, wm * 64 + mi * 32 + lane % 32, kc);
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni) d[2 + ni] = frag(t_b, wn * 64 + ni * 32 + lane % 32, kc);
+            };
+#pragma unroll
+            for (int kc = 0; kc < kDist; ++kc) read(kc, f[kc]);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4 * kDist, 0);   // DS reads
+#pragma unroll
+            for (int kc = 0; kc < kKC; ++kc) {
+                if (kc + kDist < kKC) read(kc + kDist, f[(kc + kDist) % kBufs]);
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < 2; ++ni)
+                        mfma_chunk<PREC>(acc[mi][ni], f[kc % kBufs][mi], f[kc % kBufs][2 + ni]);
+                if (kc + kDist < kKC) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+                    }
+                } else {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                }
+            }
             return;
         }
-        const uint8_t* t_a = tile(0);
-        const uint8_t* t_b = tile(1);
-        const uint8_t* t_al = tile(2);
-        const uint8_t* t_bl = tile(3);
 #pragma unroll
-        for (int kc = 0; kc < kRB / 32; ++kc) {
+        for (int kc = 0; kc < kKC; ++kc) {
             u32x4 fa[2], fb[2];
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi) fa[mi] = lds_frag<kRB>(t_a, wm * 64 + mi * 32 + lane % 32, kc, lane);
+            for (int mi = 0; mi < 2; ++mi) fa[mi] = frag(t_a, wm * 64 + mi * 32 + lane % 32, kc);
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni) fb[ni] = lds_frag<kRB>(t_b, wn * 64 + ni * 32 + lane % 32, kc, lane);
+            for (int ni = 0; ni < 2; ++ni) fb[ni] = frag(t_b, wn * 64 + ni * 32 + lane % 32, kc);
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -768,9 +780,9 @@ __global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) 
             if (kSplit) {
                 u32x4 fal[2], fbl[2];
 #pragma unroll
-                for (int mi = 0; mi < 2; ++mi) fal[mi] = lds_frag<kRB>(t_al, wm * 64 + mi * 32 + lane % 32, kc, lane);
+                for (int mi = 0; mi < 2; ++mi) fal[mi] = frag(t_al, wm * 64 + mi * 32 + lane % 32, kc);
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni) fbl[ni] = lds_frag<kRB>(t_bl, wn * 64 + ni * 32 + lane % 32, kc, lane);
+                for (int ni = 0; ni < 2; ++ni) fbl[ni] = frag(t_bl, wn * 64 + ni * 32 + lane % 32, kc);
 #pragma unroll
                 for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -781,36 +793,130 @@ __global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) 
             }
         }
     };
-
-    // Group g takes the K stages kt = 2j + g.  The groups run half a step
-    // apart: in half-step h, group 0 stores stage h (h even) into its LDS slot
-    // or computes stage h - 1 (h odd), and group 1 stores stage h (h odd) or
-    // computes stage h - 1 (h even), so one group's LDS stores and load waits
-    // overlap the other group's MFMAs.  A barrier ends every half-step; a
-    // group's store and the reads of that slot are always a half-step apart.
     const int nk = K / kBK;
-    if (kg < nk) issue(kg);
-    // First Gram: the Frobenius scale of X0 from the per-row sums of squares,
-    // while the first loads are in flight (every tile of a matrix computes the
-    // same bits; tile (0, 0) stores it for the later phases).  Its 8 floats of
-    // LDS are read before the barrier below, ahead of the first LDS stage.
-    float fscale = 0.f;
-    if (PHASE == kGram && args.first && args.fold_frob) {
-        const FrobSlot fs = args.frob[G.frob_begin + job.slot];
-        fscale = frob_scale_512(args.rowsq + fs.off, fs.rows, reinterpret_cast<float*>(lds));
-        if (job.ti == 0 && job.tj == 0 && tid == 0) G.scale[job.slot] = fscale;
-    }
-    __syncthreads();
-    for (int h = 0; h <= nk; ++h) {
-        if ((h & 1) == kg) {
-            if (h < nk) {                       // stage h: registers -> LDS, next loads
-                commit();
-                if (h + 2 < nk) issue(h + 2);
-            }
-        } else if (h > 0 && h - 1 < nk) {       // stage h - 1 of this group
-            compute();
+    // First Gram: the Frobenius scale of X0 from the per-row sums of squares
+    // (every tile of a matrix computes the same bits; tile (0, 0) stores it for
+    // the later phases).  Its 8 floats of LDS (at red_off, clear of the first
+    // stage's LDS) are read before the barrier that precedes the first LDS
+    // write of operands.
+    float fscale = 0.f, fv[4];
+    const bool fold = PHASE == kGram && args.first && args.fold_frob;
+    const FrobSlot fs = fold ? args.frob[G.frob_begin + job.slot] : FrobSlot{0, 0};
+    if (fold) frob_prefetch(args.rowsq + fs.off, fs.rows, fv);
+    auto fold_frob = [&](int red_off) {
+        if (fold) {
+            fscale = frob_finish(args.rowsq + fs.off, fs.rows, fv, reinterpret_cast<float*>(lds + red_off));
+            if (job.ti == 0 && job.tj == 0 && tid == 0) G.scale[job.slot] = fscale;
         }
+    };
+
+    if constexpr (kDma) {
+        // Direct global -> LDS loads (global_load_lds_dwordx4, lane l writes the
+        // 16 bytes at block base + 16 l).  Two LDS buffers; buffer b holds, per
+        // group, the tiles [A hi, B hi, A lo, B lo] of one stage, rows of kRB
+        // bytes without padding and the 16-byte chunk c of row r at c ^ swz(r),
+        // which keeps the fragment reads free of bank conflicts.  Both groups
+        // load and compute at the same time (group g: stages 2p + g); waits are
+        // explicit: each wave waits for its own loads of the stage (vmcnt), a
+        // barrier publishes them, and a second barrier frees the buffer for the
+        // loads two stages ahead.
+        constexpr int kC = kRB / 16;                       // 16-byte chunks per row
+        constexpr int kTileBytes = kTile * kRB;
+        constexpr int kBufBytes = 2 * kStageTiles * kTileBytes;
+        constexpr int kPerTile = kTileBytes / 1024 / 4;    // loads per wave per tile
+        auto swz = [](int row) { return (row / (16 / kC)) % kC; };
+        auto dtile = [&](int buf, int which) -> const uint8_t* {
+            if (diag && which == 1) which = 0;
+            if (diag && which == 3) which = 2;
+            return lds + buf * kBufBytes + (kg * kStageTiles + which) * kTileBytes;
+        };
+        auto dma_tile = [&](const uint8_t* src, int kt, int buf, int which) {
+            uint8_t* dst = lds + buf * kBufBytes + (kg * kStageTiles + which) * kTileBytes;
+#pragma unroll
+            for (int j = 0; j < kPerTile; ++j) {
+                const int q = j * 4 + wave;                      // 1 KB block: rows q*1024/kRB ..
+                const int row = q * (1024 / kRB) + lane / kC;
+                const int c = (lane % kC) ^ swz(row);
+                __builtin_amdgcn_global_load_lds(src + (size_t)row * ld_bytes + (size_t)kt * kRB + c * 16,
+                                                 (lds_ptr)(dst + q * 1024), 16, 0, 0);
+            }
+        };
+        auto dma_stage = [&](int kt, int buf) {
+            dma_tile(ga, kt, buf, 0);
+            if (kSplit) dma_tile(gal, kt, buf, 2);
+            if (!diag) {
+                dma_tile(gb, kt, buf, 1);
+                if (kSplit) dma_tile(gbl, kt, buf, 3);
+            }
+        };
+        // loads per wave of one stage, by diagonal and off-diagonal tiles
+        constexpr int kLoadsDiag = kPerTile * (kSplit ? 2 : 1);
+        constexpr int kLoadsOff = 2 * kLoadsDiag;
+        auto frag = [&](const uint8_t* t, int row, int kc) -> u32x4 {
+            const int c = (2 * kc + lane / 32) ^ swz(row);
+            return *reinterpret_cast<const u32x4*>(t + row * kRB + c * 16);
+        };
+        const int np = nk / 2;   // nk is even: K is a multiple of 128
+        // the folded Frobenius sum first: no loads into registers may be in
+        // flight once the direct loads start (waiting for them would also wait
+        // for every direct load issued before)
+        fold_frob(2 * kBufBytes);
+        dma_stage(kg, 0);
+        for (int p = 0; p < np; ++p) {
+            const int buf = p & 1;
+            if (p + 1 < np) {
+                dma_stage(2 * (p + 1) + kg, buf ^ 1);
+                if (diag) wait_vmcnt<kLoadsDiag>();
+                else wait_vmcnt<kLoadsOff>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            barrier_only();
+            compute_with(frag, dtile(buf, 0), dtile(buf, 1), dtile(buf, 2), dtile(buf, 3));
+            wait_lgkmcnt0();
+            barrier_only();
+        }
+    } else {
+        NtLoader<kRB> la, lb, lal, lbl;
+        auto issue = [&](int kt) {
+            const int kbyte = kt * kRB;
+            la.load(ga, ld_bytes, kbyte);
+            if (kSplit) lal.load(gal, ld_bytes, kbyte);
+            if (!diag) {
+                lb.load(gb, ld_bytes, kbyte);
+                if (kSplit) lbl.load(gbl, ld_bytes, kbyte);
+            }
+        };
+        auto commit = [&]() {
+            la.store(tile(0));
+            if (kSplit) lal.store(tile(2));
+            if (!diag) {
+                lb.store(tile(1));
+                if (kSplit) lbl.store(tile(3));
+            }
+        };
+        auto frag = [&](const uint8_t* t, int row, int kc) -> u32x4 { return lds_frag<kRB>(t, row, kc, lane); };
+        // Group g takes the K stages kt = 2j + g.  The groups run half a step
+        // apart: in half-step h, group 0 stores stage h (h even) into its LDS
+        // slot or computes stage h - 1 (h odd), and group 1 stores stage h (h
+        // odd) or computes stage h - 1 (h even), so one group's LDS stores and
+        // load waits overlap the other group's MFMAs.  A barrier ends every
+        // half-step; a group's store and the reads of that slot are always a
+        // half-step apart.
+        if (kg < nk) issue(kg);
+        fold_frob(0);
         __syncthreads();
+        for (int h = 0; h <= nk; ++h) {
+            if ((h & 1) == kg) {
+                if (h < nk) {                       // stage h: registers -> LDS, next loads
+                    commit();
+                    if (h + 2 < nk) issue(h + 2);
+                }
+            } else if (h > 0 && h - 1 < nk) {       // stage h - 1 of this group
+                compute_with(frag, tile(0), tile(1), tile(2), tile(3));
+            }
+            __syncthreads();
+        }
     }
 
     // ------------------------------------------------------- epilogue
@@ -871,7 +977,7 @@ __global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) 
     if (kg == 0) finish(std::integral_constant<int, 0>{});
     else finish(std::integral_constant<int, 1>{});
     __syncthreads();
-    const float s = (PHASE == kGram && args.first && args.fold_frob) ? fscale : G.scale[job.slot];
+    const float s = fold ? fscale : G.scale[job.slot];
     const float sc = args.first ? s * s : 1.0f;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -955,7 +1061,14 @@ hipError_t launch_update(const NsArgs& a, hipStream_t s) {
 
 size_t ns_sym_lds_bytes(int phase, int precision, bool comp) {
     const bool split = precision == kNsBf16 && (phase == kSquare || comp);
-    const int slot = ns_sym_stage_bytes(phase, precision, comp) == 256 ? Stage<256>::kSlot : Stage<128>::kSlot;
+    const bool dma = ns_sym_dma(phase, precision, comp);
+    const int rb = ns_sym_stage_bytes(phase, precision, comp, dma);
+    if (dma) {
+        // two buffers x two groups x tiles, plus the 8 floats of the folded Frobenius sum
+        const size_t bufs = (size_t)2 * 2 * (split ? 4 : 2) * kTile * rb;
+        return std::max(bufs + 32, (size_t)kSymEpilogueBytes);
+    }
+    const int slot = rb == 256 ? Stage<256>::kSlot : Stage<128>::kSlot;
     return std::max((size_t)2 * (split ? 4 : 2) * slot, (size_t)kSymEpilogueBytes);
 }
 

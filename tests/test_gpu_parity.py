@@ -188,3 +188,24 @@ def test_ragged_shapes(ns_precision, nesterov, row_norm):
     for i, (nm, r, c) in enumerate(shapes):
         gu.check_layers(mats[i], grads[i], moms[i], w_gpu[i], m_gpu[i], o_gpu[i], lr=0.05, momentum=0.9, wd=0.1,
                         coeffs=coeffs, nesterov=nesterov, row_norm=row_norm, ns_tol=tol, label=f"{nm} {r}x{c}")
+
+
+@pytest.mark.parametrize("ns_precision,tol", [(1, 1e-5), (0, gu.NS_TOL_BF16), (2, gu.NS_TOL_BF16X3)])
+@pytest.mark.parametrize("triple", [(0.0, 1.0, 0.0), (0.0, 0.0, 1.0), (1.0, 0.0, 0.0), (0.5, -0.25, 0.125)])
+def test_single_iteration_isolates_each_product(ns_precision, tol, triple):
+    """One NS iteration whose coefficients isolate one product: (0, 1, 0) gives X Xt X (the Gram and the
+    update), (0, 0, 1) gives (X Xt)^2 X (the square), (1, 0, 0) gives X back (the a X term through the
+    hi + lo planes).  Wide, tall and square shapes over several tiles with ragged tails, on both sides of
+    the compensation threshold (short side 192), against the float64 oracle's product."""
+    shapes = [(256, 256), (200, 520), (700, 300), (64, 96), (384, 1000), (130, 129)]
+    rng = np.random.default_rng(7)
+    mats = [(0.02 * rng.standard_normal(s)).astype(np.float32) for s in shapes]
+    grads = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    moms = [(0.1 * rng.standard_normal(s)).astype(np.float32) for s in shapes]
+    coeffs = [list(triple)]
+    gu.say(f"[parity] one iteration {triple} prec={ns_precision}")
+    w_gpu, m_gpu, o_gpu, _ = gu.gpu_step(mats, grads, moms, lr=0.02, momentum=0.9, wd=0.0, coeffs=coeffs,
+                                         ns_precision=ns_precision)
+    for i, (r, c) in enumerate(shapes):
+        gu.check_layers(mats[i], grads[i], moms[i], w_gpu[i], m_gpu[i], o_gpu[i], lr=0.02, momentum=0.9, wd=0.0,
+                        coeffs=coeffs, nesterov=True, row_norm=True, ns_tol=tol, label=f"{r}x{c} {triple}")

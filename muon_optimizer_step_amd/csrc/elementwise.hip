@@ -1,8 +1,9 @@
 // Streaming kernels of the Muon step: momentum / row-norm / NS-input preparation
-// (prep), the per-matrix Frobenius scale (frob), the weight update (apply) and
-// the multi-tensor weight EMA (ema).  All are HBM-bound: coalesced fp32 streams,
-// float4 where the pointers allow, wavefront-shuffle reductions in a fixed
-// order.
+// (prep), the per-matrix Frobenius scale (frob, when the first Gram launch
+// cannot fold it in), the weight update (apply), the multi-tensor weight EMA
+// (ema), the EMA swap-in (swap) and AdamW for the non-matrix parameters
+// (adamw).  All are HBM-bound: coalesced fp32 streams, float4 where the
+// pointers allow, wavefront-shuffle reductions in a fixed order.
 //
 // Method: "Record: L_ParallelResiduals_UNetSkips_DepthRecur_Muon_ 1.0901"
 // (PR #1893), "Architecture and training stack" (Muon with momentum, weight

@@ -29,7 +29,8 @@
 // two such groups splitting the K stages for the Gram and square, whose few
 // (upper-triangle) tiles would otherwise leave one wave per SIMD.  K is staged
 // through LDS 128 or 256 bytes per row at a time with the next stage's global
-// loads in flight during the MFMAs.  A and B are symmetric:
+// loads in flight during the MFMAs: through registers, or for the Gram
+// straight into LDS (global_load_lds_dwordx4).  A and B are symmetric:
 // only tiles with ti <= tj are computed and each is written twice (as is and
 // mirrored).  Epilogues go through LDS so that every global access is 16
 // bytes wide.  All work of one phase for every matrix of every shape group is
@@ -65,7 +66,7 @@ __device__ inline int stage_col(int row, int col) { return col ^ (((row >> 3) & 
 static_assert(kStageBytes <= 2 * Stage<128>::kSlot, "epilogue staging must fit in the operand LDS");
 
 #ifndef NS_SYM_DMA
-#define NS_SYM_DMA 1   // Gram / square operands loaded straight into LDS (double-buffered)
+#define NS_SYM_DMA 1   // Gram operands loaded straight into LDS (double-buffered)
 #endif
 
 // Direct loads for the phases with two operand tiles per stage (the split

@@ -1,14 +1,17 @@
 // Host side of the Muon step library: argument validation, shape grouping,
 // workspace layout and the launch sequence behind the C ABI in muonstep.h.
 //
-// One muon_step enqueues, on the caller's stream:
+// One muon_step enqueues, per lane (the caller's stream and, when the shape
+// groups split over two, an internal stream forked from it and joined back):
 //   prep  (per-row momentum, MuonEq-R row norm, NS input X0 short side first)
 //   frob  (per-matrix Frobenius scale from the per-row sums; folded into the
 //   first ns_gram unless a launch holds more than kMaxFrobSlots matrices)
-//   for each NS iteration: ns_gram, ns_square, ns_update (all shape groups
-//   batched in one launch per phase)
-//   apply (decoupled weight decay + shape-scaled update)
-// ema_update enqueues one multi-tensor EMA launch per table chunk.
+//   for each NS iteration: ns_gram, ns_square, ns_update (the lane's shape
+//   groups batched in one launch per phase)
+//   apply (decoupled weight decay + shape-scaled update, and the EMA; inside
+//   the last ns_update unless a launch holds more than kMaxFused matrices)
+// ema_update, ema_swap and adamw_step enqueue one multi-tensor launch per
+// table chunk on the caller's stream.
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
@@ -117,12 +120,22 @@ std::map<int, LaneSet> g_lanes;
 hipError_t lanes_for_device(int dev, LaneSet*& out) {
     LaneSet& L = g_lanes[dev];
     if (!L.ready) {
-        hipError_t e;
-        for (int i = 1; i < kLanes; ++i) {
-            if ((e = hipStreamCreateWithFlags(&L.stream[i], hipStreamNonBlocking)) != hipSuccess) return e;
-            if ((e = hipEventCreateWithFlags(&L.join[i], hipEventDisableTiming)) != hipSuccess) return e;
+        hipError_t e = hipSuccess;
+        for (int i = 1; i < kLanes && e == hipSuccess; ++i) {
+            e = hipStreamCreateWithFlags(&L.stream[i], hipStreamNonBlocking);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&L.join[i], hipEventDisableTiming);
         }
-        if ((e = hipEventCreateWithFlags(&L.fork, hipEventDisableTiming)) != hipSuccess) return e;
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&L.fork, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            // release what was created; the next call starts over
+            for (int i = 1; i < kLanes; ++i) {
+                if (L.stream[i]) (void)hipStreamDestroy(L.stream[i]);
+                if (L.join[i]) (void)hipEventDestroy(L.join[i]);
+            }
+            if (L.fork) (void)hipEventDestroy(L.fork);
+            L = LaneSet();
+            return e;
+        }
         L.ready = true;
     }
     out = &L;

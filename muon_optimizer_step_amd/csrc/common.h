@@ -18,7 +18,7 @@ constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dispatched round
 constexpr int kTile = 128;        // NS output tile edge; workspace dims are padded to it
 constexpr float kEps = 1e-7f;     // added to the row and Frobenius norms
 
-// Number of elements of the workspace layouts kept per NS precision.
+// Storage precision of the NS workspace planes (X, A, B): bf16 hi/lo pairs or fp32.
 enum NsPrecision { kNsBf16 = 0, kNsFp32 = 1 };
 
 __host__ __device__ inline int pad_to_tile(int x) { return (x + kTile - 1) / kTile * kTile; }

@@ -555,7 +555,7 @@ hipError_t allow_lds(K kernel, size_t lds_bytes) {
     // dynamic LDS beyond the default 64 KiB must be requested (gfx950: 160 KiB per CU)
     if (lds_bytes <= 65536) return hipSuccess;
     return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)kTransposeLdsBytes);
+                               (int)lds_bytes);
 }
 
 template <int PREC, int RV>

@@ -33,10 +33,11 @@
 // straight into LDS (global_load_lds_dwordx4).  A and B are symmetric:
 // only tiles with ti <= tj are computed and each is written twice (as is and
 // mirrored).  Epilogues go through LDS so that every global access is 16
-// bytes wide.  All work of one phase for every matrix of every shape group is
-// one launch; job indices are remapped so that the tiles of one matrix share
-// an XCD (and its L2).  Workspace dimensions are padded to 128 with zeros,
+// bytes wide.  All work of one phase for the matrices of one stream (every
+// shape group the host put there) is one launch; job indices are remapped so
+// that the tiles of one matrix share an XCD (and its L2).  Workspace dimensions are padded to 128 with zeros,
 // which the iteration keeps at zero, so no loop needs a bounds check.
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -1042,6 +1043,23 @@ __global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) 
     }
 }
 
+// Dynamic LDS beyond the default 64 KiB must be requested for each kernel
+// (gfx950 has 160 KiB per CU); done once per kernel and device.
+template <auto Kernel>
+hipError_t request_lds(size_t lds) {
+    if (lds <= 65536) return hipSuccess;
+    static std::mutex mu;
+    static uint64_t done = 0;   // bit d: requested on device d
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(mu);
+    if (dev < 64 && ((done >> dev) & 1u)) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kernel), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e == hipSuccess && dev < 64) done |= (uint64_t)1 << dev;
+    return e;
+}
+
 size_t ns_update_lds_bytes(int precision, bool comp) {
     return (size_t)((precision == kNsBf16 && comp) ? 4 : 2) * Stage<128>::kSlot;
 }
@@ -1049,12 +1067,8 @@ size_t ns_update_lds_bytes(int precision, bool comp) {
 template <int PREC, bool COMP, bool FUSE>
 hipError_t launch_update(const NsArgs& a, hipStream_t s) {
     const size_t lds = ns_update_lds_bytes(PREC, COMP);
-    if (lds > 65536) {
-        // more than the default 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU)
-        static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&ns_update_kernel<PREC, COMP, FUSE>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (attr != hipSuccess) return attr;
-    }
+    const hipError_t attr = request_lds<&ns_update_kernel<PREC, COMP, FUSE>>(lds);
+    if (attr != hipSuccess) return attr;
     const int grid = (a.total_jobs + kXcds - 1) / kXcds * kXcds;
     ns_update_kernel<PREC, COMP, FUSE><<<grid, kThreads, lds, s>>>(a);
     return hipGetLastError();
@@ -1076,11 +1090,8 @@ size_t ns_sym_lds_bytes(int phase, int precision, bool comp) {
 template <int PHASE, int PREC, bool COMP>
 hipError_t launch_sym(const NsArgs& a, hipStream_t s) {
     const size_t lds = ns_sym_lds_bytes(PHASE, PREC, COMP);
-    if (lds > 65536) {
-        static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&ns_sym_kernel<PHASE, PREC, COMP>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (attr != hipSuccess) return attr;
-    }
+    const hipError_t attr = request_lds<&ns_sym_kernel<PHASE, PREC, COMP>>(lds);
+    if (attr != hipSuccess) return attr;
     const int grid = (a.total_jobs + kXcds - 1) / kXcds * kXcds;
     ns_sym_kernel<PHASE, PREC, COMP><<<grid, kSymThreads, lds, s>>>(a);
     return hipGetLastError();

@@ -88,8 +88,9 @@ def _per_dispatch(path: str, counter: str):
     return {k: tot[k] / len(disp[k]) for k in tot}
 
 
-def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes=1 << 30):
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by the copy calibration."""
+def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes=1 << 30, out_path=None):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by the copy calibration; written to out_path
+    (profiles/hbm_traffic.json by default) and returned."""
     cf = _per_dispatch(copy_fetch_csv, "FETCH_SIZE").get("copy")
     cw = _per_dispatch(copy_write_csv, "WRITE_SIZE").get("copy")
     f_scale = copy_bytes / (cf * 1024.0)
@@ -106,14 +107,15 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, cop
     out = {"source_hash": source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,
            "calibration": f"{copy_bytes} B device-to-device copy (5 runs): FETCH_SIZE {cf:.0f} KiB, WRITE_SIZE {cw:.0f} KiB per dispatch",
            "kernels": kernels}
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    path = out_path or os.path.join(ROOT, "profiles", "hbm_traffic.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
-    print(json.dumps(out, indent=1))
+    return out
 
 
-def summarize_mfma(csv_path):
-    """Executed MFMA flops per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16 / _F32, 512 flops per count)."""
+def summarize_mfma(csv_path, out_path=None):
+    """Executed MFMA flops per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16 / _F32, 512 flops per count); written
+    to out_path (profiles/mfma_counters.json by default) and returned."""
     kernels = {}
     for counter in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32"):
         for k, v in _per_dispatch(csv_path, counter).items():
@@ -122,10 +124,10 @@ def summarize_mfma(csv_path):
             kernels.setdefault(k, {})[counter] = v
     out = {"source_hash": source_hash(),
            "kernels": {k: dict(v, flops_per_launch=512.0 * sum(v.values())) for k, v in sorted(kernels.items())}}
-    path = os.path.join(ROOT, "profiles", "mfma_counters.json")
+    path = out_path or os.path.join(ROOT, "profiles", "mfma_counters.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
-    print(json.dumps(out, indent=1))
+    return out
 
 
 def mfma_counter_flops(kernel: str):
@@ -321,10 +323,10 @@ def main():
         calibrate_copy(args.calibrate_copy)
         return
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters)
+        print(json.dumps(summarize_counters(*args.summarize_counters), indent=1))
         return
     if args.summarize_mfma:
-        summarize_mfma(args.summarize_mfma)
+        print(json.dumps(summarize_mfma(args.summarize_mfma), indent=1))
         return
     import numpy as np
     import torch

@@ -130,13 +130,18 @@ __device__ inline float process_row_regs(const float* __restrict__ g, float* __r
     for (int v = 0; v < RV; ++v) {
         const int j = lane + v * kWave;
         if (j < nv) {
-            const float4 gv = g4[j], mv = m4[j];
+            // G and M are read once and M' is not read again in the step: streaming
+            // (non-temporal) accesses leave the caches to the NS chain's planes
+            const floatx4 gx = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(g4 + j));
+            const floatx4 mx = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(m4 + j));
+            const float4 gv = make_float4(gx[0], gx[1], gx[2], gx[3]), mv = make_float4(mx[0], mx[1], mx[2], mx[3]);
             float4 mn;
             u[v].x = momentum_u(gv.x, mv.x, mu, nesterov, mn.x);
             u[v].y = momentum_u(gv.y, mv.y, mu, nesterov, mn.y);
             u[v].z = momentum_u(gv.z, mv.z, mu, nesterov, mn.z);
             u[v].w = momentum_u(gv.w, mv.w, mu, nesterov, mn.w);
-            m4[j] = mn;
+            const floatx4 mnx = {mn.x, mn.y, mn.z, mn.w};
+            __builtin_nontemporal_store(mnx, reinterpret_cast<floatx4*>(m4 + j));
             ss = fmaf(u[v].x, u[v].x, ss); ss = fmaf(u[v].y, u[v].y, ss);
             ss = fmaf(u[v].z, u[v].z, ss); ss = fmaf(u[v].w, u[v].w, ss);
         }

@@ -356,9 +356,10 @@ __device__ inline void apply_store(const FusedApply& F, size_t idx, int count, c
         en[k / 4][k % 4] = fmaf(d, e[k / 4][k % 4], omd * wn[k / 4][k % 4]);
     }
     if (count >= 8 && (F.flags & kApplyVec)) {
+        // W' and E' are not read again in the step: streaming stores
         floatx4* w4 = reinterpret_cast<floatx4*>(F.param + idx);
-        w4[0] = wn[0];
-        w4[1] = wn[1];
+        __builtin_nontemporal_store(wn[0], w4);
+        __builtin_nontemporal_store(wn[1], w4 + 1);
         if (F.out) {
             floatx4 o0, o1;
 #pragma unroll
@@ -369,8 +370,8 @@ __device__ inline void apply_store(const FusedApply& F, size_t idx, int count, c
         }
         if (F.ema) {
             floatx4* e4 = reinterpret_cast<floatx4*>(F.ema + idx);
-            e4[0] = en[0];
-            e4[1] = en[1];
+            __builtin_nontemporal_store(en[0], e4);
+            __builtin_nontemporal_store(en[1], e4 + 1);
         }
         return;
     }
@@ -541,7 +542,9 @@ __global__ __launch_bounds__(kThreads, (PREC == kNsBf16 && !COMP && !FUSE) ? 3 :
             for (int p = 0; p < 4; ++p) {
                 const size_t idx = xplane + (size_t)(job.ti * kTile + h * 64 + threadIdx.x / 16 + 16 * p) * N +
                                    job.tj * kTile + 8 * (threadIdx.x % 16);
-                xl_pre[h][p] = *reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(G.xl[src]) + idx);
+                // read by this tile only: a streaming load
+                xl_pre[h][p] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(G.xl[src]) + idx));
             }
     }
     const float s = G.scale[job.slot];

@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=1337)
+    ap.add_argument("--workload", type=int, default=WORKLOAD, choices=(2, 3, 4),
+                    help="timed workload: 2 the 11-layer 512-wide model (the metric's workload), 3 the 1024-wide "
+                         "model, 4 the structured-gradient 512-wide set")
     ap.add_argument("--rotate", type=int, default=2, help="independent state copies used in turn (MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true", help="skip the steps/s of the other workloads")
@@ -88,6 +91,9 @@ def _per_dispatch(path: str, counter: str):
     return {k: tot[k] / len(disp[k]) for k in tot}
 
 
+COUNTER_WORKLOAD = "model11L512"   # the counter runs profile the default bench workload
+
+
 def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes=1 << 30, out_path=None):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by the copy calibration; written to out_path
     (profiles/hbm_traffic.json by default) and returned."""
@@ -104,7 +110,7 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, cop
         fb = fetch[k] * 1024.0 * f_scale
         wb = write[k] * 1024.0 * w_scale
         kernels[k] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb)}
-    out = {"source_hash": source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,
+    out = {"source_hash": source_hash(), "workload": COUNTER_WORKLOAD, "fetch_scale": f_scale, "write_scale": w_scale,
            "calibration": f"{copy_bytes} B device-to-device copy (5 runs): FETCH_SIZE {cf:.0f} KiB, WRITE_SIZE {cw:.0f} KiB per dispatch",
            "kernels": kernels}
     path = out_path or os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -122,7 +128,7 @@ def summarize_mfma(csv_path, out_path=None):
             if k == "copy":
                 continue
             kernels.setdefault(k, {})[counter] = v
-    out = {"source_hash": source_hash(),
+    out = {"source_hash": source_hash(), "workload": COUNTER_WORKLOAD,
            "kernels": {k: dict(v, flops_per_launch=512.0 * sum(v.values())) for k, v in sorted(kernels.items())}}
     path = out_path or os.path.join(ROOT, "profiles", "mfma_counters.json")
     with open(path, "w") as f:
@@ -130,14 +136,22 @@ def summarize_mfma(csv_path, out_path=None):
     return out
 
 
-def mfma_counter_flops(kernel: str):
-    """Executed MFMA flops per launch from the committed counter summary, if it matches these sources."""
-    path = os.path.join(ROOT, "profiles", "mfma_counters.json")
+def _counter_file(name: str, workload: str):
+    """A committed counter summary, if it was taken on these sources and this workload."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         data = json.load(f)
-    if data.get("source_hash") != source_hash():
+    if data.get("source_hash") != source_hash() or data.get("workload", COUNTER_WORKLOAD) != workload:
+        return None
+    return data
+
+
+def mfma_counter_flops(kernel: str, workload: str = COUNTER_WORKLOAD):
+    """Executed MFMA flops per launch from the committed counter summary, if it matches these sources."""
+    data = _counter_file("mfma_counters.json", workload)
+    if data is None:
         return None
     k = data.get("kernels", {}).get(kernel)
     return None if k is None else k.get("flops_per_launch")
@@ -208,14 +222,10 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel: str):
+def traffic_for(kernel: str, workload: str = COUNTER_WORKLOAD):
     """HBM bytes per launch from the committed counter summary, if it matches these sources."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        data = json.load(f)
-    if data.get("source_hash") != source_hash():
+    data = _counter_file("hbm_traffic.json", workload)
+    if data is None:
         return None
     k = data.get("kernels", {}).get(kernel)
     return None if k is None else k.get("bytes_per_launch")
@@ -333,7 +343,7 @@ def main():
     import muon_optimizer_step_amd as ms
     import workloads as wl
 
-    w = wl.workload(WORKLOAD)
+    w = wl.workload(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     coeffs = wl.coeff_table(w, args.seed).tolist()
@@ -452,13 +462,19 @@ def main():
     ns_flops = sum(kernels[k].get("flops_per_step", 0.0) for k in ns_names)
     ns_tflops = ns_flops / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else None
     # executed MFMA work (counters: compensation products and symmetry savings included)
-    counted = [mfma_counter_flops(k) for k in ns_names]
+    counted = [mfma_counter_flops(k, w.name) for k in ns_names]
     ns_counted = (sum(c * kernels[k]["launches_per_step"] for c, k in zip(counted, ns_names))
                   if counted and all(c is not None for c in counted) else None)
-    traffic = traffic_for(dom)
+    traffic = traffic_for(dom, w.name)
 
+    describe = {
+        2: "66 matrices (11 layers x Q/K/V/O/up/down at d=512)",
+        3: "66 matrices (11 layers x Q/K/V/O/up/down at d=1024)",
+        4: "66 matrices (11 layers x Q/K/V/O/up/down at d=512) with rank-8 structured gradients and a drawn "
+           "coefficient table",
+    }[args.workload]
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == WORKLOAD else f"Muon+EMA steps/s ({w.name})",
         "value": round(value, 3),
         "unit": "steps/s",
         "n_gpus": 1,
@@ -470,8 +486,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: muon_step over 66 matrices (11 layers x Q/K/V/O/up/down at d=512), "
-                               f"5 NS steps bf16, EMA over all {w.n_params:,} fp32 params "
+        "config": {"workload": f"{w.name}: muon_step over {describe}, "
+                               f"{w.ns_steps} NS steps bf16, EMA over all {w.n_params:,} fp32 params "
                                f"(matrices inside the step, {len(w.extras)} other tensors in ema_update)",
                    "matrices": nm, "params": w.n_params, "ns_steps": w.ns_steps, "seed": args.seed,
                    "state_copies": args.rotate},

@@ -71,7 +71,7 @@ def test_traffic_summary_scales_by_the_copy_and_averages_per_dispatch(tmp_path):
     assert upd["bytes_per_launch"] == upd["fetch_bytes"] + upd["write_bytes"]
     assert out["kernels"]["ns_gram_bf16"]["bytes_per_launch"] == 10 * 1024 * 2 + 4 * 1024
     assert "copy" not in out["kernels"]
-    assert out["source_hash"] == bench.source_hash()
+    assert out["source_hash"] == bench.source_hash() and out["workload"] == "model11L512"
     with open(out_path) as f:
         assert json.load(f) == out
 
@@ -91,8 +91,18 @@ def test_committed_summaries_cover_the_bench_kernels():
         with open(os.path.join(ROOT, "profiles", name)) as f:
             data = json.load(f)
         assert len(data["source_hash"]) == 16
+        assert data["workload"] == "model11L512"
         for k in ("prep", "ns_gram_bf16", "ns_square_bf16", "ns_update_bf16", "ns_update_apply_bf16", "ema"):
             assert k in data["kernels"], (name, k)
+
+
+def test_counter_figures_are_used_only_for_the_workload_they_were_taken_on():
+    """Counters taken on the 512-wide model say nothing about another workload's kernels of the same name."""
+    if bench.traffic_for("ns_update_bf16", "model11L512") is None:
+        pytest.skip("committed counter summaries are from other sources")
+    assert bench.traffic_for("ns_update_bf16", "model11L1024") is None
+    assert bench.mfma_counter_flops("ns_gram_bf16", "model11L1024") is None
+    assert bench.mfma_counter_flops("ns_gram_bf16", "model11L512") > 0
 
 
 def test_work_model_of_the_bench_workload():

@@ -282,6 +282,32 @@ int validate_pointers(const muon_tensor_t* t, int32_t n) {
     return check_overlaps(spans, "muon_step");
 }
 
+// Scale exponents of the base bf16 square's e4m3 operands, per NS iteration.
+// X0 has sigma_max <= 1 (Frobenius scaling); iteration k maps every singular
+// value through p_k(s) = a s + b s^3 + c s^5, so sigma_max(X_k) is bounded by
+// the maximum of |p| over [0, bound of X_{k-1}] (sampled, with a margin for
+// the bf16 rounding), and |A_ij| <= sigma_max(X_k)^2.  A hi is scaled by 2^sa
+// and A lo (at most 2^-8 |A|) by 2^(sa + 8) so that both stay under 224 in
+// e4m3 (which saturates at 448).
+void f8_scale_exponents(const float* coeffs, int ns_steps, int* sa) {
+    double bound = 1.0;   // sigma_max of X_k
+    for (int k = 0; k < ns_steps; ++k) {
+        if (!(bound <= 1e30)) bound = 1e30;   // also catches NaN: far past any useful table
+        const double amax = bound * bound * 1.05;
+        int e = 64;
+        if (amax > 0.0) e = std::max(-64, std::min(64, (int)std::floor(std::log2(224.0 / amax))));
+        sa[k] = e;
+        const double a = coeffs[3 * k], b = coeffs[3 * k + 1], c = coeffs[3 * k + 2];
+        const double hi = bound * 1.02;
+        double m = 0.0;
+        for (int i = 0; i <= 4096; ++i) {
+            const double x = hi * i / 4096.0, x2 = x * x;
+            m = std::max(m, std::fabs(x * (a + x2 * (b + c * x2))));
+        }
+        bound = m * 1.02;
+    }
+}
+
 // Streaming tensors (EMA, AdamW): at most 2^30 workgroups per launch, so a
 // single tensor may hold at most this many elements (4 Ti elements; far above
 // any device memory).
@@ -417,6 +443,8 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
         if (cnt > kMaxFrobSlots) fold_frob = false;
     }
     const float keep = 1.0f - lr * weight_decay;
+    int f8_sa[MUON_MAX_NS_STEPS];
+    f8_scale_exponents(ns_coeffs, ns_steps, f8_sa);
     // 16-byte accesses to the caller's W / O / EMA rows
     auto vec_ok = [](const muon_tensor_t& x) {
         return (x.cols % 4 == 0) && (reinterpret_cast<uintptr_t>(x.param) % 16 == 0) &&
@@ -540,6 +568,8 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
             a.one_minus_decay = 1.0f - ema_decay;
             a.fold_frob = fold_frob && phase == kGram && k == 0;
             a.rowsq = rowsq;
+            a.f8_sa = f8_sa[k];
+            a.f8_sl = f8_sa[k] + 8;
             int jobs = 0, napply = 0, nfrob = 0;
             for (int q : ls.parts) {
                 const Part& pt = parts[q];

@@ -79,9 +79,9 @@ struct NsGroup {
     void* x[2];      // bf16: hi planes (ping-pong); fp32: X planes.  [count][M][N]
     void* xl[2];     // bf16: lo planes; fp32: unused
     void* a_hi;      // bf16: hi of A; fp32: A.  [count][M][M]
-    void* a_lo;      // bf16: lo of A; fp32: unused
+    void* a_lo;      // compensated: bf16 lo of A; base: e4m3 bytes of lo * 2^sl; fp32: unused
     void* b;         // bf16: hi of B; fp32: B.  [count][M][M]
-    void* b_lo;      // bf16: lo of B (written and read by the compensated kernels)
+    void* b_lo;      // compensated: bf16 lo of B; base: e4m3 bytes of A hi * 2^sa (for the square)
     float* scale;        // [count] Frobenius scale of X0 (written by a folding first Gram)
     int count, M, N;     // padded, multiples of 128
     int job_begin;
@@ -98,6 +98,7 @@ struct NsArgs {
     int fuse_apply;  // last update: write W' (and O) instead of X
     float keep;      // 1 - lr*wd
     float decay, one_minus_decay;  // weight EMA
+    int f8_sa, f8_sl;      // base bf16 Gram / square: e4m3 scale exponents of A hi and A lo
     int fold_frob;         // first Gram: compute the Frobenius scale from the row sums
     const float* rowsq;    // base of the per-row sums (fold_frob)
     union {

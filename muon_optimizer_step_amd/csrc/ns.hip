@@ -13,10 +13,11 @@
 // plus its remainder: one byte per element in units of 2^-15 of hi's binade
 // for the base groups (lo8_encode), a second bf16 plane for the compensated
 // ones, whose products use it as an MFMA operand.  MFMA operands are bf16 and
-// accumulate in fp32.  A is split into bf16 hi + lo planes and A A is formed
-// as hi*hi + hi*lo + lo*hi, because the plain bf16 square loses the small
+// accumulate in fp32.  A is split into hi + lo and A A is formed as
+// hi*hi + hi*lo + lo*hi, because the plain bf16 square loses the small
 // singular directions that the iteration amplifies; the a X term always uses
-// hi + lo.
+// hi + lo.  In the base groups the two cross products run on e4m3 operands
+// (fp8 MFMA, see below).
 //   base:        A = Xh Xh^T,  B X = Bh Xh
 //   compensated: A = Xh Xh^T + Xh Xl^T + Xl Xh^T,  B X = Bh Xh + Bl Xh + Bh Xl
 // The base products keep the error within 2e-2 of float64 once the short side
@@ -68,6 +69,9 @@ static_assert(kStageBytes <= 2 * Stage<128>::kSlot, "epilogue staging must fit i
 
 #ifndef NS_SYM_DMA
 #define NS_SYM_DMA 1   // Gram operands loaded straight into LDS (double-buffered)
+#endif
+#ifndef NS_SQ_FP8
+#define NS_SQ_FP8 1    // base bf16 square: cross terms Ah Al + Al Ah on the fp8 MFMA
 #endif
 
 // Direct loads for the phases with two operand tiles per stage (the split
@@ -303,6 +307,67 @@ __device__ inline void store8(void* hi, void* lo, size_t idx, const float* v) {
         d[0] = a;
         d[1] = b;
     }
+}
+
+// fp8 cross terms of the base square.  A = Ah + Al with Ah = rne_bf16(A); the
+// square needs Ah Ah + Ah Al + Al Ah, and the cross terms are ~2^-8 of A A, so
+// OCP e4m3 operands (3 mantissa bits) carry them with an error far below the
+// bf16 rounding of B that follows; what the base precision cannot drop is the
+// cross term as a whole.  The Gram stores, besides Ah in bf16, e4m3(Al * 2^sl)
+// and e4m3(Ah * 2^sa), one byte per element each; the square runs
+// v_mfma_scale_f32_32x32x64_f8f6f4 on them with E8M0 scales 2^-sa and 2^-sl,
+// so the cross products land unscaled in the same accumulators as Ah Ah.  sa
+// and sl (= sa + 8) come from the host's bound on |A| for the iteration, which
+// keeps every scaled operand under 224 (e4m3's largest value is 448).
+typedef int v8i __attribute__((ext_vector_type(8)));
+constexpr int kF8Pitch = 64 + 16;              // LDS row pitch of an e4m3 tile (64 K bytes per stage)
+constexpr int kF8TileBytes = kTile * kF8Pitch;
+
+// Four floats -> four e4m3 bytes (round to nearest even), a first.  Inputs
+// are clamped to the e4m3 range first: the scales keep them under 224, and a
+// table that drives X far past its bound then saturates instead of producing
+// NaN codes (the conversion writes NaN from 480 up).
+__device__ inline uint32_t f8_pack4(float a, float b, float c, float d) {
+    a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+    b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+    c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+    d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+__device__ inline float f8_decode(uint32_t word, int byte) {
+    switch (byte) {
+        case 0: return __builtin_amdgcn_cvt_f32_fp8((int)word, 0);
+        case 1: return __builtin_amdgcn_cvt_f32_fp8((int)word, 1);
+        case 2: return __builtin_amdgcn_cvt_f32_fp8((int)word, 2);
+        default: return __builtin_amdgcn_cvt_f32_fp8((int)word, 3);
+    }
+}
+
+// Store 8 A values of the base Gram: the bf16 hi plane, and two e4m3 byte
+// planes for the square's cross terms, lo * 2^sl and hi * 2^sa.
+__device__ inline void store8_hi_f8lo(void* hi, void* lo, void* hi8, size_t idx, const float* v, float lo_scale,
+                                      float hi_scale) {
+    u32x4 wh;
+    float r[8], q[8];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const bf16 h0 = to_bf16(v[2 * p]), h1 = to_bf16(v[2 * p + 1]);
+        wh[p] = bf16_bits(h0) | (bf16_bits(h1) << 16);
+        r[2 * p] = (v[2 * p] - from_bf16(h0)) * lo_scale;
+        r[2 * p + 1] = (v[2 * p + 1] - from_bf16(h1)) * lo_scale;
+        q[2 * p] = from_bf16(h0) * hi_scale;
+        q[2 * p + 1] = from_bf16(h1) * hi_scale;
+    }
+    u32x2 wl;
+    wl[0] = f8_pack4(r[0], r[1], r[2], r[3]);
+    wl[1] = f8_pack4(r[4], r[5], r[6], r[7]);
+    *reinterpret_cast<u32x4*>(static_cast<bf16*>(hi) + idx) = wh;
+    *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(lo) + idx) = wl;
+    u32x2 w8;
+    w8[0] = f8_pack4(q[0], q[1], q[2], q[3]);
+    w8[1] = f8_pack4(q[4], q[5], q[6], q[7]);
+    *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(hi8) + idx) = w8;
 }
 
 // Store 8 X values as a bf16 hi plane and a byte lo plane (lo8_encode).
@@ -676,6 +741,8 @@ __global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) 
     constexpr int kBK = kRB / (int)sizeof(T);
     constexpr int kSlot = Stage<kRB>::kSlot;
     constexpr int kStageTiles = kSplit ? 4 : 2;
+    // base bf16: A lo is an e4m3 byte plane and the square's cross terms run on the fp8 MFMA
+    constexpr bool kF8 = NS_SQ_FP8 != 0 && PREC == kNsBf16 && !COMP;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     Job job;
@@ -881,6 +948,112 @@ __global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) 
             wait_lgkmcnt0();
             barrier_only();
         }
+    } else if constexpr (kF8 && PHASE == kSquare) {
+        // Base square, cross terms on the fp8 MFMA.  Per group and stage (64 K):
+        // the bf16 Ah row tiles of both sides (for Ah Ah) and the e4m3 tiles of
+        // Ah and Al of both sides (the byte planes the Gram stored), 80-byte
+        // rows, K in natural order.  Same half-step schedule as the register
+        // path below.
+        static_assert(kRB == 128, "64 K per stage");
+        const int sa = args.f8_sa, sl = args.f8_sl;
+        uint8_t* const f8base = lds + 2 * 2 * kSlot;   // after both groups' bf16 tiles
+        auto btile = [&](int side) -> uint8_t* { return lds + (kg * 2 + (diag ? 0 : side)) * kSlot; };
+        auto ftile = [&](int which) -> uint8_t* {      // 0: Ah ti, 1: Ah tj, 2: Al ti, 3: Al tj
+            if (diag && which == 1) which = 0;
+            if (diag && which == 3) which = 2;
+            return f8base + (kg * 4 + which) * kF8TileBytes;
+        };
+        const uint8_t* g8a = static_cast<const uint8_t*>(G.a_lo) + aplane + (size_t)job.ti * kTile * M;
+        const uint8_t* g8b = static_cast<const uint8_t*>(G.a_lo) + aplane + (size_t)job.tj * kTile * M;
+        const uint8_t* h8a = static_cast<const uint8_t*>(G.b_lo) + aplane + (size_t)job.ti * kTile * M;
+        const uint8_t* h8b = static_cast<const uint8_t*>(G.b_lo) + aplane + (size_t)job.tj * kTile * M;
+        const int t = tid % kThreads;
+        NtLoader<kRB> la, lb;
+        u32x4 l8a[2], l8b[2];   // Al bytes: row t/4 + 64q, 16-byte chunk t%4 of the stage's 64
+        u32x4 h8va[2], h8vb[2]; // Ah e4m3 bytes, same mapping
+        auto issue = [&](int kt) {
+            la.load(ga, ld_bytes, kt * kRB);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const size_t o = (size_t)(t / 4 + 64 * q) * M + kt * 64 + (t % 4) * 16;
+                l8a[q] = *reinterpret_cast<const u32x4*>(g8a + o);
+                h8va[q] = *reinterpret_cast<const u32x4*>(h8a + o);
+            }
+            if (!diag) {
+                lb.load(gb, ld_bytes, kt * kRB);
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const size_t o = (size_t)(t / 4 + 64 * q) * M + kt * 64 + (t % 4) * 16;
+                    l8b[q] = *reinterpret_cast<const u32x4*>(g8b + o);
+                    h8vb[q] = *reinterpret_cast<const u32x4*>(h8b + o);
+                }
+            }
+        };
+        auto commit_side = [&](const NtLoader<kRB>& lh, const u32x4* l8, const u32x4* h8, int side) {
+            lh.store(btile(side));
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                *reinterpret_cast<u32x4*>(ftile(side) + (t / 4 + 64 * q) * kF8Pitch + (t % 4) * 16) = h8[q];
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                *reinterpret_cast<u32x4*>(ftile(2 + side) + (t / 4 + 64 * q) * kF8Pitch + (t % 4) * 16) = l8[q];
+        };
+        auto commit = [&]() {
+            commit_side(la, l8a, h8va, 0);
+            if (!diag) commit_side(lb, l8b, h8vb, 1);
+        };
+        auto f8frag = [&](const uint8_t* tl, int row) -> v8i {
+            const uint8_t* p = tl + row * kF8Pitch + (lane / 32) * 32;
+            const u32x4 x0 = *reinterpret_cast<const u32x4*>(p);
+            const u32x4 x1 = *reinterpret_cast<const u32x4*>(p + 16);
+            return v8i{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+        };
+        auto compute = [&]() {
+            const uint8_t* ta = btile(0);
+            const uint8_t* tb = btile(1);
+#pragma unroll
+            for (int kc = 0; kc < kRB / 32; ++kc) {
+                u32x4 fa[2], fb[2];
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi) fa[mi] = lds_frag<kRB>(ta, wm * 64 + mi * 32 + lane % 32, kc, lane);
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni) fb[ni] = lds_frag<kRB>(tb, wn * 64 + ni * 32 + lane % 32, kc, lane);
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < 2; ++ni) mfma_chunk<PREC>(acc[mi][ni], fa[mi], fb[ni]);
+            }
+            // Ah_i Al_j^T, then Al_i Ah_j^T: two A-side fragments and one B-side
+            // fragment live at a time
+#pragma unroll
+            for (int term = 0; term < 2; ++term) {
+                const int sx = term == 0 ? sa : sl, sy = term == 0 ? sl : sa;
+                v8i fx[2];
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi) fx[mi] = f8frag(ftile(term == 0 ? 0 : 2), wm * 64 + mi * 32 + lane % 32);
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni) {
+                    const v8i fy = f8frag(ftile(term == 0 ? 3 : 1), wn * 64 + ni * 32 + lane % 32);
+#pragma unroll
+                    for (int mi = 0; mi < 2; ++mi)
+                        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fx[mi], fy, acc[mi][ni], 0, 0, 0,
+                                                                                     127 - sx, 0, 127 - sy);
+                }
+            }
+        };
+        if (kg < nk) issue(kg);
+        __syncthreads();
+        for (int h = 0; h <= nk; ++h) {
+            if ((h & 1) == kg) {
+                if (h < nk) {
+                    commit();
+                    if (h + 2 < nk) issue(h + 2);
+                }
+            } else if (h > 0 && h - 1 < nk) {
+                compute();
+            }
+            __syncthreads();
+        }
     } else {
         NtLoader<kRB> la, lb, lal, lbl;
         auto issue = [&](int kt) {
@@ -934,7 +1107,12 @@ __global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) 
         for (int p = 0; p < 4; ++p) {
             const size_t idx = aplane + (size_t)(job.ti * kTile + tid / 16 + 32 * p) * M + job.tj * kTile + lc;
             a_pre[p][0] = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(G.a_hi) + idx);
-            a_pre[p][1] = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(G.a_lo) + idx);
+            if constexpr (kF8) {
+                const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(G.a_lo) + idx);
+                a_pre[p][1] = u32x4{w[0], w[1], 0u, 0u};
+            } else {
+                a_pre[p][1] = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(G.a_lo) + idx);
+            }
         }
     }
     // The two groups hold partial sums of the same tile.  Group g finishes the
@@ -984,6 +1162,8 @@ __global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) 
     __syncthreads();
     const float s = fold ? fscale : G.scale[job.slot];
     const float sc = args.first ? s * s : 1.0f;
+    const float f8_lo_scale = ldexpf(1.0f, args.f8_sl), f8_lo_inv = ldexpf(1.0f, -args.f8_sl);
+    const float f8_hi_scale = ldexpf(1.0f, args.f8_sa);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int lr = tid / 16 + 32 * p;
@@ -999,12 +1179,21 @@ __global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) 
         if (PHASE == kGram) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] *= sc;
-            store8<PREC>(static_cast<T*>(G.a_hi) + aplane, static_cast<T*>(G.a_lo) + aplane, idx, v);
+            if constexpr (kF8)
+                store8_hi_f8lo(static_cast<bf16*>(G.a_hi) + aplane, static_cast<uint8_t*>(G.a_lo) + aplane,
+                               static_cast<uint8_t*>(G.b_lo) + aplane, idx, v, f8_lo_scale, f8_hi_scale);
+            else
+                store8<PREC>(static_cast<T*>(G.a_hi) + aplane, static_cast<T*>(G.a_lo) + aplane, idx, v);
         } else {
             float ah[8], al[8];
             if constexpr (kPreA) {
                 unpack8(a_pre[p][0], ah);
-                unpack8(a_pre[p][1], al);
+                if constexpr (kF8) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) al[e] = f8_decode(a_pre[p][1][e / 4], e % 4) * f8_lo_inv;
+                } else {
+                    unpack8(a_pre[p][1], al);
+                }
             } else {
                 load8<PREC>(static_cast<const T*>(G.a_hi) + aplane, idx, ah);
                 if constexpr (PREC == kNsBf16) load8<PREC>(static_cast<const T*>(G.a_lo) + aplane, idx, al);
@@ -1037,7 +1226,10 @@ __global__ __launch_bounds__(kSymThreads) void ns_sym_kernel(const NsArgs args) 
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = stage[(chunk * 8 + e) * kStagePitch + stage_col(chunk * 8 + e, c)];
             const size_t idx = (size_t)(job.tj * kTile + c) * M + job.ti * kTile + chunk * 8;
-            if (PHASE == kGram)
+            if (PHASE == kGram && kF8)
+                store8_hi_f8lo(static_cast<bf16*>(G.a_hi) + aplane, static_cast<uint8_t*>(G.a_lo) + aplane,
+                               static_cast<uint8_t*>(G.b_lo) + aplane, idx, v, f8_lo_scale, f8_hi_scale);
+            else if (PHASE == kGram)
                 store8<PREC>(static_cast<T*>(G.a_hi) + aplane, static_cast<T*>(G.a_lo) + aplane, idx, v);
             else
                 store8<PREC>(static_cast<T*>(G.b) + aplane, COMP ? static_cast<T*>(G.b_lo) + aplane : nullptr,
@@ -1080,6 +1272,9 @@ hipError_t launch_update(const NsArgs& a, hipStream_t s) {
 size_t ns_sym_lds_bytes(int phase, int precision, bool comp) {
     const bool split = precision == kNsBf16 && (phase == kSquare || comp);
     const bool dma = ns_sym_dma(phase, precision, comp);
+    if (NS_SQ_FP8 != 0 && phase == kSquare && precision == kNsBf16 && !comp)
+        // both groups: bf16 Ah tiles of both sides, e4m3 Ah and Al tiles of both sides
+        return std::max((size_t)2 * 2 * Stage<128>::kSlot + (size_t)2 * 4 * kF8TileBytes, (size_t)kSymEpilogueBytes);
     const int rb = ns_sym_stage_bytes(phase, precision, comp, dma);
     if (dma) {
         // two buffers x two groups x tiles, plus the 8 floats of the folded Frobenius sum

@@ -209,3 +209,26 @@ def test_single_iteration_isolates_each_product(ns_precision, tol, triple):
     for i, (r, c) in enumerate(shapes):
         gu.check_layers(mats[i], grads[i], moms[i], w_gpu[i], m_gpu[i], o_gpu[i], lr=0.02, momentum=0.9, wd=0.0,
                         coeffs=coeffs, nesterov=True, row_norm=True, ns_tol=tol, label=f"{r}x{c} {triple}")
+
+
+@pytest.mark.parametrize("ns_precision,tol", [(1, 1e-5), (0, gu.NS_TOL_BF16), (2, gu.NS_TOL_BF16X3)])
+@pytest.mark.parametrize("table", [
+    [(16.0, 0.0, 0.0), (0.0, 0.0, 2.0 ** -16)],                    # X grows 16x, then the square alone
+    [(4.0, 0.0, 0.0), (4.0, 0.0, 0.0), (0.0, 0.0, 2.0 ** -16)],    # the same in two steps
+    [(1.0 / 16.0, 0.0, 0.0), (0.0, 0.0, 2.0 ** 16)],                # X shrinks 16x first
+])
+def test_tables_that_rescale_x(ns_precision, tol, table):
+    """Coefficient tables that scale X up or down before an iteration whose output is the square alone
+    ((X Xt)^2 X): the square's low-order products must follow |A| wherever the table takes it, not
+    assume the singular values stay near 1."""
+    shapes = [(256, 512), (512, 256), (384, 384)]
+    rng = np.random.default_rng(11)
+    mats = [(0.02 * rng.standard_normal(s)).astype(np.float32) for s in shapes]
+    grads = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    moms = [(0.1 * rng.standard_normal(s)).astype(np.float32) for s in shapes]
+    gu.say(f"[parity] rescaling table {table} prec={ns_precision}")
+    w_gpu, m_gpu, o_gpu, _ = gu.gpu_step(mats, grads, moms, lr=0.02, momentum=0.9, wd=0.0, coeffs=table,
+                                         ns_precision=ns_precision)
+    for i, (r, c) in enumerate(shapes):
+        gu.check_layers(mats[i], grads[i], moms[i], w_gpu[i], m_gpu[i], o_gpu[i], lr=0.02, momentum=0.9, wd=0.0,
+                        coeffs=np.asarray(table), nesterov=True, row_norm=True, ns_tol=tol, label=f"{r}x{c}")

@@ -52,7 +52,8 @@ def parse():
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter files of this bench and of "
                          "--calibrate-copy into profiles/hbm_traffic.json, then exit (no GPU needed)")
     ap.add_argument("--summarize-mfma", metavar="MOPS_CSV",
-                    help="turn a rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 counter "
+                    help="turn a rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 "
+                         "SQ_INSTS_VALU_MFMA_MOPS_F8 counter "
                          "file of this bench into profiles/mfma_counters.json, then exit (no GPU needed)")
     return ap.parse_args()
 
@@ -120,10 +121,10 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, cop
 
 
 def summarize_mfma(csv_path, out_path=None):
-    """Executed MFMA flops per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16 / _F32, 512 flops per count); written
-    to out_path (profiles/mfma_counters.json by default) and returned."""
+    """Executed MFMA flops per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16 / _F32 / _F8, 512 flops per count);
+    written to out_path (profiles/mfma_counters.json by default) and returned."""
     kernels = {}
-    for counter in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32"):
+    for counter in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_INSTS_VALU_MFMA_MOPS_F8"):
         for k, v in _per_dispatch(csv_path, counter).items():
             if k == "copy":
                 continue

@@ -294,9 +294,9 @@ void f8_scale_exponents(const float* coeffs, int ns_steps, int* sa) {
     for (int k = 0; k < ns_steps; ++k) {
         if (!(bound <= 1e30)) bound = 1e30;   // also catches NaN: far past any useful table
         const double amax = bound * bound * 1.05;
-        int e = 64;
-        if (amax > 0.0) e = std::max(-64, std::min(64, (int)std::floor(std::log2(224.0 / amax))));
-        sa[k] = e;
+        double e = 64.0;   // clamped before the conversion to int
+        if (amax > 0.0) e = std::max(-64.0, std::min(64.0, std::floor(std::log2(224.0) - std::log2(amax))));
+        sa[k] = (int)e;
         const double a = coeffs[3 * k], b = coeffs[3 * k + 1], c = coeffs[3 * k + 2];
         const double hi = bound * 1.02;
         double m = 0.0;

@@ -216,6 +216,8 @@ def test_single_iteration_isolates_each_product(ns_precision, tol, triple):
     [(16.0, 0.0, 0.0), (0.0, 0.0, 2.0 ** -16)],                    # X grows 16x, then the square alone
     [(4.0, 0.0, 0.0), (4.0, 0.0, 0.0), (0.0, 0.0, 2.0 ** -16)],    # the same in two steps
     [(1.0 / 16.0, 0.0, 0.0), (0.0, 0.0, 2.0 ** 16)],                # X shrinks 16x first
+    [(2.0 ** 20, 0.0, 0.0), (0.0, 0.0, 2.0 ** -80)],                # far outside the unit range, both ways
+    [(2.0 ** -20, 0.0, 0.0), (0.0, 0.0, 2.0 ** 80)],
 ])
 def test_tables_that_rescale_x(ns_precision, tol, table):
     """Coefficient tables that scale X up or down before an iteration whose output is the square alone

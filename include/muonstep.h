@@ -99,9 +99,10 @@ size_t muon_workspace_size(const muon_tensor_t* tensors, int32_t n, int32_t ns_p
  *                 product runs on MFMA with fp32 accumulation; X is carried to
  *                 ~16 significant bits (bf16 hi + lo) or in fp32.  MUON_NS_BF16
  *                 forms X X^T and B X from the bf16 hi parts only (and A A from
- *                 hi*hi + hi*lo + lo*hi) for matrices whose short side is at
- *                 least 192, and the compensated products (hi*hi + hi*lo +
- *                 lo*hi everywhere) below that; MUON_NS_BF16X3 compensates every
+ *                 hi*hi in bf16 plus hi*lo + lo*hi on e4m3 operands) for
+ *                 matrices whose short side is at least 192, and the
+ *                 compensated products (hi*hi + hi*lo + lo*hi in bf16
+ *                 everywhere) below that; MUON_NS_BF16X3 compensates every
  *                 matrix.
  *   ema_decay     EMA decay d for the tensors whose ema is set; finite, in [0, 1]
  *                 (checked on every call).

@@ -85,6 +85,13 @@ def test_full_model_512d_with_ema():
     _check_ema(w, st, w_gpu, w.ema_decay)
 
 
+@pytest.mark.parametrize("seed", wl.ROBUST_SEEDS)
+def test_full_model_512d_robustness_seeds(seed):
+    """The bench workload on the other seeds, the NS output checked on a different sample of matrices
+    (one per stored shape, from other layers)."""
+    _run_workload(2, seed, o_sample={60, 55, 50, 45, 40, 65})
+
+
 def test_full_model_1024d_with_ema():
     w, st, w_gpu = _run_workload(3, wl.PRIMARY_SEED, o_sample={0, 7, 28, 35})
     _check_ema(w, st, w_gpu, w.ema_decay)

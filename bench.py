@@ -214,6 +214,31 @@ def kernel_model(w, fused=True):
     return model
 
 
+def roof_of(kernel: str) -> str:
+    """"mfma" for the Newton-Schulz products, "hbm" for the streaming passes."""
+    return "mfma" if kernel.startswith("ns_") else "hbm"
+
+
+def streaming_fractions(kernels, workload: str):
+    """HBM rate of the streaming passes (momentum prep, EMA) by algorithmic bytes and, where the
+    committed counter summary matches these sources, by FETCH_SIZE + WRITE_SIZE bytes."""
+    out = {}
+    for k in ("prep", "ema", "apply"):
+        if k not in kernels or "bytes_per_launch" not in kernels[k]:
+            continue
+        d = kernels[k]
+        e = {"avg_launch_us": round(d["avg_us"], 3), "algorithmic_bytes_per_launch": round(d["bytes_per_launch"]),
+             "algorithmic_gbs": round(d["bytes_per_launch"] / (d["avg_us"] * 1e-6) / 1e9, 1)}
+        e["algorithmic_frac"] = round(e["algorithmic_gbs"] / HBM_PEAK_GBS, 4)
+        t = traffic_for(k, workload)
+        if t is not None:
+            e["counter_bytes_per_launch"] = t
+            e["counter_gbs"] = round(t / (d["avg_us"] * 1e-6) / 1e9, 1)
+            e["counter_frac"] = round(e["counter_gbs"] / HBM_PEAK_GBS, 4)
+        out[k] = e
+    return out
+
+
 def source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "muon_optimizer_step_amd", "csrc")
@@ -269,7 +294,8 @@ def cpu_baseline(w, seed, target_s):
         t1 = time.perf_counter()
         one_step()
         el1 = time.perf_counter() - t1
-    return {"value": reps / el, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+    return {"value": reps / el, "unit": "steps/s", "cores": int(threads), "host_cpus": os.cpu_count(),
+            "kind": "oracle",
             "sample": f"{reps} full step(s) of the float64 NumPy oracle on the same workload "
                       f"(66 matrices + EMA over {w.n_params:,} params), {el:.1f} s",
             "blas": blas, "single_thread": {"value": 1.0 / el1, "unit": "steps/s", "sample": f"1 step, {el1:.1f} s"}}
@@ -451,10 +477,10 @@ def main():
         kernels[name] = entry
     dom = max((k for k in kernels if k in model), key=lambda k: kernels[k]["ms_per_step"])
     d = kernels[dom]
-    # the binding roofline: whichever of MFMA time and HBM time is longer at peak
-    t_mfma = d["flops_per_step"] / (BF16_PEAK_TFLOPS * 1e12)
-    t_hbm = d["bytes_per_step"] / (HBM_PEAK_GBS * 1e9)
-    if t_mfma >= t_hbm:
+    # The roof of each kernel is fixed by what it computes: the Newton-Schulz
+    # products are dense contractions (bf16 MFMA, dense-formula flops), the
+    # streaming passes move bytes (HBM).
+    if roof_of(dom) == "mfma":
         bound, achieved, peak, unit = "mfma", d["tflops"], BF16_PEAK_TFLOPS, "TFLOP/s"
     else:
         bound, achieved, peak, unit = "hbm", d["gbs"], HBM_PEAK_GBS, "GB/s"
@@ -494,10 +520,12 @@ def main():
                    "state_copies": args.rotate},
         "roofline": {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "algorithmic_flops_per_launch": round(d["flops_per_step"] / d["launches_per_step"]),
                      "algorithmic_bytes_per_launch": round(d["bytes_per_launch"]),
                      "avg_launch_us": round(d["avg_us"], 3),
                      "mfma_frac": round(d.get("tflops", 0.0) / BF16_PEAK_TFLOPS, 4),
                      "hbm_frac": round(d["gbs"] / HBM_PEAK_GBS, 4)},
+        "streaming": streaming_fractions(kernels, w.name),
         "ns": {"tflops_over_summed_kernel_time": round(ns_tflops, 2) if ns_tflops else None,
                "frac_of_bf16_peak": round(ns_tflops / BF16_PEAK_TFLOPS, 4) if ns_tflops else None,
                "summed_kernel_ms_per_step": round(ns_ms, 4),

@@ -116,7 +116,14 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
               size_t workspace_bytes, void* stream);
 
 /* Weight EMA over n fp32 tensors: ema[i][j] = decay*ema[i][j] + (1-decay)*params[i][j]
- * for j < numel[i].
+ * for j < numel[i].  Defined by "Record: L_ParallelResiduals_UNetSkips_DepthRecur_
+ * Muon_ 1.0901" (PR #1893), "Architecture and training stack", EMA row (an
+ * exponential moving average of the weights with EMA_DECAY 0.9965, kept over
+ * every parameter and applied before quantization), and batched over all
+ * tensors in one pass as in "Record: Improved Parallel Residuals + Systems
+ * Optimization" (PR #1584), "Summary" ("batched EMA").  The decay multiplies
+ * the old average and (1 - decay) the current parameter; call it after the
+ * optimizer step, on the post-step parameters.
  *   ema, params   host arrays of n device pointers; ema[i] is updated in place,
  *                 params[i] is read only and must not overlap any ema[j].
  *   numel         host array of n element counts, each >= 0 (0 is skipped).

@@ -7,7 +7,13 @@ from typing import Dict, Optional, Sequence, Tuple
 
 from . import _lib
 
-_workspaces: Dict[Tuple[int, int], "object"] = {}
+# Cached workspaces, one per (device, stream), at most _MAX_WORKSPACES of them
+# (least recently used first out).  Each is allocated with its stream current,
+# so the caching allocator hands its memory to no other stream, and hands it
+# back to that stream only in stream order once it is dropped: a workspace that
+# kernels on its stream may still read is never reused under them.
+_MAX_WORKSPACES = 4
+_workspaces: "Dict[Tuple[int, int], object]" = {}
 
 
 def _torch():
@@ -69,14 +75,19 @@ def _entries(params, grads, moms, update_outs, emas):
     return entries
 
 
-def _workspace_for(nbytes: int, device):
+def _workspace_for(nbytes: int, device, stream):
+    """A workspace of at least nbytes for kernels enqueued on `stream` (a torch stream)."""
     torch = _torch()
-    key = (device.index if device.index is not None else torch.cuda.current_device(), nbytes)
-    ws = _workspaces.get(key)
-    if ws is None:
-        _workspaces.clear()
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
-        _workspaces[key] = ws
+    index = device.index if device.index is not None else torch.cuda.current_device()
+    key = (index, int(stream.cuda_stream))
+    ws = _workspaces.pop(key, None)
+    if ws is None or ws.numel() < nbytes:
+        ws = None  # dropped on its own stream: stream-ordered reuse only
+        with torch.cuda.stream(stream):
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _workspaces[key] = ws  # most recently used last
+    while len(_workspaces) > _MAX_WORKSPACES:
+        _workspaces.pop(next(iter(_workspaces)))
     return ws
 
 
@@ -99,11 +110,13 @@ def muon_step(params, grads, moms, *, lr: float, momentum: float, weight_decay: 
     table = _lib.tensor_table(entries)
     carr, steps = _lib.coeff_array(coeffs)
     device = params[0].device if n else None
+    if stream is None and n:
+        stream = _torch().cuda.current_stream(device)
     if workspace is None:
         need = lib.muon_workspace_size(table, n, int(ns_precision))
         if need == 0:
             raise _lib.MuonError(_lib.MUON_ERR_INVALID_ARG, lib.muon_last_error().decode())
-        workspace = _workspace_for(int(need), device)
+        workspace = _workspace_for(int(need), device, stream)
     rc = lib.muon_step(table, n, float(lr), float(momentum), int(bool(nesterov)), float(weight_decay),
                        int(bool(row_norm)), steps, carr if steps else None, int(ns_precision), float(ema_decay),
                        ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
@@ -241,7 +254,7 @@ class PreparedMuonStep:
     """
 
     def __init__(self, params, grads, moms, *, ns_precision: int = _lib.MUON_NS_BF16, update_outs=None,
-                 emas=None, workspace=None):
+                 emas=None, workspace=None, stream=None):
         if len(grads) != len(params) or len(moms) != len(params):
             raise ValueError("params, grads and moms must have the same length")
         self._keep = (list(params), list(grads), list(moms), update_outs, emas, workspace)
@@ -255,7 +268,12 @@ class PreparedMuonStep:
         if need == 0:
             raise _lib.MuonError(_lib.MUON_ERR_INVALID_ARG, lib.muon_last_error().decode())
         if workspace is None:
-            workspace = _torch().empty(int(need), dtype=_torch().uint8, device=self.device)
+            # allocated on the stream the steps run on, so that its memory is
+            # reused only in that stream's order once this object is dropped
+            torch = _torch()
+            s = stream if stream is not None else torch.cuda.current_stream(self.device)
+            with torch.cuda.stream(s):
+                workspace = torch.empty(int(need), dtype=torch.uint8, device=self.device)
         self.workspace = workspace
         self._ws_ptr = ctypes.c_void_p(workspace.data_ptr())
         self._ws_bytes = workspace.numel() * workspace.element_size()

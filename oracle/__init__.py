@@ -18,6 +18,5 @@ from .muon import (  # noqa: F401
     shape_scale,
     apply_update,
     muon_step_matrix,
-    muon_step,
     ema_update,
 )

@@ -51,7 +51,7 @@ use; callers pass the same float32 values the GPU library receives.
 from __future__ import annotations
 
 import math
-from typing import Iterable, Sequence
+from typing import Sequence
 
 import numpy as np
 
@@ -149,14 +149,6 @@ def muon_step_matrix(w, g, buf, *, lr: float, mu: float, nesterov: bool, wd: flo
     rows, cols = o.shape
     w_new = apply_update(w, o, lr, wd, shape_scale(rows, cols))
     return w_new, buf_new, o
-
-
-def muon_step(params: Iterable, grads: Iterable, bufs: Iterable, **kw):
-    """muon_step_matrix over a list of matrices (each one is independent)."""
-    out = []
-    for w, g, b in zip(params, grads, bufs):
-        out.append(muon_step_matrix(w, g, b, **kw))
-    return out
 
 
 def ema_update(ema, param, decay: float):

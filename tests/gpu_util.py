@@ -84,8 +84,8 @@ def check_fused_ema(e_in, w_gpu, e_gpu, decay, label=""):
 
 
 def check_layers(w_in, g_in, m_in, w_gpu, m_gpu, o_gpu, *, lr, momentum, wd, coeffs, nesterov, row_norm,
-                 ns_tol, check_o=True, label=""):
-    """Layered parity for one matrix; returns the O error (or None)."""
+                 ns_tol, label=""):
+    """Layered parity for one matrix; returns the O error."""
     mu = f32(momentum)
     m_ref, u_ref = om.momentum_update(m_in, g_in, mu, nesterov)
     e_m = rel_max(m_gpu, m_ref)
@@ -95,8 +95,6 @@ def check_layers(w_in, g_in, m_in, w_gpu, m_gpu, o_gpu, *, lr, momentum, wd, coe
     w_ref = om.apply_update(w_in, o_gpu, f32(lr), f32(wd), om.shape_scale(rows, cols))
     e_w = rel_max(w_gpu, w_ref)
     assert e_w <= ELEM_TOL, f"{label} weight rel err {e_w:.3e}"
-    if not check_o:
-        return None
     o_ref = om.orthogonalize(u_ref, [[f32(v) for v in row] for row in coeffs], row_norm)
     e_o = rel_frob(o_gpu, o_ref)
     assert e_o <= ns_tol, f"{label} NS output rel Frobenius err {e_o:.3e} > {ns_tol}"

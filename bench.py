@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--rotate", type=int, default=2, help="independent state copies used in turn (MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true", help="skip the steps/s of the other workloads")
+    ap.add_argument("--ns-schedule", choices=("phases", "chain"), default="phases",
+                    help="Newton-Schulz schedule of the timed line: one launch per phase (default) or the "
+                         "persistent chain")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (counter calibration) and exit")
@@ -211,6 +214,12 @@ def kernel_model(w, fused=True):
         model["ns_update_apply_bf16"] = {"flops": gram_f, "bytes": upda_b}  # last X, then W' and E'
     else:
         model["apply"] = {"flops": 0.0, "bytes": 20.0 * elems}           # read W, E, X hi + lo; write W, E
+    # The persistent chain runs every phase of every iteration in one launch:
+    # its algorithmic work is the sum of the phases above (the last update
+    # carrying W' and E'), and its intermediate planes may stay in the L2.
+    model["ns_chain_bf16"] = {"flops": k * (2.0 * gram_f + sq_f),
+                              "bytes": k * (gram_b + sq_b) + (k - 1) * upd_b + upda_b}
+    model["chain_setup"] = {"flops": 0.0, "bytes": 64.0 * len(w.matrices)}  # records written
     return model
 
 
@@ -373,6 +382,7 @@ def main():
     w = wl.workload(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    ms.set_ns_schedule(ms.MUON_NS_SCHEDULE_CHAIN if args.ns_schedule == "chain" else ms.MUON_NS_SCHEDULE_PHASES)
     coeffs = wl.coeff_table(w, args.seed).tolist()
     nm = len(w.matrices)
     # args.rotate independent copies of the whole state (seeds seed, seed + 1, ...),
@@ -435,6 +445,21 @@ def main():
     elapsed = time.perf_counter() - t0
     value = args.steps / elapsed
     print(f"[bench] timed {args.steps} steps in {elapsed * 1e3:.1f} ms", flush=True)
+
+    # The other Newton-Schulz schedule on the same state, for comparison.
+    other = "chain" if args.ns_schedule == "phases" else "phases"
+    ms.set_ns_schedule(ms.MUON_NS_SCHEDULE_CHAIN if other == "chain" else ms.MUON_NS_SCHEDULE_PHASES)
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    tc = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    other_rate = args.steps / (time.perf_counter() - tc)
+    ms.set_ns_schedule(ms.MUON_NS_SCHEDULE_CHAIN if args.ns_schedule == "chain" else ms.MUON_NS_SCHEDULE_PHASES)
+    print(f"[bench] {args.ns_schedule} schedule {value:.1f} steps/s, {other} schedule {other_rate:.1f} steps/s",
+          flush=True)
 
     # Spread of single steps: an event pair around each step on the caller's
     # stream (the lanes join it before the step's last kernel).
@@ -536,6 +561,7 @@ def main():
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "steps_per_s_spread": spread,
+        "ns_schedule": {"timed": args.ns_schedule, "other": other, "other_steps_per_s": round(other_rate, 2)},
         "ms_per_step_with_events": round(prof_elapsed / args.steps * 1e3, 4),
         "cpu_baseline": None,
     }

@@ -178,6 +178,36 @@ typedef struct adamw_tensor_t {
 int adamw_step(const adamw_tensor_t* tensors, int32_t n, float lr, float beta1, float beta2, float eps,
                float weight_decay, int32_t step, float ema_decay, void* stream);
 
+/* How muon_step schedules the Newton-Schulz iterations of the matrices whose
+ * products run in base-precision bf16 (MUON_NS_BF16, short side >= 192):
+ *   MUON_NS_SCHEDULE_PHASES  one launch per phase (Gram, square, update) and
+ *                            iteration, the shape groups spread over two
+ *                            streams (the default);
+ *   MUON_NS_SCHEDULE_CHAIN   one persistent launch for every iteration of
+ *                            every such matrix, each matrix bound to one XCD,
+ *                            tiles taken in dependency order per matrix.
+ * Both compute the same products with the same roundings (results within the
+ * same tolerances of the float64 reference; not bit-identical, since the
+ * Frobenius sum is reduced in another order).  The setting is library-wide
+ * and part of the schedule signature below.  Returns the previous setting,
+ * or MUON_ERR_INVALID_ARG for an unknown value.  The environment variable
+ * MUON_CHAIN=1 selects the chain when the library loads.  Needs no GPU. */
+#define MUON_NS_SCHEDULE_PHASES 0
+#define MUON_NS_SCHEDULE_CHAIN 1
+int muon_set_ns_schedule(int32_t schedule);
+
+/* Introspection of muon_step's schedule cache.  muon_step derives every table
+ * it needs from the tensor list (pointer validation, shape groups, workspace
+ * layout, launch sets, the Newton-Schulz chain's binding of matrices to XCDs)
+ * and caches the result under the call's signature: every descriptor field,
+ * the precision, the workspace pointer and size.  A later call with the same
+ * signature (and the same muon_set_ns_schedule setting) checks only its
+ * scalars and enqueues.  Writes the number of
+ * schedules built and of cache hits since the library was loaded (either
+ * pointer may be NULL) and returns the number of schedules held (at most 8,
+ * least recently used dropped first).  Needs no GPU. */
+int muon_plan_cache_stats(int64_t* built, int64_t* hits);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* muon_last_error(void);
 

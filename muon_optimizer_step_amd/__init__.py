@@ -6,7 +6,8 @@ Every step of the computation runs in the library's HIP kernels.
 """
 
 from ._lib import (  # noqa: F401
-    MUON_NS_BF16, MUON_NS_FP32, MUON_NS_BF16X3, MuonError, LIB_PATH, load,
+    MUON_NS_BF16, MUON_NS_FP32, MUON_NS_BF16X3, MUON_NS_SCHEDULE_PHASES, MUON_NS_SCHEDULE_CHAIN, MuonError, LIB_PATH,
+    load, set_ns_schedule, plan_cache_stats,
 )
 from .api import (  # noqa: F401
     muon_step, ema_update, ema_swap, adamw_step, workspace_size, profile_enable, profile_read, version,

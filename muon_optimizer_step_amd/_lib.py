@@ -19,6 +19,8 @@ MUON_MAX_TENSORS = 4096
 MUON_NS_BF16 = 0
 MUON_NS_FP32 = 1
 MUON_NS_BF16X3 = 2
+MUON_NS_SCHEDULE_PHASES = 0
+MUON_NS_SCHEDULE_CHAIN = 1
 
 
 class MuonTensor(ctypes.Structure):
@@ -83,6 +85,10 @@ def load() -> ctypes.CDLL:
     f.argtypes = [ctypes.POINTER(AdamWTensor), ctypes.c_int32, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                   ctypes.c_float, ctypes.c_float, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p]
     f.restype = ctypes.c_int
+    lib.muon_set_ns_schedule.argtypes = [ctypes.c_int32]
+    lib.muon_set_ns_schedule.restype = ctypes.c_int
+    lib.muon_plan_cache_stats.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+    lib.muon_plan_cache_stats.restype = ctypes.c_int
     lib.muon_last_error.argtypes = []
     lib.muon_last_error.restype = ctypes.c_char_p
     lib.muon_version.argtypes = []
@@ -122,3 +128,19 @@ def adamw_table(entries) -> "ctypes.Array[AdamWTensor]":
 def coeff_array(coeffs):
     flat = [float(v) for row in coeffs for v in row]
     return (ctypes.c_float * max(1, len(flat)))(*flat), len(flat) // 3
+
+
+def plan_cache_stats():
+    """(schedules built, cache hits, schedules held) of muon_step's schedule cache."""
+    built = ctypes.c_int64(0)
+    hits = ctypes.c_int64(0)
+    held = load().muon_plan_cache_stats(ctypes.byref(built), ctypes.byref(hits))
+    return int(built.value), int(hits.value), int(held)
+
+
+def set_ns_schedule(schedule: int) -> int:
+    """Select MUON_NS_SCHEDULE_PHASES or MUON_NS_SCHEDULE_CHAIN; returns the previous setting."""
+    rc = load().muon_set_ns_schedule(int(schedule))
+    if rc < 0:
+        check(rc)
+    return int(rc)

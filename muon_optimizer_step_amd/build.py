@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmuonstep.so")
-SOURCES = ["api.hip", "elementwise.hip", "ns.hip"]
+SOURCES = ["api.hip", "elementwise.hip", "ns.hip", "chain.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -13,11 +13,14 @@
 // ema_update, ema_swap and adamw_step enqueue one multi-tensor launch per
 // table chunk on the caller's stream.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <cstdlib>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <utility>
@@ -159,6 +162,12 @@ struct Plan {
     std::vector<size_t> rowsq_off;  // in floats
     size_t rowsq_base = 0;          // byte offset of the rowsq array
     size_t scale_base = 0;          // byte offset of the per-matrix scale array
+    // persistent chain over the base-precision bf16 groups (chain.hip)
+    std::vector<std::vector<int>> chain_launch_groups;  // groups of each chain launch (<= kMaxGroups)
+    int chain_mats = 0;             // matrices in those groups
+    size_t chain_rec_base = 0;      // byte offset of the ChainMat records
+    size_t chain_ctr_base = 0;      // byte offset of the counters (+ one status block per launch)
+    int chain_ctr_words = 0;
     size_t bytes = 0;
 };
 
@@ -227,6 +236,21 @@ void make_plan(const muon_tensor_t* t, int n, int mode, Plan& p) {
     off += align256((size_t)scale_count * sizeof(float));
     p.rowsq_base = off;
     off += align256(rowsq_total * sizeof(float));
+    // chain launches: the base bf16 groups, kMaxGroups per launch
+    if (precision == kNsBf16) {
+        for (int g = 0; g < (int)p.groups.size(); ++g) {
+            if (p.groups[g].comp) continue;
+            if (p.chain_launch_groups.empty() || (int)p.chain_launch_groups.back().size() == kMaxGroups)
+                p.chain_launch_groups.emplace_back();
+            p.chain_launch_groups.back().push_back(g);
+            p.chain_mats += p.groups[g].count;
+        }
+    }
+    p.chain_rec_base = off;
+    off += align256((size_t)p.chain_mats * sizeof(ChainMat));
+    p.chain_ctr_base = off;
+    p.chain_ctr_words = (p.chain_mats + (int)p.chain_launch_groups.size()) * kChainCtrWords;
+    off += align256((size_t)p.chain_ctr_words * sizeof(uint32_t));
     p.bytes = off;
 }
 
@@ -313,6 +337,320 @@ void f8_scale_exponents(const float* coeffs, int ns_steps, int* sa) {
 // any device memory).
 constexpr int64_t kMaxStreamElems = ((int64_t)1 << 30) * 1024;
 
+// ------------------------------------------------------------- schedules
+// Everything muon_step derives from the tensor list alone (validation of the
+// pointers, shape groups, workspace layout, lanes, launch sets, the chain's
+// XCD binding and matrix records) is a Schedule, cached by the call's
+// signature: the tensor descriptors, the precision and the workspace.  A call
+// whose signature matches a cached one only checks its scalars and enqueues.
+struct Part {
+    int group, s0, s1;  // slots [s0, s1) of the group
+    int lane;
+};
+struct NsLaunchSet {
+    int lane, comp;
+    std::vector<int> parts;
+};
+struct ChainLaunch {
+    ChainArgs a;          // groups, records, counters, XCD table; scalars set per call
+};
+struct Schedule {
+    std::vector<uint64_t> key;
+    Plan p;
+    int mode = 0, prec = 0;
+    // per-phase path (lanes), for the groups the chain does not take
+    std::vector<Part> parts;
+    int nlanes = 1;
+    std::vector<NsLaunchSet> sets;
+    std::vector<std::vector<int>> mine;        // tensors of each lane (prep)
+    std::vector<std::vector<int>> legacy;      // tensors of each lane outside the chain
+    int max_set_count = 0;                     // matrices of the largest launch set
+    // chain
+    bool chain = false;
+    std::vector<ChainLaunch> chains;
+    std::vector<ChainSetupArgs> setups;
+    // e4m3 scale exponents of the last coefficient table seen
+    std::vector<float> f8_coeffs;
+    int f8_sa[MUON_MAX_NS_STEPS] = {};
+};
+
+std::mutex g_sched_mu;
+std::vector<std::shared_ptr<Schedule>> g_sched;   // most recently used last
+constexpr size_t kMaxSchedules = 8;
+int64_t g_sched_built = 0, g_sched_hits = 0;
+
+std::vector<uint64_t> schedule_key(const muon_tensor_t* t, int n, int mode, int schedule, const void* ws,
+                                   size_t ws_bytes) {
+    std::vector<uint64_t> k;
+    k.reserve(5 + 6 * (size_t)n);
+    k.push_back((uint64_t)n);
+    k.push_back((uint64_t)mode);
+    k.push_back((uint64_t)schedule);
+    k.push_back(reinterpret_cast<uintptr_t>(ws));
+    k.push_back((uint64_t)ws_bytes);
+    for (int i = 0; i < n; ++i) {
+        k.push_back(reinterpret_cast<uintptr_t>(t[i].param));
+        k.push_back(reinterpret_cast<uintptr_t>(t[i].grad));
+        k.push_back(reinterpret_cast<uintptr_t>(t[i].momentum));
+        k.push_back(reinterpret_cast<uintptr_t>(t[i].update_out));
+        k.push_back(reinterpret_cast<uintptr_t>(t[i].ema));
+        k.push_back(((uint64_t)(uint32_t)t[i].rows << 32) | (uint32_t)t[i].cols);
+    }
+    return k;
+}
+
+// How the Newton-Schulz iterations of the base bf16 groups are scheduled:
+// MUON_NS_SCHEDULE_PHASES (one launch per phase, the default) or
+// MUON_NS_SCHEDULE_CHAIN (the persistent chain).  MUON_CHAIN=1 in the
+// environment selects the chain at load time; muon_set_ns_schedule changes it.
+std::atomic<int> g_ns_schedule{[] {
+    const char* v = std::getenv("MUON_CHAIN");
+    return (v && v[0] == '1') ? MUON_NS_SCHEDULE_CHAIN : MUON_NS_SCHEDULE_PHASES;
+}()};
+bool chain_allowed(int schedule) { return schedule == MUON_NS_SCHEDULE_CHAIN; }
+
+// Compute units of device dev (cached); 0 if unknown.
+int device_cus(int dev) {
+    static std::mutex mu;
+    static std::map<int, int> cache;
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find(dev);
+    if (it != cache.end()) return it->second;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+    cache[dev] = cus;
+    return cus;
+}
+
+double ns_flops_per_iter(const Group& G) {
+    return 4.0 * G.M * (double)G.M * G.N + 2.0 * G.M * (double)G.M * G.M;
+}
+
+// The chain binds a matrix to one XCD (an eighth of the GPU).  It is not used
+// when one matrix alone holds more than half of the NS work of a call and is
+// large enough for the whole GPU to matter (a single very large matrix runs
+// faster on the per-phase kernels, which spread its tiles over every XCD).
+bool chain_worthwhile(const Plan& p) {
+    double total = 0.0, biggest = 0.0;
+    for (const auto& lg : p.chain_launch_groups)
+        for (int g : lg) {
+            total += ns_flops_per_iter(p.groups[g]) * p.groups[g].count;
+            biggest = std::max(biggest, ns_flops_per_iter(p.groups[g]));
+        }
+    if (total <= 0.0) return false;
+    return biggest <= 0.5 * total || biggest < 4e9;
+}
+
+float shape_scale_of(const muon_tensor_t& x) {
+    return (float)std::sqrt(std::max(1.0, (double)x.rows / (double)x.cols));
+}
+bool vec_ok(const muon_tensor_t& x) {
+    // 16-byte accesses to the caller's W / O / EMA rows
+    return (x.cols % 4 == 0) && (reinterpret_cast<uintptr_t>(x.param) % 16 == 0) &&
+           (reinterpret_cast<uintptr_t>(x.update_out) % 16 == 0) && (reinterpret_cast<uintptr_t>(x.ema) % 16 == 0);
+}
+
+// Validation of the tensor list and the workspace, then every derived table.
+int build_schedule(const muon_tensor_t* tensors, int n, int mode, int schedule, void* workspace,
+                   size_t workspace_bytes, Schedule& S) {
+    int rc = validate_pointers(tensors, n);
+    if (rc) return rc;
+    Plan& p = S.p;
+    make_plan(tensors, n, mode, p);
+    if (!workspace) return fail(MUON_ERR_WORKSPACE, "workspace is NULL (needs %zu bytes)", p.bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+        return fail(MUON_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (workspace_bytes < p.bytes)
+        return fail(MUON_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, p.bytes);
+    {
+        // the workspace must not overlap any tensor
+        const uintptr_t wlo = reinterpret_cast<uintptr_t>(workspace), whi = wlo + p.bytes;
+        for (int i = 0; i < n; ++i) {
+            const muon_tensor_t& x = tensors[i];
+            const size_t bytes = (size_t)x.rows * x.cols * sizeof(float);
+            const void* ptrs[5] = {x.param, x.grad, x.momentum, x.update_out, x.ema};
+            for (int k = 0; k < 5; ++k) {
+                if (!ptrs[k]) continue;
+                const uintptr_t lo = reinterpret_cast<uintptr_t>(ptrs[k]);
+                if (lo < whi && wlo < lo + bytes)
+                    return fail(MUON_ERR_UNSUPPORTED, "tensor %d overlaps the workspace", i);
+            }
+        }
+    }
+    S.mode = mode;
+    S.prec = mode == MUON_NS_FP32 ? kNsFp32 : kNsBf16;
+    S.chain = chain_allowed(schedule) && !p.chain_launch_groups.empty() && chain_worthwhile(p);
+    const int ngroups = (int)p.groups.size();
+    std::vector<char> in_chain(ngroups, 0);
+    if (S.chain)
+        for (const auto& lg : p.chain_launch_groups)
+            for (int g : lg) in_chain[g] = 1;
+
+    // ---- lanes of the per-phase path: shape groups longest first onto the
+    // least loaded lane (by NS flops), whole.  With the chain, everything runs
+    // on the caller's stream (the chain fills the GPU by itself).
+    {
+        std::vector<std::pair<double, int>> work;
+        for (int g = 0; g < ngroups; ++g) work.push_back({ns_flops_per_iter(p.groups[g]) * p.groups[g].count, g});
+        std::sort(work.begin(), work.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
+        const int lanes = S.chain ? 1 : kLanes;
+        std::vector<double> load(lanes, 0.0);
+        for (const auto& wg : work) {
+            const int g = wg.second;
+            const int l = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+            S.parts.push_back({g, 0, p.groups[g].count, l});
+            load[l] += wg.first;
+        }
+    }
+    S.nlanes = 1;
+    for (const Part& pt : S.parts) S.nlanes = std::max(S.nlanes, pt.lane + 1);
+    std::vector<int> tensor_lane(n, 0);
+    for (const Part& pt : S.parts)
+        for (int sl = pt.s0; sl < pt.s1; ++sl) tensor_lane[p.members[pt.group][sl]] = pt.lane;
+    S.mine.assign(S.nlanes, {});
+    S.legacy.assign(S.nlanes, {});
+    for (int i = 0; i < n; ++i) {
+        S.mine[tensor_lane[i]].push_back(i);
+        if (!in_chain[p.group_of[i]]) S.legacy[tensor_lane[i]].push_back(i);
+    }
+    // launch sets of the per-phase path: (lane, compensated?, up to kMaxGroups parts)
+    for (int l = 0; l < S.nlanes; ++l)
+        for (int comp = 0; comp < 2; ++comp) {
+            std::vector<int> pl;
+            for (int q = 0; q < (int)S.parts.size(); ++q)
+                if (S.parts[q].lane == l && (int)p.groups[S.parts[q].group].comp == comp && !in_chain[S.parts[q].group])
+                    pl.push_back(q);
+            for (size_t q0 = 0; q0 < pl.size(); q0 += kMaxGroups)
+                S.sets.push_back({l, comp, std::vector<int>(pl.begin() + q0, pl.begin() + std::min(pl.size(), q0 + kMaxGroups))});
+        }
+    for (const NsLaunchSet& ls : S.sets) {
+        int cnt = 0;
+        for (int q : ls.parts) cnt += S.parts[q].s1 - S.parts[q].s0;
+        S.max_set_count = std::max(S.max_set_count, cnt);
+    }
+
+    // ---- chain launches: each matrix bound to an XCD (longest first onto the
+    // least loaded XCD by NS flops), records ordered by XCD and, within an XCD,
+    // by decreasing work (the scheduler's priority)
+    if (S.chain) {
+        uint8_t* ws = static_cast<uint8_t*>(workspace);
+        ChainMat* recs = reinterpret_cast<ChainMat*>(ws + p.chain_rec_base);
+        uint32_t* ctr = reinterpret_cast<uint32_t*>(ws + p.chain_ctr_base);
+        const size_t xe = 2;
+        std::vector<ChainMat> all;
+        int ctr_words = 0;
+        for (const auto& lg : p.chain_launch_groups) {
+            ChainLaunch L;
+            memset(&L.a, 0, sizeof(L.a));
+            struct M { double w; int group_idx, slot; };
+            std::vector<M> mats;
+            for (int gi = 0; gi < (int)lg.size(); ++gi) {
+                const Group& G = p.groups[lg[gi]];
+                NsGroup& D = L.a.g[gi];
+                for (int b = 0; b < 2; ++b) {
+                    D.x[b] = ws + G.x_off[b];
+                    D.xl[b] = ws + G.xl_off[b];
+                }
+                D.a_hi = ws + G.ah_off;
+                D.a_lo = ws + G.al_off;
+                D.b = ws + G.b_off;
+                D.b_lo = ws + G.bl_off;
+                D.scale = reinterpret_cast<float*>(ws + p.scale_base) + G.scale_begin;
+                D.count = G.count;
+                D.M = G.M;
+                D.N = G.N;
+                for (int sl = 0; sl < G.count; ++sl) mats.push_back({ns_flops_per_iter(G), gi, sl});
+            }
+            (void)xe;
+            std::stable_sort(mats.begin(), mats.end(), [](const M& x, const M& y) { return x.w > y.w; });
+            std::vector<double> load(kXcds, 0.0);
+            std::vector<std::vector<M>> per(kXcds);
+            for (const M& m : mats) {
+                const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+                per[x].push_back(m);
+                load[x] += m.w;
+            }
+            L.a.mats = recs + all.size();
+            L.a.ctr = ctr + ctr_words;
+            L.a.rowsq = reinterpret_cast<const float*>(ws + p.rowsq_base);
+            int nm = 0;
+            for (int x = 0; x < kXcds; ++x) {
+                L.a.xcd_begin[x] = nm;
+                for (const M& m : per[x]) {
+                    const int gidx = lg[m.group_idx];
+                    const Group& G = p.groups[gidx];
+                    const int ti = p.members[gidx][m.slot];
+                    const muon_tensor_t& t = tensors[ti];
+                    ChainMat R;
+                    memset(&R, 0, sizeof(R));
+                    R.param = t.param;
+                    R.out = t.update_out;
+                    R.ema = t.ema;
+                    R.shape_scale = shape_scale_of(t);
+                    R.flags = (t.rows > t.cols ? kApplyTransposed : 0) | (vec_ok(t) ? kApplyVec : 0);
+                    R.rows = t.rows;
+                    R.cols = t.cols;
+                    R.group = m.group_idx;
+                    R.slot = m.slot;
+                    R.rowsq_off = (int)p.rowsq_off[ti];
+                    const int tm = G.M / kTile, tn = G.N / kTile;
+                    R.tiles_sym = tm * (tm + 1) / 2;
+                    R.tiles_upd = tm * tn;
+                    all.push_back(R);
+                    ++nm;
+                }
+            }
+            L.a.xcd_begin[kXcds] = nm;
+            L.a.nmat = nm;
+            L.a.timeout_ticks = (uint64_t)100000000 * 10;   // 10 s of the 100 MHz counter
+            ctr_words += (nm + 1) * kChainCtrWords;         // counters, then the launch's status block
+            S.chains.push_back(L);
+        }
+        for (size_t r0 = 0; r0 < all.size(); r0 += kChainSetupChunk) {
+            ChainSetupArgs sa;
+            memset(&sa, 0, sizeof(sa));
+            sa.n = (int)std::min(all.size() - r0, (size_t)kChainSetupChunk);
+            for (int i = 0; i < sa.n; ++i) sa.rec[i] = all[r0 + i];
+            sa.dst = recs + r0;
+            if (r0 == 0) {
+                sa.zero = ctr;
+                sa.nzero = ctr_words;
+            }
+            S.setups.push_back(sa);
+        }
+    }
+    return MUON_OK;
+}
+
+// The cached schedule of this signature, or a new one; null on a validation
+// error (its code in rc).
+std::shared_ptr<Schedule> find_schedule(const muon_tensor_t* t, int n, int mode, void* ws, size_t ws_bytes, int& rc) {
+    rc = MUON_OK;
+    const int schedule = g_ns_schedule.load();
+    std::vector<uint64_t> key = schedule_key(t, n, mode, schedule, ws, ws_bytes);
+    {
+        std::lock_guard<std::mutex> lk(g_sched_mu);
+        for (size_t i = 0; i < g_sched.size(); ++i)
+            if (g_sched[i]->key == key) {
+                std::shared_ptr<Schedule> hit = g_sched[i];
+                g_sched.erase(g_sched.begin() + i);
+                g_sched.push_back(hit);
+                ++g_sched_hits;
+                return hit;
+            }
+    }
+    auto S = std::make_shared<Schedule>();
+    rc = build_schedule(t, n, mode, schedule, ws, ws_bytes, *S);
+    if (rc != MUON_OK) return nullptr;
+    S->key = std::move(key);
+    std::lock_guard<std::mutex> lk(g_sched_mu);
+    ++g_sched_built;
+    g_sched.push_back(S);
+    if (g_sched.size() > kMaxSchedules) g_sched.erase(g_sched.begin());
+    return S;
+}
+
+
 }  // namespace
 }  // namespace muon
 
@@ -347,112 +685,43 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
     if (ns_steps > 0 && !ns_coeffs) return fail(MUON_ERR_INVALID_ARG, "ns_coeffs is NULL with ns_steps = %d", ns_steps);
     for (int k = 0; k < 3 * ns_steps; ++k)
         if (!std::isfinite(ns_coeffs[k])) return fail(MUON_ERR_INVALID_ARG, "ns_coeffs[%d] is not finite", k);
-    rc = validate_pointers(tensors, n);
-    if (rc) return rc;
-    Plan p;
-    make_plan(tensors, n, ns_precision, p);
-    if (!workspace) return fail(MUON_ERR_WORKSPACE, "workspace is NULL (needs %zu bytes)", p.bytes);
-    if (reinterpret_cast<uintptr_t>(workspace) % 256)
-        return fail(MUON_ERR_WORKSPACE, "workspace is not 256-byte aligned");
-    if (workspace_bytes < p.bytes)
-        return fail(MUON_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, p.bytes);
-    {
-        // the workspace must not overlap any tensor
-        const uintptr_t wlo = reinterpret_cast<uintptr_t>(workspace), whi = wlo + p.bytes;
-        for (int i = 0; i < n; ++i) {
-            const muon_tensor_t& x = tensors[i];
-            const size_t bytes = (size_t)x.rows * x.cols * sizeof(float);
-            const void* ptrs[5] = {x.param, x.grad, x.momentum, x.update_out, x.ema};
-            for (int k = 0; k < 5; ++k) {
-                if (!ptrs[k]) continue;
-                const uintptr_t lo = reinterpret_cast<uintptr_t>(ptrs[k]);
-                if (lo < whi && wlo < lo + bytes)
-                    return fail(MUON_ERR_UNSUPPORTED, "tensor %d overlaps the workspace", i);
-            }
-        }
-    }
+    std::shared_ptr<Schedule> sched = find_schedule(tensors, n, ns_precision, workspace, workspace_bytes, rc);
+    if (!sched) return rc;
+    const Schedule& S = *sched;
+    const Plan& p = S.p;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     float* rowsq = reinterpret_cast<float*>(ws + p.rowsq_base);
-    const int prec = ns_precision == MUON_NS_FP32 ? kNsFp32 : kNsBf16;  // storage precision
+    const int prec = S.prec;                                             // storage precision
     const size_t xe = prec == kNsBf16 ? 2 : 4;                           // bytes per X element
     // bytes per element of X's lo plane: base-precision bf16 groups keep bytes
     // (the NS kernels index that plane by element), the compensated ones bf16
     auto lo_bytes = [&](const Group& G) -> size_t { return prec == kNsBf16 ? (G.comp ? 2 : 1) : xe; };
     hipError_t err = hipSuccess;
+    // the chain runs the NS iterations of its groups; with no iteration every
+    // matrix takes the per-phase path's prep, Frobenius scale and apply
+    const bool use_chain = S.chain && ns_steps > 0;
+    const std::vector<std::vector<int>>& legacy = use_chain ? S.legacy : S.mine;
+    const int nlanes = S.nlanes;
+    const std::vector<Part>& parts = S.parts;
 
-    // ---- lanes: the matrices are independent NS problems.  Shape groups go
-    // to lanes longest first onto the least loaded lane (by NS flops), whole.
-    // Each lane runs prep -> frob -> NS iterations -> apply for
-    // its own matrices on its own stream, so short chains fill the compute
-    // units the long ones leave idle.
-    const int ngroups = (int)p.groups.size();
-    struct Part {
-        int group, s0, s1;  // slots [s0, s1) of the group
-        int lane;
-    };
-    std::vector<Part> parts;
-    {
-        std::vector<double> per(ngroups);  // NS flops of one matrix
-        std::vector<std::pair<double, int>> work;
-        for (int g = 0; g < ngroups; ++g) {
-            const Group& G = p.groups[g];
-            per[g] = 4.0 * G.M * G.M * (double)G.N + 2.0 * G.M * G.M * (double)G.M;
-            work.push_back({per[g] * G.count, g});
-        }
-        std::sort(work.begin(), work.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
-        std::vector<double> load(kLanes, 0.0);
-        for (const auto& wg : work) {
-            const int g = wg.second;
-            const int count = p.groups[g].count;
-            const int l = (int)(std::min_element(load.begin(), load.end()) - load.begin());
-            parts.push_back({g, 0, count, l});
-            load[l] += count * per[g];
-        }
-    }
-    int nlanes = 1;
-    for (const Part& pt : parts) nlanes = std::max(nlanes, pt.lane + 1);
-    // lane of every tensor
-    std::vector<int> tensor_lane(n, 0);
-    for (const Part& pt : parts)
-        for (int sl = pt.s0; sl < pt.s1; ++sl) tensor_lane[p.members[pt.group][sl]] = pt.lane;
-    // NS launch sets: (lane, compensated?, up to kMaxGroups parts)
-    struct NsLaunchSet {
-        int lane, comp;
-        std::vector<int> parts;
-    };
-    std::vector<NsLaunchSet> sets;
-    for (int l = 0; l < nlanes; ++l)
-        for (int comp = 0; comp < 2; ++comp) {
-            std::vector<int> pl;
-            for (int q = 0; q < (int)parts.size(); ++q)
-                if (parts[q].lane == l && (int)p.groups[parts[q].group].comp == comp) pl.push_back(q);
-            for (size_t q0 = 0; q0 < pl.size(); q0 += kMaxGroups)
-                sets.push_back({l, comp, std::vector<int>(pl.begin() + q0, pl.begin() + std::min(pl.size(), q0 + kMaxGroups))});
-        }
     // The weight update runs inside the last NS update launch when every launch
-    // holds at most kMaxFused matrices.
-    // The first Gram launch computes the Frobenius scales itself (no separate
-    // frob launch) when every launch holds at most kMaxFrobSlots matrices.
-    bool fuse = ns_steps > 0, fold_frob = ns_steps > 0;
-    for (const NsLaunchSet& ls : sets) {
-        int cnt = 0;
-        for (int q : ls.parts) cnt += parts[q].s1 - parts[q].s0;
-        if (cnt > kMaxFused) fuse = false;
-        if (cnt > kMaxFrobSlots) fold_frob = false;
-    }
+    // holds at most kMaxFused matrices.  The first Gram launch computes the
+    // Frobenius scales itself (no separate frob launch) when every launch holds
+    // at most kMaxFrobSlots matrices.
+    const bool fuse = ns_steps > 0 && S.max_set_count <= kMaxFused;
+    const bool fold_frob = ns_steps > 0 && S.max_set_count <= kMaxFrobSlots;
     const float keep = 1.0f - lr * weight_decay;
-    int f8_sa[MUON_MAX_NS_STEPS];
-    f8_scale_exponents(ns_coeffs, ns_steps, f8_sa);
-    // 16-byte accesses to the caller's W / O / EMA rows
-    auto vec_ok = [](const muon_tensor_t& x) {
-        return (x.cols % 4 == 0) && (reinterpret_cast<uintptr_t>(x.param) % 16 == 0) &&
-               (reinterpret_cast<uintptr_t>(x.update_out) % 16 == 0) && (reinterpret_cast<uintptr_t>(x.ema) % 16 == 0);
-    };
-    auto lr_scale = [&](const muon_tensor_t& x) {
-        return lr * (float)std::sqrt(std::max(1.0, (double)x.rows / (double)x.cols));
-    };
+    // e4m3 scale exponents of the table (cached per thread for the last table)
+    thread_local std::vector<float> f8_last;
+    thread_local int f8_sa[MUON_MAX_NS_STEPS];
+    if (f8_last.size() != (size_t)(3 * ns_steps) ||
+        (ns_steps > 0 && memcmp(f8_last.data(), ns_coeffs, sizeof(float) * 3 * ns_steps) != 0)) {
+        f8_scale_exponents(ns_coeffs, ns_steps, f8_sa);
+        f8_last.assign(ns_coeffs, ns_coeffs + 3 * ns_steps);
+    }
+    auto lr_scale = [&](const muon_tensor_t& x) { return lr * shape_scale_of(x); };
 
     std::unique_lock<std::mutex> lane_lock(g_lane_mu, std::defer_lock);
     hipStream_t lane_stream[kLanes];
@@ -471,15 +740,19 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
         if (err != hipSuccess) return fail(MUON_ERR_HIP, "lane fork failed: %s", hipGetErrorString(err));
     }
 
-    // Each lane's tensors, in call order.
-    std::vector<std::vector<int>> mine(nlanes);
-    for (int i = 0; i < n; ++i) mine[tensor_lane[i]].push_back(i);
+    // ---- chain records and counters (before prep: nothing waits for it)
+    if (use_chain) {
+        for (const ChainSetupArgs& sa : S.setups) {
+            err = timed_launch("chain_setup", s, [&] { return launch_chain_setup(sa, s); });
+            if (err != hipSuccess) return fail(MUON_ERR_HIP, "chain setup launch failed: %s", hipGetErrorString(err));
+        }
+    }
 
     // ---- prep: momentum, row norm, X0 (short side first, zero padded), in
     // evenly sized launches of at most kPrepChunk tensors
     auto enqueue_prep = [&](int lane) -> int {
         hipStream_t ls_stream = lane_stream[lane];
-        const std::vector<int>& my = mine[lane];
+        const std::vector<int>& my = S.mine[lane];
         const int nm = (int)my.size();
         const int prep_launches = (nm + kPrepChunk - 1) / kPrepChunk;
         const int prep_take = (nm + prep_launches - 1) / prep_launches;
@@ -526,10 +799,10 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
         return MUON_OK;
     };
 
-    // ---- Frobenius scales
+    // ---- Frobenius scales (per-phase path)
     auto enqueue_frob = [&](int lane) -> int {
         hipStream_t ls_stream = lane_stream[lane];
-        const std::vector<int>& my = mine[lane];
+        const std::vector<int>& my = legacy[lane];
         const int nm = (int)my.size();
         for (int c0 = 0; c0 < nm; c0 += kFrobChunk) {
             FrobArgs a;
@@ -553,7 +826,7 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
     // ---- one Newton-Schulz phase of iteration k: one launch per launch set
     auto enqueue_ns = [&](int lane, int k, int phase) -> int {
         hipStream_t ls_stream = lane_stream[lane];
-        for (const NsLaunchSet& ls : sets) {
+        for (const NsLaunchSet& ls : S.sets) {
             if (ls.lane != lane) continue;
             NsArgs a;
             memset(&a, 0, sizeof(a));
@@ -628,7 +901,7 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
     // update did it)
     auto enqueue_apply = [&](int lane) -> int {
         hipStream_t ls_stream = lane_stream[lane];
-        const std::vector<int>& my = mine[lane];
+        const std::vector<int>& my = legacy[lane];
         const int nm = (int)my.size();
         const int final_buf = ns_steps & 1;
         for (int c0 = 0; c0 < nm; c0 += kApplyChunk) {
@@ -675,6 +948,34 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
         return MUON_OK;
     };
 
+    // ---- the chain: every NS iteration of its groups in one launch per chunk
+    // of kMaxGroups groups, on the caller's stream
+    auto enqueue_chain = [&]() -> int {
+        int dev = 0;
+        err = hipGetDevice(&dev);
+        if (err != hipSuccess) return fail(MUON_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(err));
+        const int cus = device_cus(dev);
+        const int wgs = std::max(cus, kXcds) * kChainWgPerCu;
+        for (const ChainLaunch& CL : S.chains) {
+            ChainArgs a = CL.a;
+            a.ns_steps = ns_steps;
+            a.fuse_apply = 1;
+            a.keep = keep;
+            a.lr = lr;
+            a.decay = ema_decay;
+            a.one_minus_decay = 1.0f - ema_decay;
+            for (int k = 0; k < ns_steps; ++k) {
+                a.a[k] = ns_coeffs[3 * k + 0];
+                a.b[k] = ns_coeffs[3 * k + 1];
+                a.c[k] = ns_coeffs[3 * k + 2];
+                a.f8_sa[k] = f8_sa[k];
+            }
+            err = timed_launch("ns_chain_bf16", s, [&] { return launch_chain(a, wgs, s); });
+            if (err != hipSuccess) return fail(MUON_ERR_HIP, "ns_chain launch failed: %s", hipGetErrorString(err));
+        }
+        return MUON_OK;
+    };
+
     // Enqueue stage by stage across the lanes, so every lane has work queued
     // early even when the host is only just ahead of the GPU.
     for (int lane = 0; lane < nlanes; ++lane)
@@ -689,6 +990,7 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
     if (!fuse)
         for (int lane = 0; lane < nlanes; ++lane)
             if ((rc = enqueue_apply(lane))) return rc;
+    if (use_chain && (rc = enqueue_chain())) return rc;
 
     if (L) {
         for (int l = 1; l < nlanes && err == hipSuccess; ++l) {
@@ -698,6 +1000,20 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
         if (err != hipSuccess) return fail(MUON_ERR_HIP, "lane join failed: %s", hipGetErrorString(err));
     }
     return MUON_OK;
+}
+
+int muon_set_ns_schedule(int32_t schedule) {
+    if (schedule != MUON_NS_SCHEDULE_PHASES && schedule != MUON_NS_SCHEDULE_CHAIN)
+        return fail(MUON_ERR_INVALID_ARG, "schedule = %d is not MUON_NS_SCHEDULE_PHASES or MUON_NS_SCHEDULE_CHAIN",
+                    schedule);
+    return g_ns_schedule.exchange(schedule);
+}
+
+int muon_plan_cache_stats(int64_t* built, int64_t* hits) {
+    std::lock_guard<std::mutex> lk(g_sched_mu);
+    if (built) *built = g_sched_built;
+    if (hits) *hits = g_sched_hits;
+    return (int)g_sched.size();
 }
 
 int ema_update(float* const* ema, const float* const* params, const int64_t* numel, int32_t n, float decay,

@@ -110,6 +110,55 @@ struct NsArgs {
 enum NsPhase { kGram = 0, kSquare = 1, kUpdate = 2 };
 enum NsMode { kModeBf16 = 0, kModeFp32 = 1, kModeBf16x3 = 2 };  // the ns_precision argument
 
+// ------------------------------------------------------- NS chain (persistent)
+// One launch runs every Newton-Schulz iteration of every base-precision bf16
+// matrix of a call.  Each matrix is bound to one XCD; the workgroups of an XCD
+// take the tiles of its matrices in dependency order (Gram, square, update of
+// iteration 0, then of iteration 1, ...), so a matrix's planes are only ever
+// shared through that XCD's L2.  Per-matrix records and counters live in the
+// workspace; chain_setup writes them before the chain launch.
+struct ChainMat {
+    float* param;        // fused apply (last iteration): W, optional O copy, optional EMA
+    float* out;
+    float* ema;
+    float shape_scale;   // sqrt(max(1, rows / cols)); the apply uses lr * shape_scale
+    int flags;           // kApplyTransposed | kApplyVec
+    int rows, cols;      // stored shape
+    int group, slot;     // NsGroup of the launch and slot in it
+    int rowsq_off;       // first per-row sum of squares (floats)
+    int tiles_sym;       // Gram / square tiles per iteration (upper triangle)
+    int tiles_upd;       // update tiles per iteration
+    int pad;
+};
+static_assert(sizeof(ChainMat) == 64, "ChainMat is one 64-byte record");
+constexpr int kChainCtrWords = 64;   // per matrix: grab counter at [0], done counter at [32] (own 128-byte lines)
+constexpr int kChainMaxSteps = 16;
+struct ChainArgs {
+    NsGroup g[kMaxGroups];
+    const ChainMat* mats;     // ordered by XCD, highest priority first within an XCD
+    uint32_t* ctr;            // [nmat][kChainCtrWords], then the status word
+    const float* rowsq;
+    int xcd_begin[kXcds + 1]; // matrices [xcd_begin[x], xcd_begin[x + 1]) run on XCD x
+    int nmat;
+    int ns_steps;
+    int fuse_apply;           // the last update writes W' (and O, E') instead of X
+    float keep;               // 1 - lr*wd
+    float lr;
+    float decay, one_minus_decay;
+    float a[kChainMaxSteps], b[kChainMaxSteps], c[kChainMaxSteps];
+    int f8_sa[kChainMaxSteps];  // e4m3 scale exponent of A hi per iteration (A lo: + 8)
+    uint64_t timeout_ticks;   // bound on any wait, in s_memrealtime ticks (100 MHz)
+};
+constexpr int kChainSetupChunk = 60;
+struct ChainSetupArgs {
+    ChainMat rec[kChainSetupChunk];
+    ChainMat* dst;
+    uint32_t* zero;           // counters to clear (first setup launch of a call), or NULL
+    int n;
+    int nzero;
+};
+constexpr uint32_t kChainStatusTimeout = 1u;   // a wait ran past timeout_ticks
+
 // ------------------------------------------------------------- apply (K3)
 struct ApplyTensor {
     float* param;
@@ -194,6 +243,8 @@ static_assert(sizeof(AdamArgs) <= 4096, "AdamW kernel arguments exceed 4 KiB");
 static_assert(sizeof(SwapArgs) <= 4096, "swap kernel arguments exceed 4 KiB");
 static_assert(sizeof(FrobArgs) <= 4096, "frob kernel arguments exceed 4 KiB");
 static_assert(sizeof(NsArgs) <= 4096, "NS kernel arguments exceed 4 KiB");
+static_assert(sizeof(ChainArgs) <= 4096, "chain kernel arguments exceed 4 KiB");
+static_assert(sizeof(ChainSetupArgs) <= 4096, "chain setup arguments exceed 4 KiB");
 static_assert(sizeof(ApplyArgs) <= 4096, "apply kernel arguments exceed 4 KiB");
 static_assert(sizeof(EmaArgs) <= 4096, "EMA kernel arguments exceed 4 KiB");
 
@@ -205,6 +256,9 @@ hipError_t launch_apply(const ApplyArgs& a, int precision, int blocks, size_t ld
 hipError_t launch_ema(const EmaArgs& a, int blocks, hipStream_t s);
 hipError_t launch_adamw(const AdamArgs& a, int blocks, hipStream_t s);
 hipError_t launch_swap(const SwapArgs& a, int blocks, hipStream_t s);
+hipError_t launch_chain_setup(const ChainSetupArgs& a, hipStream_t s);
+hipError_t launch_chain(const ChainArgs& a, int workgroups, hipStream_t s);
+constexpr int kChainWgPerCu = 2;   // resident chain workgroups per CU (LDS-bound)
 
 const char* ns_kernel_name(int phase, int precision, bool compensated, bool fused_apply);
 

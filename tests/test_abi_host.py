@@ -30,7 +30,8 @@ def _declared_functions():
 def test_header_declares_the_abi():
     names = _declared_functions()
     assert names == sorted(["muon_workspace_size", "muon_step", "ema_update", "ema_swap", "adamw_step",
-                            "muon_last_error", "muon_version", "muon_profile_enable", "muon_profile_read"])
+                            "muon_last_error", "muon_version", "muon_profile_enable", "muon_profile_read",
+                            "muon_plan_cache_stats", "muon_set_ns_schedule"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -47,7 +48,8 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     for name in ["MUON_OK", "MUON_ERR_INVALID_ARG", "MUON_ERR_UNSUPPORTED", "MUON_ERR_WORKSPACE", "MUON_ERR_HIP",
                  "MUON_MAX_NS_STEPS", "MUON_MAX_SHORT_SIDE", "MUON_MAX_LONG_SIDE", "MUON_MAX_TENSORS",
-                 "MUON_NS_BF16", "MUON_NS_FP32", "MUON_NS_BF16X3"]:
+                 "MUON_NS_BF16", "MUON_NS_FP32", "MUON_NS_BF16X3", "MUON_NS_SCHEDULE_PHASES",
+                 "MUON_NS_SCHEDULE_CHAIN"]:
         m = re.search(rf"#define {name} \(?(-?\d+)\)?", text)
         assert m, name
         assert int(m.group(1)) == getattr(_lib, name), name
@@ -161,7 +163,11 @@ def test_workspace_size_properties():
     assert _ws([(512, 512)] * 22) > 21 * one
     assert _ws([(4, 4)]) % 256 == 0
     assert _ws([]) == 0 and _ws([(0, 4)]) == 0 and _ws([(4, 4)], 7) == 0
-    assert _ws([(512, 512)], 2) == one                   # the compensated mode needs no more
+    # the compensated mode needs no more; the base mode adds the NS chain's
+    # per-matrix record (64 B) and counters (two 128-byte lines, plus one status
+    # block per chain launch), each region 256-byte aligned
+    assert 0 <= one - _ws([(512, 512)], 2) <= 256 + 3 * 256
+    assert _ws([(512, 512)] * 22) - _ws([(512, 512)] * 22, 2) <= 22 * 64 + 23 * 256 + 512
 
 
 def test_ema_rejects_bad_arguments():
@@ -267,3 +273,53 @@ def test_ema_swap_rejects_bad_arguments():
     assert rc == _lib.MUON_ERR_UNSUPPORTED and "overlap" in err
     assert call(e=(ctypes.c_void_p * n)(0, BASE + (1 << 30)))[0] == _lib.MUON_ERR_INVALID_ARG
     assert call(p=(ctypes.c_void_p * n)(BASE + (2 << 30) + 1, BASE + (3 << 30)))[0] == _lib.MUON_ERR_INVALID_ARG
+
+
+def test_second_call_with_the_same_signature_reuses_the_schedule():
+    """muon_step plans once per signature (tensor descriptors, precision, workspace).
+
+    Without a GPU the call fails at its first HIP call, after validation and
+    planning, so the schedule cache can be observed here: the second call with
+    the same descriptors is a hit, a changed pointer or shape is a new plan.
+    """
+    entries = [_t(0, 512, 512), _t(1, 256, 512), _t(2, 2048, 512), _t(3, 512, 2048)]
+    built0, hits0, _ = _lib.plan_cache_stats()
+    rc, _ = _call(entries)
+    assert rc in (_lib.MUON_ERR_HIP, _lib.MUON_OK)
+    built1, hits1, _ = _lib.plan_cache_stats()
+    assert (built1, hits1) == (built0 + 1, hits0)
+    rc, _ = _call(entries, lr=0.05, mu=0.9, steps=3)   # scalars are not part of the signature
+    built2, hits2, _ = _lib.plan_cache_stats()
+    assert (built2, hits2) == (built1, hits1 + 1)
+    moved = list(entries)
+    moved[1] = _t(7, 256, 512)                          # another buffer: another signature
+    _call(moved)
+    built3, hits3, _ = _lib.plan_cache_stats()
+    assert (built3, hits3) == (built2 + 1, hits2)
+    reshaped = list(entries)
+    reshaped[0] = _t(0, 512, 384)
+    _call(reshaped)
+    built4, _, held = _lib.plan_cache_stats()
+    assert built4 == built3 + 1 and 1 <= held <= 8
+    # a rejected call plans nothing
+    rc, _ = _call(entries, lr=float("nan"))
+    assert rc == _lib.MUON_ERR_INVALID_ARG
+    assert _lib.plan_cache_stats()[0] == built4
+
+
+def test_ns_schedule_setting_is_part_of_the_signature():
+    entries = [_t(20, 512, 512), _t(21, 512, 2048)]
+    prev = _lib.set_ns_schedule(_lib.MUON_NS_SCHEDULE_PHASES)
+    try:
+        _call(entries)
+        built0, _, _ = _lib.plan_cache_stats()
+        _call(entries)
+        assert _lib.plan_cache_stats()[0] == built0
+        assert _lib.set_ns_schedule(_lib.MUON_NS_SCHEDULE_CHAIN) == _lib.MUON_NS_SCHEDULE_PHASES
+        _call(entries)                                   # another schedule: another plan
+        assert _lib.plan_cache_stats()[0] == built0 + 1
+        with pytest.raises(_lib.MuonError):
+            _lib.set_ns_schedule(7)
+        assert _lib.set_ns_schedule(_lib.MUON_NS_SCHEDULE_PHASES) == _lib.MUON_NS_SCHEDULE_CHAIN
+    finally:
+        _lib.set_ns_schedule(prev)

@@ -64,6 +64,16 @@ def load() -> ctypes.CDLL:
         raise RuntimeError(
             f"{LIB_PATH} is missing: build it with `python -m muon_optimizer_step_amd.build` "
             "(there is no fallback implementation)")
+    # The library must run on the same HIP runtime as torch, whose device
+    # pointers and streams it is handed: torch's wheel carries its own
+    # libamdhip64, and loading the library first would bind it to the system
+    # copy, a second runtime in the process that then finds no device.  So torch
+    # (when installed) is imported first and the library links against the
+    # runtime it loaded.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     f = lib.muon_workspace_size
     f.argtypes = [ctypes.POINTER(MuonTensor), ctypes.c_int32, ctypes.c_int32]

@@ -115,6 +115,23 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
               const float* ns_coeffs, int32_t ns_precision, float ema_decay, void* workspace,
               size_t workspace_bytes, void* stream);
 
+/* muon_step for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results and errors as muon_step, without the workspace: the
+ * library's static device workspace of MUON_STATIC_WORKSPACE_BYTES (a
+ * file-scope device array that each GPU the library runs on holds until the
+ * process ends) takes its place.  Calls that need more workspace than that
+ * (muon_workspace_size) fail with MUON_ERR_WORKSPACE before anything is
+ * enqueued.  The call allocates nothing (no hipMalloc, no allocating library
+ * routine).  Every call on one GPU shares that GPU's static workspace and it
+ * keeps the last call's contents (which no call depends on): calls that
+ * overlap in time on one GPU, on any streams, race and must be serialised by
+ * the caller. */
+#define MUON_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+int muon_step_static(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
+                     int32_t nesterov, float weight_decay, int32_t row_norm, int32_t ns_steps,
+                     const float* ns_coeffs, int32_t ns_precision, float ema_decay, void* stream);
+
 /* Weight EMA over n fp32 tensors: ema[i][j] = decay*ema[i][j] + (1-decay)*params[i][j]
  * for j < numel[i].  Defined by "Record: L_ParallelResiduals_UNetSkips_DepthRecur_
  * Muon_ 1.0901" (PR #1893), "Architecture and training stack", EMA row (an

@@ -10,6 +10,6 @@ from ._lib import (  # noqa: F401
     load, set_ns_schedule, plan_cache_stats,
 )
 from .api import (  # noqa: F401
-    muon_step, ema_update, ema_swap, adamw_step, workspace_size, profile_enable, profile_read, version,
+    muon_step, muon_step_static, ema_update, ema_swap, adamw_step, workspace_size, profile_enable, profile_read, version,
     PreparedMuonStep, PreparedEma, PreparedAdamW,
 )

@@ -16,6 +16,7 @@ MUON_MAX_NS_STEPS = 16
 MUON_MAX_SHORT_SIDE = 8192
 MUON_MAX_LONG_SIDE = 65536
 MUON_MAX_TENSORS = 4096
+MUON_STATIC_WORKSPACE_BYTES = 64 << 20
 MUON_NS_BF16 = 0
 MUON_NS_FP32 = 1
 MUON_NS_BF16X3 = 2
@@ -82,6 +83,11 @@ def load() -> ctypes.CDLL:
     f.argtypes = [ctypes.POINTER(MuonTensor), ctypes.c_int32, ctypes.c_float, ctypes.c_float, ctypes.c_int32,
                   ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_float), ctypes.c_int32,
                   ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    f = lib.muon_step_static
+    f.argtypes = [ctypes.POINTER(MuonTensor), ctypes.c_int32, ctypes.c_float, ctypes.c_float, ctypes.c_int32,
+                  ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_float), ctypes.c_int32,
+                  ctypes.c_float, ctypes.c_void_p]
     f.restype = ctypes.c_int
     f = lib.ema_update
     f.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_int64),

@@ -124,6 +124,27 @@ def muon_step(params, grads, moms, *, lr: float, momentum: float, weight_decay: 
     _lib.check(rc)
 
 
+def muon_step_static(params, grads, moms, *, lr: float, momentum: float, weight_decay: float, coeffs,
+                     nesterov: bool = True, row_norm: bool = True, ns_precision: int = _lib.MUON_NS_BF16,
+                     update_outs=None, emas=None, ema_decay: float = 0.0, stream=None) -> None:
+    """muon_step on the library's static device workspace: allocates nothing.
+
+    For callers that cannot allocate (graph capture, serving loops).  Calls that
+    overlap in time on one GPU race on the shared static workspace.
+    """
+    lib = _lib.load()
+    n = len(params)
+    if len(grads) != n or len(moms) != n:
+        raise ValueError("params, grads and moms must have the same length")
+    table = _lib.tensor_table(_entries(params, grads, moms, update_outs, emas))
+    carr, steps = _lib.coeff_array(coeffs)
+    device = params[0].device if n else None
+    rc = lib.muon_step_static(table, n, float(lr), float(momentum), int(bool(nesterov)), float(weight_decay),
+                              int(bool(row_norm)), steps, carr if steps else None, int(ns_precision),
+                              float(ema_decay), _stream_handle(stream, device))
+    _lib.check(rc)
+
+
 def ema_update(emas, params, decay: float, stream=None) -> None:
     """emas[i] = decay * emas[i] + (1 - decay) * params[i] for fp32 tensors of any shape."""
     lib = _lib.load()

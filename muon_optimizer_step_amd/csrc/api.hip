@@ -651,6 +651,33 @@ std::shared_ptr<Schedule> find_schedule(const muon_tensor_t* t, int n, int mode,
 }
 
 
+// ------------------------------------------------------------- static workspace
+// The allocation-free entry point's workspace: a file-scope device array that
+// every GPU the library runs on holds until the process ends.  Host code never
+// uses the array's name as an address: its device address comes from
+// hipGetSymbolAddress, once per device, and is kept here.
+constexpr size_t kStaticScratchBytes = MUON_STATIC_WORKSPACE_BYTES;
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;
+
+int static_scratch(void*& out) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return fail(MUON_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(err));
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    auto it = g_scratch_ptr.find(dev);
+    if (it == g_scratch_ptr.end()) {
+        void* ptr = nullptr;
+        err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (err != hipSuccess || !ptr)
+            return fail(MUON_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(err));
+        it = g_scratch_ptr.emplace(dev, ptr).first;
+    }
+    out = it->second;
+    return MUON_OK;
+}
+
 }  // namespace
 }  // namespace muon
 
@@ -1000,6 +1027,23 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
         if (err != hipSuccess) return fail(MUON_ERR_HIP, "lane join failed: %s", hipGetErrorString(err));
     }
     return MUON_OK;
+}
+
+int muon_step_static(const muon_tensor_t* tensors, int32_t n, float lr, float momentum, int32_t nesterov,
+                     float weight_decay, int32_t row_norm, int32_t ns_steps, const float* ns_coeffs,
+                     int32_t ns_precision, float ema_decay, void* stream) {
+    int rc = validate_tensors(tensors, n, ns_precision);
+    if (rc) return rc;
+    Plan p;
+    make_plan(tensors, n, ns_precision, p);
+    if (p.bytes > kStaticScratchBytes)
+        return fail(MUON_ERR_WORKSPACE,
+                    "these matrices need %zu bytes of workspace; the static workspace holds %zu (use muon_step with "
+                    "a caller workspace)", p.bytes, kStaticScratchBytes);
+    void* ws = nullptr;
+    if ((rc = static_scratch(ws))) return rc;
+    return muon_step(tensors, n, lr, momentum, nesterov, weight_decay, row_norm, ns_steps, ns_coeffs, ns_precision,
+                     ema_decay, ws, kStaticScratchBytes, stream);
 }
 
 int muon_set_ns_schedule(int32_t schedule) {

@@ -31,7 +31,7 @@ def test_header_declares_the_abi():
     names = _declared_functions()
     assert names == sorted(["muon_workspace_size", "muon_step", "ema_update", "ema_swap", "adamw_step",
                             "muon_last_error", "muon_version", "muon_profile_enable", "muon_profile_read",
-                            "muon_plan_cache_stats", "muon_set_ns_schedule"])
+                            "muon_plan_cache_stats", "muon_set_ns_schedule", "muon_step_static"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -323,3 +323,16 @@ def test_ns_schedule_setting_is_part_of_the_signature():
         assert _lib.set_ns_schedule(_lib.MUON_NS_SCHEDULE_PHASES) == _lib.MUON_NS_SCHEDULE_CHAIN
     finally:
         _lib.set_ns_schedule(prev)
+
+
+def test_static_entry_rejects_what_the_static_workspace_cannot_hold():
+    """muon_step_static checks the workspace it would need before any HIP call."""
+    lib = _lib.load()
+    entries = [_t(40 + i, 2048, 512) for i in range(30)]   # about 150 MB of workspace
+    table = _lib.tensor_table(entries)
+    assert lib.muon_workspace_size(table, len(entries), 0) > _lib.MUON_STATIC_WORKSPACE_BYTES
+    carr, k = _lib.coeff_array([(3.4445, -4.775, 2.0315)] * 5)
+    rc = lib.muon_step_static(table, len(entries), 0.02, 0.95, 1, 0.1, 1, k, carr, 0, 0.99, None)
+    assert rc == _lib.MUON_ERR_WORKSPACE
+    assert "static workspace" in lib.muon_last_error().decode()
+    assert lib.muon_step_static(table, 0, 0.02, 0.95, 1, 0.1, 1, k, carr, 0, 0.99, None) == _lib.MUON_ERR_INVALID_ARG

@@ -51,9 +51,14 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (counter calibration) and exit")
-    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
-                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter files of this bench and of "
-                         "--calibrate-copy into profiles/hbm_traffic.json, then exit (no GPU needed)")
+    ap.add_argument("--ema-only", type=int, default=0, metavar="CALLS",
+                    help="only run CALLS calls of ema_update over every parameter of the workload (two state "
+                         "copies in turn) and exit: the counter run of the EMA pass")
+    ap.add_argument("--summarize-counters", nargs="+",
+                    metavar="CSV",
+                    help="FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV [EMA_FETCH_CSV EMA_WRITE_CSV]: turn "
+                         "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter files of this bench, of --calibrate-copy "
+                         "and of --ema-only into profiles/hbm_traffic.json, then exit (no GPU needed)")
     ap.add_argument("--summarize-mfma", metavar="MOPS_CSV",
                     help="turn a rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 "
                          "SQ_INSTS_VALU_MFMA_MOPS_F8 counter "
@@ -73,7 +78,10 @@ def _kernel_key(name: str) -> str:
         prec, comp, fuse = int(m.group(1)), m.group(2) == "true", m.group(3) == "true"
         base = "ns_update_apply" if fuse else "ns_update"
         return base + ("_fp32" if prec == 1 else ("_bf16x3" if comp else "_bf16"))
-    for k in ("prep_kernel", "apply_kernel", "ema_kernel", "frob_kernel", "adamw_kernel", "swap_kernel"):
+    if "ns_chain_kernel" in name:
+        return "ns_chain_bf16"
+    for k in ("chain_setup_kernel", "prep_kernel", "apply_kernel", "ema_kernel", "frob_kernel", "adamw_kernel",
+              "swap_kernel"):
         if k in name:
             return k.replace("_kernel", "")
     return "copy" if "copyBuffer" in name else name
@@ -98,9 +106,11 @@ def _per_dispatch(path: str, counter: str):
 COUNTER_WORKLOAD = "model11L512"   # the counter runs profile the default bench workload
 
 
-def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes=1 << 30, out_path=None):
+def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, ema_fetch_csv=None, ema_write_csv=None,
+                       copy_bytes=1 << 30, out_path=None):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by the copy calibration; written to out_path
-    (profiles/hbm_traffic.json by default) and returned."""
+    (profiles/hbm_traffic.json by default) and returned.  The EMA-only run's ema dispatches, if given, become
+    the entry "ema_full" in bytes per call (its two launches summed)."""
     cf = _per_dispatch(copy_fetch_csv, "FETCH_SIZE").get("copy")
     cw = _per_dispatch(copy_write_csv, "WRITE_SIZE").get("copy")
     f_scale = copy_bytes / (cf * 1024.0)
@@ -114,6 +124,14 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, cop
         fb = fetch[k] * 1024.0 * f_scale
         wb = write[k] * 1024.0 * w_scale
         kernels[k] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb)}
+    if ema_fetch_csv and ema_write_csv:
+        ef = _per_dispatch(ema_fetch_csv, "FETCH_SIZE").get("ema")
+        ew = _per_dispatch(ema_write_csv, "WRITE_SIZE").get("ema")
+        if ef is not None and ew is not None:
+            per_call = 2   # the 187 tensors take two launches (144 table entries per launch)
+            fb, wb = ef * 1024.0 * f_scale * per_call, ew * 1024.0 * w_scale * per_call
+            kernels["ema_full"] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb),
+                                   "note": "bytes per ema_update call over all parameters (two launches)"}
     out = {"source_hash": source_hash(), "workload": COUNTER_WORKLOAD, "fetch_scale": f_scale, "write_scale": w_scale,
            "calibration": f"{copy_bytes} B device-to-device copy (5 runs): FETCH_SIZE {cf:.0f} KiB, WRITE_SIZE {cw:.0f} KiB per dispatch",
            "kernels": kernels}
@@ -172,6 +190,25 @@ def calibrate_copy(mib: int) -> None:
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 5}), flush=True)
+
+
+def ema_only(calls: int, seed: int) -> None:
+    """ema_update over every parameter of the bench workload, `calls` times, two state copies in turn."""
+    import torch
+    import muon_optimizer_step_amd as ms
+    import workloads as wl
+    w = wl.workload(WORKLOAD)
+    dev = torch.device("cuda:0")
+    sets = []
+    for r in range(2):
+        st = wl.make_state(w, seed + r)
+        sets.append(ms.PreparedEma([torch.from_numpy(e).to(dev) for e in st["ema"]],
+                                   [torch.from_numpy(p).to(dev) for p in st["params"]]))
+    torch.cuda.synchronize()
+    for i in range(calls):
+        sets[i % 2](w.ema_decay)
+    torch.cuda.synchronize()
+    print(json.dumps({"ema_only_calls": calls, "params": w.n_params}), flush=True)
 
 
 def kernel_model(w, fused=True):
@@ -369,7 +406,13 @@ def main():
         calibrate_copy(args.calibrate_copy)
         return
     if args.summarize_counters:
+        if len(args.summarize_counters) not in (4, 6):
+            print("--summarize-counters takes 4 or 6 files", file=sys.stderr)
+            sys.exit(2)
         print(json.dumps(summarize_counters(*args.summarize_counters), indent=1))
+        return
+    if args.ema_only:
+        ema_only(args.ema_only, args.seed)
         return
     if args.summarize_mfma:
         print(json.dumps(summarize_mfma(args.summarize_mfma), indent=1))
@@ -390,6 +433,7 @@ def main():
     # 256 MB MALL.  One workspace serves all of them (the steps are serial on
     # one stream).
     states = []
+    ema_lists = []
     workspace = None
     for r in range(args.rotate):
         st = wl.make_state(w, args.seed + r)
@@ -404,6 +448,7 @@ def main():
         muon = ms.PreparedMuonStep(P[:nm], G, M, emas=E[:nm], workspace=workspace)
         workspace = muon.workspace
         states.append((muon, ms.PreparedEma(E[nm:], P[nm:]), ms.PreparedAdamW(P[nm:], AG, AM, AV, emas=E[nm:])))
+        ema_lists.append((E, P))
         if r == 0:
             swap_lists = (E, P)
     stream = torch.cuda.current_stream(dev)
@@ -597,6 +642,39 @@ def main():
     out["full_optimizer_step"] = {"steps_per_s": round(1.0 / full_el, 2), "ms_per_step": round(full_el * 1e3, 4),
                                   "what": "muon_step on the 66 matrices (EMA fused) + adamw_step on the 121 other "
                                           "tensors (EMA fused)"}
+    # The weight EMA as a pass of its own over all 187 tensors (34,401,372
+    # parameters; read E and P, write E: 12 B per parameter), the state copies
+    # used in turn so that no call finds its tensors in the MALL.
+    full = [ms.PreparedEma(E, P) for E, P in ema_lists]
+    for i in range(3):
+        full[i % len(full)](w.ema_decay, stream=stream)
+    torch.cuda.synchronize()
+    te = time.perf_counter()
+    for i in range(args.steps):
+        full[i % len(full)](w.ema_decay, stream=stream)
+    torch.cuda.synchronize()
+    e_wall_us = (time.perf_counter() - te) / args.steps * 1e6
+    ms.profile_read(reset=True)
+    ms.profile_enable(True)
+    for i in range(args.steps):
+        full[i % len(full)](w.ema_decay, stream=stream)
+    torch.cuda.synchronize()
+    ms.profile_enable(False)
+    eprof = ms.profile_read(reset=True)["ema"]
+    e_us = eprof[1] / args.steps * 1e3          # summed launch durations per call (HIP events)
+    e_bytes = 12.0 * w.n_params
+    e_traffic = traffic_for("ema_full", w.name)
+    out["ema_full"] = {"tensors": len(ema_lists[0][0]), "elements": w.n_params,
+                       "us_per_call": round(e_wall_us, 3), "kernel_us_per_call": round(e_us, 3),
+                       "launches_per_call": eprof[0] / args.steps, "algorithmic_bytes_per_call": e_bytes,
+                       "gbs": round(e_bytes / (e_wall_us * 1e-6) / 1e9, 1),
+                       "frac_of_hbm_peak": round(e_bytes / (e_wall_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                       "kernel_gbs": round(e_bytes / (e_us * 1e-6) / 1e9, 1),
+                       "counter_bytes_per_call": e_traffic,
+                       "counter_frac_of_hbm_peak": (round(e_traffic / (e_wall_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                                                    if e_traffic else None),
+                       "what": "ema_update over every parameter tensor of the model as its own pass, "
+                               f"{args.steps} calls back to back on two state copies in turn"}
     # EMA swap-in over all 187 tensors (read and write both buffers: 16 B per parameter)
     sw_e, sw_p = swap_lists
     for _ in range(3):
@@ -616,7 +694,8 @@ def main():
                        "gbs": round(sw_bytes / (sw_us * 1e-6) / 1e9, 1),
                        "frac_of_hbm_peak": round(sw_bytes / (sw_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     print(f"[bench] adamw {out['adamw']['us_per_call']} us per call; full optimizer step "
-          f"{out['full_optimizer_step']['steps_per_s']} steps/s", flush=True)
+          f"{out['full_optimizer_step']['steps_per_s']} steps/s; EMA over all parameters "
+          f"{out['ema_full']['us_per_call']} us ({out['ema_full']['gbs']} GB/s)", flush=True)
     if not args.no_other_configs:
         # the other workloads (parity cases), each on its own; steps/s only
         del states, workspace

@@ -435,14 +435,14 @@ __global__ __launch_bounds__(kEmaThreads) void ema_kernel(const EmaArgs a) {
     if (vec && end - base == kEmaElemsPerBlock) {
         floatx4* e4 = reinterpret_cast<floatx4*>(T.ema + base);
         const floatx4* p4 = reinterpret_cast<const floatx4*>(T.param + base);
-        floatx4 ev[4], pv[4];
+        floatx4 ev[kEmaVec], pv[kEmaVec];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < kEmaVec; ++k) {
             ev[k] = __builtin_nontemporal_load(e4 + threadIdx.x + k * kEmaThreads);
             pv[k] = __builtin_nontemporal_load(p4 + threadIdx.x + k * kEmaThreads);
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < kEmaVec; ++k) {
             floatx4 r;
 #pragma unroll
             for (int e = 0; e < 4; ++e) r[e] = fmaf(d, ev[k][e], omd * pv[k][e]);
@@ -465,14 +465,14 @@ __global__ __launch_bounds__(kEmaThreads) void swap_kernel(const SwapArgs a) {
     if (vec && end - base == kEmaElemsPerBlock) {
         floatx4* a4 = reinterpret_cast<floatx4*>(T.a + base);
         floatx4* b4 = reinterpret_cast<floatx4*>(T.b + base);
-        floatx4 av[4], bv[4];
+        floatx4 av[kEmaVec], bv[kEmaVec];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < kEmaVec; ++k) {
             av[k] = __builtin_nontemporal_load(a4 + threadIdx.x + k * kEmaThreads);
             bv[k] = __builtin_nontemporal_load(b4 + threadIdx.x + k * kEmaThreads);
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < kEmaVec; ++k) {
             __builtin_nontemporal_store(bv[k], a4 + threadIdx.x + k * kEmaThreads);
             __builtin_nontemporal_store(av[k], b4 + threadIdx.x + k * kEmaThreads);
         }

@@ -199,7 +199,8 @@ struct EmaArgs {
     float one_minus_decay;
 };
 constexpr int kEmaThreads = 256;
-constexpr int kEmaElemsPerBlock = kEmaThreads * 4 * 4;  // float4 x 4 per thread
+constexpr int kEmaVec = 4;                                    // float4 per thread per operand
+constexpr int kEmaElemsPerBlock = kEmaThreads * 4 * kEmaVec;
 
 // Swap of two fp32 buffers per tensor (the EMA swap-in), same chunking as the EMA
 struct SwapTensor {

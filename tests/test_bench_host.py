@@ -37,6 +37,8 @@ def test_more_than_one_gpu_is_refused_before_any_gpu_work():
     ("muon::(anonymous namespace)::ema_kernel(muon::EmaArgs)", "ema"),
     ("muon::(anonymous namespace)::adamw_kernel(muon::AdamArgs)", "adamw"),
     ("__amd_rocclr_copyBuffer", "copy"),
+    ("muon::(anonymous namespace)::ns_chain_kernel(muon::ChainArgs)", "ns_chain_bf16"),
+    ("muon::(anonymous namespace)::chain_setup_kernel(muon::ChainSetupArgs)", "chain_setup"),
 ])
 def test_kernel_symbols_map_to_hook_names(symbol, key):
     assert bench._kernel_key(symbol) == key
@@ -74,6 +76,23 @@ def test_traffic_summary_scales_by_the_copy_and_averages_per_dispatch(tmp_path):
     assert out["source_hash"] == bench.source_hash() and out["workload"] == "model11L512"
     with open(out_path) as f:
         assert json.load(f) == out
+
+
+def test_ema_only_run_becomes_the_full_ema_entry(tmp_path):
+    """The EMA-only counter run (all 187 tensors, two launches per call) is reported per call."""
+    p = {k: str(tmp_path / f"{k}.csv") for k in ("fetch", "write", "cfetch", "cwrite", "efetch", "ewrite")}
+    EMA = "muon::(anonymous namespace)::ema_kernel(muon::EmaArgs)"
+    _write_counters(p["cfetch"], [(1, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 524288)])
+    _write_counters(p["cwrite"], [(1, "__amd_rocclr_copyBuffer", "WRITE_SIZE", 1048576)])
+    _write_counters(p["fetch"], [(4, GRAM, "FETCH_SIZE", 10)])
+    _write_counters(p["write"], [(4, GRAM, "WRITE_SIZE", 4)])
+    _write_counters(p["efetch"], [(1, EMA, "FETCH_SIZE", 100), (2, EMA, "FETCH_SIZE", 300)])
+    _write_counters(p["ewrite"], [(1, EMA, "WRITE_SIZE", 60), (2, EMA, "WRITE_SIZE", 140)])
+    out = bench.summarize_counters(p["fetch"], p["write"], p["cfetch"], p["cwrite"], p["efetch"], p["ewrite"],
+                                   out_path=str(tmp_path / "t.json"))
+    full = out["kernels"]["ema_full"]
+    assert full["fetch_bytes"] == 2 * 200 * 1024 * 2 and full["write_bytes"] == 2 * 100 * 1024
+    assert "ema" not in out["kernels"] or out["kernels"]["ema"]["bytes_per_launch"] != full["bytes_per_launch"]
 
 
 def test_mfma_summary_counts_512_flops_per_mop(tmp_path):
@@ -115,6 +134,10 @@ def test_work_model_of_the_bench_workload():
     ns = sum(k * (4.0 * min(r, c) ** 2 * max(r, c) + 2.0 * min(r, c) ** 3) for _, r, c in w.matrices)
     got = sum(model[n]["flops"] for n in ("ns_gram_bf16", "ns_square_bf16", "ns_update_bf16", "ns_update_apply_bf16"))
     assert got == pytest.approx(ns, rel=1e-12)
+    assert model["ns_chain_bf16"]["flops"] == pytest.approx(ns, rel=1e-12)   # the chain runs all of it
+    per_phase = sum(model[n]["bytes"] for n in ("ns_gram_bf16", "ns_square_bf16", "ns_update_bf16",
+                                                  "ns_update_apply_bf16"))
+    assert model["ns_chain_bf16"]["bytes"] == pytest.approx(per_phase, rel=1e-12)
     assert ns == pytest.approx(372.8e9, rel=1e-3)
     elems = sum(r * c for _, r, c in w.matrices)
     assert elems == 31_719_424 and w.n_params == 34_401_372

@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3     # MI355X dense fp32 MFMA
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 WORKLOAD = 2
 METRIC = "Muon+EMA steps/s (66-matrix 11L-512d set); NS bf16 MFMA TFLOP/s vs peak"
@@ -59,10 +60,16 @@ def parse():
                     help="FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV [EMA_FETCH_CSV EMA_WRITE_CSV]: turn "
                          "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter files of this bench, of --calibrate-copy "
                          "and of --ema-only into profiles/hbm_traffic.json, then exit (no GPU needed)")
-    ap.add_argument("--summarize-mfma", metavar="MOPS_CSV",
-                    help="turn a rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 "
-                         "SQ_INSTS_VALU_MFMA_MOPS_F8 counter "
-                         "file of this bench into profiles/mfma_counters.json, then exit (no GPU needed)")
+    ap.add_argument("--summarize-mfma", nargs="+", metavar="MOPS_CSV",
+                    help="MOPS_CSV [CHAIN_MOPS_CSV]: turn rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+                         "SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_VALU_MFMA_MOPS_F8 counter files of this bench (and of "
+                         "its chain-schedule run) into profiles/mfma_counters.json, then exit (no GPU needed)")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
+                    help="turn the rocprofv3 --kernel-trace --stats summary of this bench into "
+                         "profiles/kernel_trace.json (average launch duration per kernel), then exit (no GPU needed)")
+    ap.add_argument("--counter-run", action="store_true",
+                    help="time only the step itself (no schedule comparison, AdamW, EMA or swap passes): the "
+                         "run under rocprofv3 counters, whose per-kernel averages must not mix other passes")
     return ap.parse_args()
 
 
@@ -107,10 +114,11 @@ COUNTER_WORKLOAD = "model11L512"   # the counter runs profile the default bench 
 
 
 def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, ema_fetch_csv=None, ema_write_csv=None,
-                       copy_bytes=1 << 30, out_path=None):
+                       chain_fetch_csv=None, chain_write_csv=None, copy_bytes=1 << 30, out_path=None):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by the copy calibration; written to out_path
     (profiles/hbm_traffic.json by default) and returned.  The EMA-only run's ema dispatches, if given, become
-    the entry "ema_full" in bytes per call (its two launches summed)."""
+    the entry "ema_full" in bytes per call (its two launches summed); the chain-schedule run's chain kernels,
+    if given, their own entries."""
     cf = _per_dispatch(copy_fetch_csv, "FETCH_SIZE").get("copy")
     cw = _per_dispatch(copy_write_csv, "WRITE_SIZE").get("copy")
     f_scale = copy_bytes / (cf * 1024.0)
@@ -132,6 +140,13 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, ema
             fb, wb = ef * 1024.0 * f_scale * per_call, ew * 1024.0 * w_scale * per_call
             kernels["ema_full"] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb),
                                    "note": "bytes per ema_update call over all parameters (two launches)"}
+    if chain_fetch_csv and chain_write_csv:
+        cfch = _per_dispatch(chain_fetch_csv, "FETCH_SIZE")
+        cwr = _per_dispatch(chain_write_csv, "WRITE_SIZE")
+        for k in ("ns_chain_bf16", "chain_setup"):
+            if k in cfch and k in cwr:
+                fb, wb = cfch[k] * 1024.0 * f_scale, cwr[k] * 1024.0 * w_scale
+                kernels[k] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb)}
     out = {"source_hash": source_hash(), "workload": COUNTER_WORKLOAD, "fetch_scale": f_scale, "write_scale": w_scale,
            "calibration": f"{copy_bytes} B device-to-device copy (5 runs): FETCH_SIZE {cf:.0f} KiB, WRITE_SIZE {cw:.0f} KiB per dispatch",
            "kernels": kernels}
@@ -141,21 +156,54 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, ema
     return out
 
 
-def summarize_mfma(csv_path, out_path=None):
+def summarize_mfma(csv_path, chain_csv=None, out_path=None):
     """Executed MFMA flops per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16 / _F32 / _F8, 512 flops per count);
-    written to out_path (profiles/mfma_counters.json by default) and returned."""
+    written to out_path (profiles/mfma_counters.json by default) and returned.  chain_csv: the
+    chain-schedule run, whose chain kernel gets its own entry."""
     kernels = {}
     for counter in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_INSTS_VALU_MFMA_MOPS_F8"):
         for k, v in _per_dispatch(csv_path, counter).items():
             if k == "copy":
                 continue
             kernels.setdefault(k, {})[counter] = v
+        if chain_csv:
+            v = _per_dispatch(chain_csv, counter).get("ns_chain_bf16")
+            if v is not None:
+                kernels.setdefault("ns_chain_bf16", {})[counter] = v
     out = {"source_hash": source_hash(), "workload": COUNTER_WORKLOAD,
            "kernels": {k: dict(v, flops_per_launch=512.0 * sum(v.values())) for k, v in sorted(kernels.items())}}
     path = out_path or os.path.join(ROOT, "profiles", "mfma_counters.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     return out
+
+
+def summarize_trace(stats_csv, out_path=None):
+    """Average launch duration (us) and launch count per kernel from a rocprofv3 kernel_stats.csv; written
+    to out_path (profiles/kernel_trace.json by default) and returned."""
+    import csv
+    kernels = {}
+    for r in csv.DictReader(open(stats_csv)):
+        k = _kernel_key(r["Name"])
+        e = kernels.setdefault(k, {"calls": 0, "total_ns": 0.0})
+        e["calls"] += int(r["Calls"])
+        e["total_ns"] += float(r["TotalDurationNs"])
+    out = {"source_hash": source_hash(), "workload": COUNTER_WORKLOAD,
+           "kernels": {k: {"calls": v["calls"], "avg_us": round(v["total_ns"] / v["calls"] / 1e3, 3)}
+                       for k, v in sorted(kernels.items()) if k != "copy"}}
+    path = out_path or os.path.join(ROOT, "profiles", "kernel_trace.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
+def rocprof_avg_us(kernel: str, workload: str = COUNTER_WORKLOAD):
+    """Average launch duration from the committed rocprofv3 trace summary, if it matches these sources."""
+    data = _counter_file("kernel_trace.json", workload)
+    if data is None:
+        return None
+    k = data.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("avg_us")
 
 
 def _counter_file(name: str, workload: str):
@@ -177,6 +225,18 @@ def mfma_counter_flops(kernel: str, workload: str = COUNTER_WORKLOAD):
         return None
     k = data.get("kernels", {}).get(kernel)
     return None if k is None else k.get("flops_per_launch")
+
+
+def mfma_counter_split(kernel: str, workload: str = COUNTER_WORKLOAD):
+    """(bf16, fp8, fp32) executed MFMA flops per launch from the committed counter summary, or None."""
+    data = _counter_file("mfma_counters.json", workload)
+    if data is None:
+        return None
+    k = data.get("kernels", {}).get(kernel)
+    if k is None:
+        return None
+    return tuple(512.0 * k.get(c, 0.0) for c in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F8",
+                                                 "SQ_INSTS_VALU_MFMA_MOPS_F32"))
 
 
 def calibrate_copy(mib: int) -> None:
@@ -406,16 +466,19 @@ def main():
         calibrate_copy(args.calibrate_copy)
         return
     if args.summarize_counters:
-        if len(args.summarize_counters) not in (4, 6):
-            print("--summarize-counters takes 4 or 6 files", file=sys.stderr)
+        if len(args.summarize_counters) not in (4, 6, 8):
+            print("--summarize-counters takes 4, 6 or 8 files", file=sys.stderr)
             sys.exit(2)
         print(json.dumps(summarize_counters(*args.summarize_counters), indent=1))
         return
     if args.ema_only:
         ema_only(args.ema_only, args.seed)
         return
+    if args.summarize_trace:
+        print(json.dumps(summarize_trace(args.summarize_trace), indent=1))
+        return
     if args.summarize_mfma:
-        print(json.dumps(summarize_mfma(args.summarize_mfma), indent=1))
+        print(json.dumps(summarize_mfma(*args.summarize_mfma[:2]), indent=1))
         return
     import numpy as np
     import torch
@@ -493,18 +556,20 @@ def main():
 
     # The other Newton-Schulz schedule on the same state, for comparison.
     other = "chain" if args.ns_schedule == "phases" else "phases"
-    ms.set_ns_schedule(ms.MUON_NS_SCHEDULE_CHAIN if other == "chain" else ms.MUON_NS_SCHEDULE_PHASES)
-    for _ in range(5):
-        step()
-    torch.cuda.synchronize()
-    tc = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    other_rate = args.steps / (time.perf_counter() - tc)
-    ms.set_ns_schedule(ms.MUON_NS_SCHEDULE_CHAIN if args.ns_schedule == "chain" else ms.MUON_NS_SCHEDULE_PHASES)
-    print(f"[bench] {args.ns_schedule} schedule {value:.1f} steps/s, {other} schedule {other_rate:.1f} steps/s",
-          flush=True)
+    other_rate = None
+    if not args.counter_run:
+        ms.set_ns_schedule(ms.MUON_NS_SCHEDULE_CHAIN if other == "chain" else ms.MUON_NS_SCHEDULE_PHASES)
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
+        tc = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        other_rate = args.steps / (time.perf_counter() - tc)
+        ms.set_ns_schedule(ms.MUON_NS_SCHEDULE_CHAIN if args.ns_schedule == "chain" else ms.MUON_NS_SCHEDULE_PHASES)
+        print(f"[bench] {args.ns_schedule} schedule {value:.1f} steps/s, {other} schedule {other_rate:.1f} steps/s",
+              flush=True)
 
     # Spread of single steps: an event pair around each step on the caller's
     # stream (the lanes join it before the step's last kernel).
@@ -563,6 +628,15 @@ def main():
     ns_counted = (sum(c * kernels[k]["launches_per_step"] for c, k in zip(counted, ns_names))
                   if counted and all(c is not None for c in counted) else None)
     traffic = traffic_for(dom, w.name)
+    # executed work by operand type: the square's cross terms run on the fp8 MFMA
+    # (twice the bf16 rate), so the MFMA time at peak counts each type at its own peak
+    split = [mfma_counter_split(k, w.name) for k in ns_names]
+    if split and all(x is not None for x in split):
+        ex_bf16 = sum(x[0] * kernels[k]["launches_per_step"] for x, k in zip(split, ns_names))
+        ex_fp8 = sum(x[1] * kernels[k]["launches_per_step"] for x, k in zip(split, ns_names))
+        mfma_at_peak_ms = (ex_bf16 / (BF16_PEAK_TFLOPS * 1e12) + ex_fp8 / (FP8_PEAK_TFLOPS * 1e12)) * 1e3
+    else:
+        ex_bf16 = ex_fp8 = mfma_at_peak_ms = None
 
     describe = {
         2: "66 matrices (11 layers x Q/K/V/O/up/down at d=512)",
@@ -594,7 +668,12 @@ def main():
                      "algorithmic_bytes_per_launch": round(d["bytes_per_launch"]),
                      "avg_launch_us": round(d["avg_us"], 3),
                      "mfma_frac": round(d.get("tflops", 0.0) / BF16_PEAK_TFLOPS, 4),
-                     "hbm_frac": round(d["gbs"] / HBM_PEAK_GBS, 4)},
+                     "hbm_frac": round(d["gbs"] / HBM_PEAK_GBS, 4),
+                     "rocprof_avg_launch_us": rocprof_avg_us(dom, w.name),
+                     "rocprof_frac": (round(achieved * d["avg_us"] / rocprof_avg_us(dom, w.name) / peak, 4)
+                                      if rocprof_avg_us(dom, w.name) else None),
+                     "timing": "avg_launch_us from HIP events around each launch inside this run (on the launch's "
+                               "stream); rocprof_avg_launch_us from profiles/kernel_trace.json of the same sources"},
         "streaming": streaming_fractions(kernels, w.name),
         "ns": {"tflops_over_summed_kernel_time": round(ns_tflops, 2) if ns_tflops else None,
                "frac_of_bf16_peak": round(ns_tflops / BF16_PEAK_TFLOPS, 4) if ns_tflops else None,
@@ -602,14 +681,23 @@ def main():
                "tflops_over_step_time": round(ns_flops / elapsed * args.steps / 1e12, 2),
                "executed_flops_per_step": ns_counted,
                "executed_tflops_over_summed_kernel_time":
-                   round(ns_counted / (ns_ms * 1e-3) / 1e12, 2) if ns_counted and ns_ms > 0 else None},
+                   round(ns_counted / (ns_ms * 1e-3) / 1e12, 2) if ns_counted and ns_ms > 0 else None,
+               "executed_bf16_flops_per_step": ex_bf16, "executed_fp8_flops_per_step": ex_fp8,
+               "mfma_busy_frac_at_peaks": (round(mfma_at_peak_ms / ns_ms, 4) if mfma_at_peak_ms and ns_ms > 0
+                                           else None),
+               "note": "executed work from profiles/mfma_counters.json; the fp8 share (the square's cross terms) "
+                       "is priced at the 5.0 PFLOP/s fp8 peak, the bf16 share at 2.5 PFLOP/s"},
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "steps_per_s_spread": spread,
-        "ns_schedule": {"timed": args.ns_schedule, "other": other, "other_steps_per_s": round(other_rate, 2)},
+        "ns_schedule": {"timed": args.ns_schedule, "other": other,
+                        "other_steps_per_s": round(other_rate, 2) if other_rate else None},
         "ms_per_step_with_events": round(prof_elapsed / args.steps * 1e3, 4),
         "cpu_baseline": None,
     }
+    if args.counter_run:
+        print(json.dumps(out), flush=True)
+        return
     # AdamW on the 121 non-matrix tensors (with their EMA fused), alone and
     # inside the whole optimizer step
     for _ in range(5):

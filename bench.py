@@ -407,6 +407,66 @@ def cpu_baseline(w, seed, target_s):
             "blas": blas, "single_thread": {"value": 1.0 / el1, "unit": "steps/s", "sample": f"1 step, {el1:.1f} s"}}
 
 
+def library_ns_baseline(w, steps, stream):
+    """The NS iterations of the workload built from vendor BLAS calls, for comparison.
+
+    Per shape group (matrices stacked, short side first) and iteration:
+    Xt = X^T (a copy: torch's bf16 batched products take no transposed view
+    here), A = X Xt (bmm), B = b A + c A A (baddbmm), X' = a X + B X (baddbmm),
+    all bf16 with fp32 accumulation inside the library, no compensation and no
+    symmetry.  The inputs are random bf16 (the values do not change the time).
+    Times every iteration of all matrices on one stream, without prep or apply.
+    """
+    import torch
+    import workloads as wl
+    groups = {}
+    for _, r, c in w.matrices:
+        m, n = min(r, c), max(r, c)
+        groups[(m, n)] = groups.get((m, n), 0) + 1
+    bufs = []
+    g = torch.Generator(device="cuda").manual_seed(0)
+    for (m, n), cnt in sorted(groups.items()):
+        x = (torch.randn(cnt, m, n, device="cuda", generator=g) / (m * n) ** 0.5).to(torch.bfloat16)
+        bufs.append({"x": [x, torch.empty_like(x)], "xt": torch.empty(cnt, n, m, device="cuda", dtype=torch.bfloat16),
+                     "a": torch.empty(cnt, m, m, device="cuda", dtype=torch.bfloat16),
+                     "b": torch.empty(cnt, m, m, device="cuda", dtype=torch.bfloat16)})
+    a_, b_, c_ = wl.STANDARD_TRIPLE
+
+    def ns(with_transpose=True):
+        for it in range(w.ns_steps):
+            for d in bufs:
+                x, x2 = d["x"][it % 2], d["x"][(it + 1) % 2]
+                if with_transpose:
+                    d["xt"].copy_(x.transpose(1, 2))
+                torch.bmm(x, d["xt"], out=d["a"])
+                torch.baddbmm(d["a"], d["a"], d["a"], beta=b_, alpha=c_, out=d["b"])
+                torch.baddbmm(x, d["b"], x, beta=a_, alpha=1.0, out=x2)
+
+    res = {}
+    with torch.cuda.stream(stream):
+        for tag, wt in (("us_per_step", True), ("us_per_step_without_transposes", False)):
+            for _ in range(5):
+                ns(wt)
+            torch.cuda.synchronize()
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            for _ in range(steps):
+                ns(wt)
+            e.record(stream)
+            torch.cuda.synchronize()
+            res[tag] = round(s.elapsed_time(e) / steps * 1e3, 2)
+    flops = sum((4.0 * m * m * n + 2.0 * m ** 3) * cnt for (m, n), cnt in groups.items()) * w.ns_steps
+    res["tflops_dense_formula"] = round(flops / (res["us_per_step_without_transposes"] * 1e-6) / 1e12, 1)
+    try:
+        res["blas"] = str(torch.backends.cuda.preferred_blas_library())
+    except Exception:  # older torch
+        res["blas"] = None
+    res["what"] = ("the workload's NS iterations (all matrices, no prep, no apply) as torch bf16 bmm/baddbmm calls "
+                   "on one stream; plain bf16 products, no compensation, no symmetry")
+    return res
+
+
 def time_other_config(cfg, steps, warmup, seed):
     """Steps/s of one more workload (the parity configs), same method as the main line, no profiling."""
     import torch
@@ -610,7 +670,17 @@ def main():
                 entry["tflops"] = entry["flops_per_step"] / step_s / 1e12
             entry["gbs"] = entry["bytes_per_step"] / step_s / 1e9
         kernels[name] = entry
-    dom = max((k for k in kernels if k in model), key=lambda k: kernels[k]["ms_per_step"])
+    # The dominant kernel is the one with the most time per step in the rocprof
+    # trace of the same sources (launches per step from this run times the
+    # trace's average duration); without a trace, the HIP-event time decides.
+    cands = [k for k in kernels if k in model]
+    traced = {k: rocprof_avg_us(k, w.name) for k in cands}
+    if all(traced[k] for k in cands):
+        dom = max(cands, key=lambda k: kernels[k]["launches_per_step"] * traced[k])
+        dom_from = "rocprof trace (launches per step x average duration)"
+    else:
+        dom = max(cands, key=lambda k: kernels[k]["ms_per_step"])
+        dom_from = "HIP-event time per step"
     d = kernels[dom]
     # The roof of each kernel is fixed by what it computes: the Newton-Schulz
     # products are dense contractions (bf16 MFMA, dense-formula flops), the
@@ -662,7 +732,7 @@ def main():
                                f"(matrices inside the step, {len(w.extras)} other tensors in ema_update)",
                    "matrices": nm, "params": w.n_params, "ns_steps": w.ns_steps, "seed": args.seed,
                    "state_copies": args.rotate},
-        "roofline": {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+        "roofline": {"kernel": dom, "dominant_by": dom_from, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "algorithmic_flops_per_launch": round(d["flops_per_step"] / d["launches_per_step"]),
                      "algorithmic_bytes_per_launch": round(d["bytes_per_launch"]),
@@ -781,6 +851,7 @@ def main():
                        "launches_per_call": sprof[0] / args.steps, "algorithmic_bytes_per_call": sw_bytes,
                        "gbs": round(sw_bytes / (sw_us * 1e-6) / 1e9, 1),
                        "frac_of_hbm_peak": round(sw_bytes / (sw_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    out["library_ns"] = library_ns_baseline(w, args.steps, stream)
     print(f"[bench] adamw {out['adamw']['us_per_call']} us per call; full optimizer step "
           f"{out['full_optimizer_step']['steps_per_s']} steps/s; EMA over all parameters "
           f"{out['ema_full']['us_per_call']} us ({out['ema_full']['gbs']} GB/s)", flush=True)

@@ -27,33 +27,34 @@ __host__ __device__ inline int pad_to_tile(int x) { return (x + kTile - 1) / kTi
 __device__ inline bf16 to_bf16(float x) { return (bf16)x; }
 __device__ inline float from_bf16(bf16 x) { return (float)x; }
 
-// x == hi + lo to ~16 significant bits: hi = rne(x), lo = rne(x - hi).
-__device__ inline void split_bf16(float x, bf16& hi, bf16& lo) {
-    hi = to_bf16(x);
-    lo = to_bf16(x - from_bf16(hi));
+// Two floats -> two bf16 in one word, a in the low half (round to nearest
+// even; one v_cvt_pk_bf16_f32 for the pair), and the two halves back as floats.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
+__device__ inline float bf16_lo_f(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ inline float bf16_hi_f(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
-// Base-precision groups keep the low part of X as one signed byte per element
-// instead of a second bf16: lo = q * 2^(e - 15), e the unbiased exponent of hi
-// and |q| <= 127.  |x - hi| is at most half a bf16 ulp, 2^(e - 8), so q covers
-// it in steps of 2^(e - 15): hi + lo holds x to 2^-16 of its magnitude, as a
-// bf16 pair does, in 3 bytes instead of 4.
-__device__ inline float lo8_step(float hi) {
-    const uint32_t eb = (__builtin_bit_cast(uint32_t, hi) >> 23) & 0xFFu;
-    return eb < 16u ? 0.0f : __builtin_bit_cast(float, (eb - 15u) << 23);
+
+// Base-precision groups keep the low part of X as one byte per element
+// instead of a second bf16.  With hi = m 2^e (m in [0.5, 1), the frexp
+// exponent), |x - hi| is at most half a bf16 ulp, 2^(e - 9), so the byte
+// u = round((x - hi) 2^(16 - e)) + 128, clamped to [0, 255], holds it in
+// steps of 2^(e - 16): hi + lo keeps x to 2^-16 of its magnitude (2^-15 where
+// the code clamps, |x - hi| within a step of half an ulp), as a bf16 pair
+// does, in 3 bytes instead of 4.  Both directions are exact apart from the
+// one rounding to the byte (ldexp scales by a power of two; x - hi is exact).
+// lo8_insert returns word with byte b set to the code of x (v_cvt_pk_u8_f32:
+// round to nearest even, clamp to [0, 255]); lo8_decode reads byte b back.
+__device__ inline uint32_t lo8_insert(float x, float hi, uint32_t word, int b) {
+    const int e = __builtin_amdgcn_frexp_expf(hi);
+    return __builtin_amdgcn_cvt_pk_u8_f32(ldexpf(x - hi, 16 - e) + 128.0f, b, word);
 }
-__device__ inline uint32_t lo8_encode(float x, float hi) {
-    // straight-line code (a select, not a branch, for the tiny binades)
-    const uint32_t eb = (__builtin_bit_cast(uint32_t, hi) >> 23) & 0xFFu;
-    const uint32_t ebc = eb < 16u ? 16u : eb;
-    const float inv = __builtin_bit_cast(float, (269u - ebc) << 23);  // 2^(15 - e)
-    const float q = fminf(fmaxf(rintf((x - hi) * inv), -127.0f), 127.0f);
-    const uint32_t code = (uint32_t)(int32_t)q & 0xFFu;
-    return eb < 16u ? 0u : code;
-}
-__device__ inline float lo8_decode(float hi, uint32_t byte) {
-    const int32_t q = (int32_t)(int8_t)(uint8_t)byte;
-    return fmaf((float)q, lo8_step(hi), hi);
+__device__ inline float lo8_decode(float hi, uint32_t word, int b) {
+    const float u = (float)((word >> (8 * b)) & 0xFFu);
+    return hi + ldexpf(u - 128.0f, __builtin_amdgcn_frexp_expf(hi) - 16);
 }
 
 __device__ inline uint32_t bf16_bits(bf16 x) { return (uint32_t)__builtin_bit_cast(uint16_t, x); }

@@ -35,13 +35,13 @@ __device__ inline float momentum_u(float g, float m, float mu, int nesterov, flo
 }
 
 // X element stores and loads.  bf16: hi plane plus either a bf16 lo plane or,
-// for base-precision groups (lo8), a byte plane (see lo8_encode); fp32: one plane.
+// for base-precision groups (lo8), a byte plane (see lo8_insert); fp32: one plane.
 template <int PREC>
 __device__ inline void store_x(void* xh, void* xl, size_t idx, float v, bool lo8) {
     if (PREC == kNsBf16) {
         const bf16 h = to_bf16(v);
         static_cast<bf16*>(xh)[idx] = h;
-        if (lo8) static_cast<uint8_t*>(xl)[idx] = (uint8_t)lo8_encode(v, from_bf16(h));
+        if (lo8) static_cast<uint8_t*>(xl)[idx] = (uint8_t)lo8_insert(v, from_bf16(h), 0u, 0);
         else static_cast<bf16*>(xl)[idx] = to_bf16(v - from_bf16(h));
     } else {
         static_cast<float*>(xh)[idx] = v;
@@ -52,7 +52,7 @@ template <int PREC>
 __device__ inline float load_x(const void* xh, const void* xl, size_t idx, bool lo8) {
     if (PREC == kNsBf16) {
         const float h = from_bf16(static_cast<const bf16*>(xh)[idx]);
-        if (lo8) return lo8_decode(h, static_cast<const uint8_t*>(xl)[idx]);
+        if (lo8) return lo8_decode(h, static_cast<const uint8_t*>(xl)[idx], 0);
         return h + from_bf16(static_cast<const bf16*>(xl)[idx]);
     } else {
         return static_cast<const float*>(xh)[idx];
@@ -64,25 +64,20 @@ template <int PREC>
 __device__ inline void store_x4(void* xh, void* xl, size_t idx, float4 v, bool lo8) {
     if (PREC == kNsBf16) {
         const float x[4] = {v.x, v.y, v.z, v.w};
-        bf16 h[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) h[e] = to_bf16(x[e]);
         u32x2 ph;
-        ph.x = bf16_bits(h[0]) | (bf16_bits(h[1]) << 16);
-        ph.y = bf16_bits(h[2]) | (bf16_bits(h[3]) << 16);
+        ph.x = pack_bf16x2(x[0], x[1]);
+        ph.y = pack_bf16x2(x[2], x[3]);
+        const float h[4] = {bf16_lo_f(ph.x), bf16_hi_f(ph.x), bf16_lo_f(ph.y), bf16_hi_f(ph.y)};
         *reinterpret_cast<u32x2*>(static_cast<bf16*>(xh) + idx) = ph;
         if (lo8) {
             uint32_t q = 0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) q |= lo8_encode(x[e], from_bf16(h[e])) << (8 * e);
+            for (int e = 0; e < 4; ++e) q = lo8_insert(x[e], h[e], q, e);
             *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(xl) + idx) = q;
         } else {
-            bf16 l[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) l[e] = to_bf16(x[e] - from_bf16(h[e]));
             u32x2 pl;
-            pl.x = bf16_bits(l[0]) | (bf16_bits(l[1]) << 16);
-            pl.y = bf16_bits(l[2]) | (bf16_bits(l[3]) << 16);
+            pl.x = pack_bf16x2(x[0] - h[0], x[1] - h[1]);
+            pl.y = pack_bf16x2(x[2] - h[2], x[3] - h[3]);
             *reinterpret_cast<u32x2*>(static_cast<bf16*>(xl) + idx) = pl;
         }
     } else {
@@ -100,7 +95,7 @@ __device__ inline float4 load_x4(const void* xh, const void* xl, size_t idx, boo
         if (lo8) {
             const uint32_t q = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(xl) + idx);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) r[e] = lo8_decode(hf[e], q >> (8 * e));
+            for (int e = 0; e < 4; ++e) r[e] = lo8_decode(hf[e], q, e);
         } else {
             const u32x2 l = *reinterpret_cast<const u32x2*>(static_cast<const bf16*>(xl) + idx);
             r[0] = hf[0] + from_bf16(bits_bf16(l.x & 0xFFFFu));

@@ -11,7 +11,7 @@
 //
 // bf16 numerics.  X is kept to ~16 significant bits as hi = rne(X) in bf16
 // plus its remainder: one byte per element in units of 2^-15 of hi's binade
-// for the base groups (lo8_encode), a second bf16 plane for the compensated
+// for the base groups (lo8_insert), a second bf16 plane for the compensated
 // ones, whose products use it as an MFMA operand.  MFMA operands are bf16 and
 // accumulate in fp32.  A is split into hi + lo and A A is formed as
 // hi*hi + hi*lo + lo*hi, because the plain bf16 square loses the small

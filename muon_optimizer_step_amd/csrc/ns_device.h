@@ -242,11 +242,8 @@ __device__ inline void store8(void* hi, void* lo, size_t idx, const float* v) {
         u32x4 wh, wl;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            bf16 h0, l0, h1, l1;
-            split_bf16(v[2 * p], h0, l0);
-            split_bf16(v[2 * p + 1], h1, l1);
-            wh[p] = bf16_bits(h0) | (bf16_bits(h1) << 16);
-            wl[p] = bf16_bits(l0) | (bf16_bits(l1) << 16);
+            wh[p] = pack_bf16x2(v[2 * p], v[2 * p + 1]);
+            wl[p] = pack_bf16x2(v[2 * p] - bf16_lo_f(wh[p]), v[2 * p + 1] - bf16_hi_f(wh[p]));
         }
         *reinterpret_cast<u32x4*>(static_cast<bf16*>(hi) + idx) = wh;
         if (lo) *reinterpret_cast<u32x4*>(static_cast<bf16*>(lo) + idx) = wl;
@@ -303,12 +300,12 @@ __device__ inline void store8_hi_f8lo(void* hi, void* lo, void* hi8, size_t idx,
     float r[8], q[8];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const bf16 h0 = to_bf16(v[2 * p]), h1 = to_bf16(v[2 * p + 1]);
-        wh[p] = bf16_bits(h0) | (bf16_bits(h1) << 16);
-        r[2 * p] = (v[2 * p] - from_bf16(h0)) * lo_scale;
-        r[2 * p + 1] = (v[2 * p + 1] - from_bf16(h1)) * lo_scale;
-        q[2 * p] = from_bf16(h0) * hi_scale;
-        q[2 * p + 1] = from_bf16(h1) * hi_scale;
+        wh[p] = pack_bf16x2(v[2 * p], v[2 * p + 1]);
+        const float h0 = bf16_lo_f(wh[p]), h1 = bf16_hi_f(wh[p]);
+        r[2 * p] = (v[2 * p] - h0) * lo_scale;
+        r[2 * p + 1] = (v[2 * p + 1] - h1) * lo_scale;
+        q[2 * p] = h0 * hi_scale;
+        q[2 * p + 1] = h1 * hi_scale;
     }
     u32x2 wl;
     wl[0] = f8_pack4(r[0], r[1], r[2], r[3]);
@@ -321,16 +318,15 @@ __device__ inline void store8_hi_f8lo(void* hi, void* lo, void* hi8, size_t idx,
     *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(hi8) + idx) = w8;
 }
 
-// Store 8 X values as a bf16 hi plane and a byte lo plane (lo8_encode).
+// Store 8 X values as a bf16 hi plane and a byte lo plane (lo8_insert).
 __device__ inline void store8_lo8(void* hi, void* lo, size_t idx, const float* v) {
     u32x4 wh;
     u32x2 wl = {0u, 0u};
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const bf16 h0 = to_bf16(v[2 * p]), h1 = to_bf16(v[2 * p + 1]);
-        wh[p] = bf16_bits(h0) | (bf16_bits(h1) << 16);
-        wl[p / 2] |= (lo8_encode(v[2 * p], from_bf16(h0)) | (lo8_encode(v[2 * p + 1], from_bf16(h1)) << 8))
-                     << (16 * (p % 2));
+        wh[p] = pack_bf16x2(v[2 * p], v[2 * p + 1]);
+        wl[p / 2] = lo8_insert(v[2 * p], bf16_lo_f(wh[p]), wl[p / 2], 2 * (p % 2));
+        wl[p / 2] = lo8_insert(v[2 * p + 1], bf16_hi_f(wh[p]), wl[p / 2], 2 * (p % 2) + 1);
     }
     *reinterpret_cast<u32x4*>(static_cast<bf16*>(hi) + idx) = wh;
     *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(lo) + idx) = wl;
@@ -555,7 +551,7 @@ __device__ inline void update_tile(const NsGroup& G, const Job& job, const Updat
     // accumulators in LDS, then all threads finish 8 consecutive columns of a
     // row each with 16-byte global accesses.
     float* stage = reinterpret_cast<float*>(lds);
-    // Base-precision bf16 updates carry X's low part as bytes (lo8_encode);
+    // Base-precision bf16 updates carry X's low part as bytes (lo8_insert);
     // that plane for both halves is fetched before the accumulators are
     // staged, so one memory latency overlaps the LDS work.
     constexpr bool kLo8 = (PREC == kNsBf16) && !COMP;
@@ -628,7 +624,7 @@ __device__ inline void update_tile(const NsGroup& G, const Job& job, const Updat
             if constexpr (kLo8) {
                 const u32x2 q = xl_pre[h][p];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = lo8_decode(xh[e], q[e / 4] >> (8 * (e % 4)));
+                for (int e = 0; e < 8; ++e) x[e] = lo8_decode(xh[e], q[e / 4], e % 4);
             } else if constexpr (PREC == kNsBf16) {
                 unpack8(keep_l[h][p], xl);
 #pragma unroll

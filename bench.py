@@ -183,14 +183,18 @@ def summarize_trace(stats_csv, out_path=None):
     to out_path (profiles/kernel_trace.json by default) and returned."""
     import csv
     kernels = {}
+    other = {"calls": 0, "total_ns": 0.0}
     for r in csv.DictReader(open(stats_csv)):
         k = _kernel_key(r["Name"])
-        e = kernels.setdefault(k, {"calls": 0, "total_ns": 0.0})
+        # kernels that are not this library's (copies, the vendor-BLAS comparison, torch's own)
+        e = other if k in ("copy", r["Name"]) else kernels.setdefault(k, {"calls": 0, "total_ns": 0.0})
         e["calls"] += int(r["Calls"])
         e["total_ns"] += float(r["TotalDurationNs"])
     out = {"source_hash": source_hash(), "workload": COUNTER_WORKLOAD,
            "kernels": {k: {"calls": v["calls"], "avg_us": round(v["total_ns"] / v["calls"] / 1e3, 3)}
-                       for k, v in sorted(kernels.items()) if k != "copy"}}
+                       for k, v in sorted(kernels.items())},
+           "other_kernels": {"calls": other["calls"], "total_us": round(other["total_ns"] / 1e3, 1),
+                             "what": "copies, the vendor-BLAS comparison leg and torch's own kernels"}}
     path = out_path or os.path.join(ROOT, "profiles", "kernel_trace.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)

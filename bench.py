@@ -617,6 +617,20 @@ def main():
     elapsed = time.perf_counter() - t0
     value = args.steps / elapsed
     print(f"[bench] timed {args.steps} steps in {elapsed * 1e3:.1f} ms", flush=True)
+    # Host cost of enqueueing one step (muon_step + ema_update through the
+    # binding): wall time of each call, the GPU idle at the start of the burst
+    # and the launch queue far from full, so no call waits for the device.
+    host_us = []
+    for _ in range(min(args.steps, 20)):
+        th = time.perf_counter()
+        step()
+        host_us.append((time.perf_counter() - th) * 1e6)
+    torch.cuda.synchronize()
+    built, hits, _ = ms.plan_cache_stats()
+    host_enqueue = {"mean_us": round(float(np.mean(host_us)), 1), "p50_us": round(float(np.median(host_us)), 1),
+                    "max_us": round(float(np.max(host_us)), 1), "calls": len(host_us),
+                    "schedules_built": built, "schedule_cache_hits": hits,
+                    "what": "host wall time per step() call (muon_step + ema_update), GPU work enqueued only"}
 
     # The other Newton-Schulz schedule on the same state, for comparison.
     other = "chain" if args.ns_schedule == "phases" else "phases"
@@ -767,6 +781,7 @@ def main():
         "ns_schedule": {"timed": args.ns_schedule, "other": other,
                         "other_steps_per_s": round(other_rate, 2) if other_rate else None},
         "ms_per_step_with_events": round(prof_elapsed / args.steps * 1e3, 4),
+        "host_enqueue": host_enqueue,
         "cpu_baseline": None,
     }
     if args.counter_run:

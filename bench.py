@@ -367,8 +367,11 @@ def traffic_for(kernel: str, workload: str = COUNTER_WORKLOAD):
     return None if k is None else k.get("bytes_per_launch")
 
 
-def cpu_baseline(w, seed, target_s):
-    """The float64 oracle on the host: full Muon step + EMA of workload w, repeated ~target_s."""
+def cpu_baseline(w, seed, target_s, gpu_o=None):
+    """The float64 oracle on the host: full Muon step + EMA of workload w, repeated ~target_s.
+
+    gpu_o: the library's O for every matrix from one step on the same initial state; the oracle's first
+    step is compared with it (relative Frobenius error per matrix, worst per shape)."""
     import numpy as np
     import oracle.muon as om
     import workloads as wl
@@ -383,19 +386,24 @@ def cpu_baseline(w, seed, target_s):
     nm = len(w.matrices)
 
     def one_step():
-        new_w = []
+        new_w, outs = [], []
         for i in range(nm):
-            wn, _, _ = om.muon_step_matrix(st["params"][i], grads[i], st["moms"][i], lr=f(w.lr), mu=f(w.momentum),
+            wn, _, o = om.muon_step_matrix(st["params"][i], grads[i], st["moms"][i], lr=f(w.lr), mu=f(w.momentum),
                                            nesterov=True, wd=f(w.weight_decay), row_norm=True, coeffs=coeffs)
             new_w.append(wn)
+            outs.append(o)
         post = new_w + st["params"][nm:]
         for e, p in zip(st["ema"], post):
             om.ema_update(e, p, f(w.ema_decay))
+        return outs
 
     reps = 0
+    first = None
     t0 = time.perf_counter()
     while True:
-        one_step()
+        outs = one_step()
+        if first is None:
+            first = outs
         reps += 1
         el = time.perf_counter() - t0
         if el >= target_s or reps >= 20:
@@ -404,11 +412,42 @@ def cpu_baseline(w, seed, target_s):
         t1 = time.perf_counter()
         one_step()
         el1 = time.perf_counter() - t1
-    return {"value": reps / el, "unit": "steps/s", "cores": int(threads), "host_cpus": os.cpu_count(),
-            "kind": "oracle",
-            "sample": f"{reps} full step(s) of the float64 NumPy oracle on the same workload "
-                      f"(66 matrices + EMA over {w.n_params:,} params), {el:.1f} s",
-            "blas": blas, "single_thread": {"value": 1.0 / el1, "unit": "steps/s", "sample": f"1 step, {el1:.1f} s"}}
+    res = {"value": reps / el, "unit": "steps/s", "cores": int(threads), "host_cpus": os.cpu_count(),
+           "kind": "oracle",
+           "sample": f"{reps} full step(s) of the float64 NumPy oracle on the same workload "
+                     f"(66 matrices + EMA over {w.n_params:,} params), {el:.1f} s",
+           "blas": blas, "single_thread": {"value": 1.0 / el1, "unit": "steps/s", "sample": f"1 step, {el1:.1f} s"}}
+    if gpu_o is not None:
+        worst = {}
+        for (name, _, _), o_ref, o_gpu in zip(w.matrices, first, gpu_o):
+            err = float(np.linalg.norm(o_gpu.astype(np.float64) - o_ref) / max(np.linalg.norm(o_ref), 1e-300))
+            shape = name.split(".")[-1]
+            worst[shape] = max(worst.get(shape, 0.0), err)
+        res["parity_vs_library"] = {
+            "ns_rel_frobenius_worst": max(worst.values()), "worst_per_shape": {k: float(f"{v:.3e}") for k, v in
+                                                                               worst.items()},
+            "tolerance": 2e-2, "matrices": nm,
+            "what": "O of the oracle's first step against the library's O from one step on the same initial state"}
+    return res
+
+
+def library_outputs(w, seed):
+    """O of every matrix from one muon_step of this library on a fresh copy of the initial state (float32)."""
+    import torch
+    import muon_optimizer_step_amd as ms
+    import workloads as wl
+    nm = len(w.matrices)
+    st = wl.make_state(w, seed)
+    dev = torch.device("cuda:0")
+    P = [torch.from_numpy(p).to(dev) for p in st["params"][:nm]]
+    G = [torch.from_numpy(g).to(dev) for g in wl.make_grads(w, seed, 0)]
+    M = [torch.from_numpy(m).to(dev) for m in st["moms"]]
+    E = [torch.from_numpy(e).to(dev) for e in st["ema"][:nm]]
+    O = [torch.empty_like(p) for p in P]
+    ms.muon_step(P, G, M, lr=w.lr, momentum=w.momentum, weight_decay=w.weight_decay,
+                 coeffs=wl.coeff_table(w, seed).tolist(), update_outs=O, emas=E, ema_decay=w.ema_decay)
+    torch.cuda.synchronize()
+    return [o.cpu().numpy() for o in O]
 
 
 def library_ns_baseline(w, steps, stream):
@@ -886,7 +925,7 @@ def main():
         out["other_workloads"] = others
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_seconds, library_outputs(w, args.seed))
     print(json.dumps(out), flush=True)
 
 

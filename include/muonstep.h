@@ -26,16 +26,22 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers to contiguous fp32 data on the
  *     current HIP device.  The library never allocates, frees or synchronises
- *     on these calls; all work is enqueued on `stream` (a hipStream_t; NULL is
- *     the null stream) and runs asynchronously.  Faults inside kernels surface
- *     at the caller's next synchronisation.
+ *     on these calls; all work is ordered on `stream` (a hipStream_t; NULL is
+ *     the null stream) and runs asynchronously.  muon_step runs part of its
+ *     work on an internal stream of default priority (one per device, created
+ *     on first use), forked from `stream` with an event recorded there and
+ *     joined back into it with a second event, so what it enqueues still runs
+ *     after the caller's earlier work on `stream` and before the caller's later
+ *     work.  Faults inside kernels surface at the caller's next
+ *     synchronisation.
  *   - Host arrays (the tensor list, the coefficient table, the EMA lists) are
  *     read during the call only; the caller keeps ownership.
  *   - Every argument is validated on the host before anything is enqueued, so a
  *     call that returns an error has no side effect and needs no GPU.
  *   - Return value 0 on success, otherwise one of the MUON_ERR_* codes; the
  *     message of the last error on the calling thread is muon_last_error().
- *   - Results are deterministic: fixed reduction orders, no atomics.
+ *   - Results are deterministic: every sum is taken in a fixed order; the only
+ *     atomics (the persistent chain's tile counters) order work, never values.
  *   - Calls that share a workspace must not overlap in time.
  */
 #ifndef MUONSTEP_H
@@ -108,7 +114,8 @@ size_t muon_workspace_size(const muon_tensor_t* tensors, int32_t n, int32_t ns_p
  *                 (checked on every call).
  *   workspace     device buffer of at least muon_workspace_size(...) bytes,
  *                 256-byte aligned; its contents on entry do not matter.
- *   stream        hipStream_t to enqueue on.
+ *   stream        hipStream_t the step is ordered on (see the conventions
+ *                 above for the internal stream it forks and joins).
  * NaN or Inf inside the tensors is not checked and propagates. */
 int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
               int32_t nesterov, float weight_decay, int32_t row_norm, int32_t ns_steps,
@@ -203,9 +210,11 @@ int adamw_step(const adamw_tensor_t* tensors, int32_t n, float lr, float beta1, 
  *   MUON_NS_SCHEDULE_CHAIN   one persistent launch for every iteration of
  *                            every such matrix, each matrix bound to one XCD,
  *                            tiles taken in dependency order per matrix.
- * Both compute the same products with the same roundings (results within the
- * same tolerances of the float64 reference; not bit-identical, since the
- * Frobenius sum is reduced in another order).  The setting is library-wide
+ * Both compute the same products on the same operand types and store the
+ * same planes; the chain's Gram and square tiles run 4 waves instead of two
+ * K groups of 4 and its Frobenius sum uses 256 threads instead of 512, so the
+ * fp32 sums are taken in another order: results agree within the same
+ * tolerances of the float64 reference, not bit for bit.  The setting is library-wide
  * and part of the schedule signature below.  Returns the previous setting,
  * or MUON_ERR_INVALID_ARG for an unknown value.  The environment variable
  * MUON_CHAIN=1 selects the chain when the library loads.  Needs no GPU. */

@@ -122,6 +122,31 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
               const float* ns_coeffs, int32_t ns_precision, float ema_decay, void* workspace,
               size_t workspace_bytes, void* stream);
 
+/* muon_step together with the weight EMA of n_extra more tensors -- the
+ * parameters that are not Muon matrices (embeddings, gains) -- in one call:
+ * "Record: Improved Parallel Residuals + Systems Optimization" (PR #1584),
+ * "Summary": the fused Muon step and one batched EMA over all parameters;
+ * "Record: L_ParallelResiduals_UNetSkips_DepthRecur_Muon_ 1.0901" (PR #1893),
+ * "Architecture and training stack", EMA row.  The results are those of
+ * muon_step(...) followed by ema_update(extra_ema, extra_params, extra_numel,
+ * n_extra, ema_decay, stream): the extra tensors' EMA uses the call's
+ * ema_decay and the extra parameters as they are (the Muon step does not touch
+ * them).  Because the extra buffers are disjoint from the matrices', their EMA
+ * is enqueued on the internal stream with the least Newton-Schulz work, where
+ * it runs beside the last phases of the others instead of after them.
+ *   extra_ema, extra_params, extra_numel  host arrays of n_extra entries, as
+ *                 in ema_update; extra_ema[i] is updated in place.
+ *   n_extra       0 <= n_extra <= MUON_MAX_TENSORS (0: exactly muon_step).
+ * Every other argument as in muon_step.  No buffer of the extra list may
+ * overlap another, any buffer of the matrices, or the workspace
+ * (MUON_ERR_UNSUPPORTED); everything is validated before anything is
+ * enqueued. */
+int muon_step_ema(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
+                  int32_t nesterov, float weight_decay, int32_t row_norm, int32_t ns_steps,
+                  const float* ns_coeffs, int32_t ns_precision, float ema_decay,
+                  float* const* extra_ema, const float* const* extra_params, const int64_t* extra_numel,
+                  int32_t n_extra, void* workspace, size_t workspace_bytes, void* stream);
+
 /* muon_step for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
  * arguments, results and errors as muon_step, without the workspace: the

@@ -84,6 +84,12 @@ def load() -> ctypes.CDLL:
                   ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_float), ctypes.c_int32,
                   ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     f.restype = ctypes.c_int
+    f = lib.muon_step_ema
+    f.argtypes = [ctypes.POINTER(MuonTensor), ctypes.c_int32, ctypes.c_float, ctypes.c_float, ctypes.c_int32,
+                  ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_float), ctypes.c_int32,
+                  ctypes.c_float, ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
+                  ctypes.POINTER(ctypes.c_int64), ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    f.restype = ctypes.c_int
     f = lib.muon_step_static
     f.argtypes = [ctypes.POINTER(MuonTensor), ctypes.c_int32, ctypes.c_float, ctypes.c_float, ctypes.c_int32,
                   ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_float), ctypes.c_int32,

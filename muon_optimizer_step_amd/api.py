@@ -94,13 +94,16 @@ def _workspace_for(nbytes: int, device, stream):
 def muon_step(params, grads, moms, *, lr: float, momentum: float, weight_decay: float,
               coeffs, nesterov: bool = True, row_norm: bool = True,
               ns_precision: int = _lib.MUON_NS_BF16, update_outs=None, emas=None, ema_decay: float = 0.0,
-              workspace=None, stream=None) -> None:
+              extra_emas=None, extra_params=None, workspace=None, stream=None) -> None:
     """One Muon step over lists of 2-D fp32 tensors (params and moms updated in place).
 
     coeffs: ns_steps rows of (a, b, c); update_outs: optional list of tensors
     (or None entries) that receive the orthogonalised update O; emas: optional
     list of tensors (or None entries) advanced as ema = d*ema + (1-d)*W' with
-    d = ema_decay, in the pass that writes W'.
+    d = ema_decay, in the pass that writes W'.  extra_emas / extra_params:
+    optional lists of other fp32 tensors (any shape) whose EMA is advanced with
+    the same d in the same call (muon_step_ema), as ema_update after the step
+    would.
     """
     lib = _lib.load()
     n = len(params)
@@ -117,10 +120,17 @@ def muon_step(params, grads, moms, *, lr: float, momentum: float, weight_decay: 
         if need == 0:
             raise _lib.MuonError(_lib.MUON_ERR_INVALID_ARG, lib.muon_last_error().decode())
         workspace = _workspace_for(int(need), device, stream)
-    rc = lib.muon_step(table, n, float(lr), float(momentum), int(bool(nesterov)), float(weight_decay),
-                       int(bool(row_norm)), steps, carr if steps else None, int(ns_precision), float(ema_decay),
-                       ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
-                       _stream_handle(stream, device))
+    if extra_emas is not None or extra_params is not None:
+        xe, xp, xn, nx = _ema_list(extra_emas or [], extra_params or [], "extra_emas")
+        rc = lib.muon_step_ema(table, n, float(lr), float(momentum), int(bool(nesterov)), float(weight_decay),
+                               int(bool(row_norm)), steps, carr if steps else None, int(ns_precision),
+                               float(ema_decay), xe, xp, xn, nx, ctypes.c_void_p(workspace.data_ptr()),
+                               workspace.numel() * workspace.element_size(), _stream_handle(stream, device))
+    else:
+        rc = lib.muon_step(table, n, float(lr), float(momentum), int(bool(nesterov)), float(weight_decay),
+                           int(bool(row_norm)), steps, carr if steps else None, int(ns_precision), float(ema_decay),
+                           ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+                           _stream_handle(stream, device))
     _lib.check(rc)
 
 
@@ -145,23 +155,29 @@ def muon_step_static(params, grads, moms, *, lr: float, momentum: float, weight_
     _lib.check(rc)
 
 
-def ema_update(emas, params, decay: float, stream=None) -> None:
-    """emas[i] = decay * emas[i] + (1 - decay) * params[i] for fp32 tensors of any shape."""
-    lib = _lib.load()
+def _ema_list(emas, params, what: str = "emas"):
+    """Checked pointer arrays (ema, params, numel) and the count of an EMA list."""
     n = len(emas)
     if len(params) != n:
-        raise ValueError("emas and params must have the same length")
+        raise ValueError(f"{what} and its params must have the same length")
     e_ptrs = (ctypes.c_void_p * max(1, n))()
     p_ptrs = (ctypes.c_void_p * max(1, n))()
     numel = (ctypes.c_int64 * max(1, n))()
     for i, (e, p) in enumerate(zip(emas, params)):
-        _check_tensor(e, f"emas[{i}]")
-        _check_tensor(p, f"params[{i}]")
+        _check_tensor(e, f"{what}[{i}]")
+        _check_tensor(p, f"params of {what}[{i}]")
         if e.numel() != p.numel():
-            raise ValueError(f"tensor {i}: {e.numel()} != {p.numel()} elements")
+            raise ValueError(f"{what}[{i}]: {e.numel()} != {p.numel()} elements")
         e_ptrs[i] = e.data_ptr()
         p_ptrs[i] = p.data_ptr()
         numel[i] = e.numel()
+    return e_ptrs, p_ptrs, numel, n
+
+
+def ema_update(emas, params, decay: float, stream=None) -> None:
+    """emas[i] = decay * emas[i] + (1 - decay) * params[i] for fp32 tensors of any shape."""
+    lib = _lib.load()
+    e_ptrs, p_ptrs, numel, n = _ema_list(emas, params)
     device = emas[0].device if n else None
     rc = lib.ema_update(e_ptrs, p_ptrs, numel, n, float(decay), _stream_handle(stream, device))
     _lib.check(rc)
@@ -275,10 +291,14 @@ class PreparedMuonStep:
     """
 
     def __init__(self, params, grads, moms, *, ns_precision: int = _lib.MUON_NS_BF16, update_outs=None,
-                 emas=None, workspace=None, stream=None):
+                 emas=None, extra_emas=None, extra_params=None, workspace=None, stream=None):
         if len(grads) != len(params) or len(moms) != len(params):
             raise ValueError("params, grads and moms must have the same length")
-        self._keep = (list(params), list(grads), list(moms), update_outs, emas, workspace)
+        self._keep = (list(params), list(grads), list(moms), update_outs, emas, workspace, extra_emas, extra_params)
+        # the other tensors' EMA, run in the same call (muon_step_ema)
+        self._extra = None
+        if extra_emas is not None or extra_params is not None:
+            self._extra = _ema_list(extra_emas or [], extra_params or [], "extra_emas")
         entries = _entries(params, grads, moms, update_outs, emas)
         self.n = len(entries)
         self.table = _lib.tensor_table(entries)
@@ -306,10 +326,18 @@ class PreparedMuonStep:
             key = [tuple(float(v) for v in row) for row in coeffs]
             self._coeffs = (coeffs, _lib.coeff_array(key))
         carr, steps = self._coeffs[1]
-        rc = _lib.load().muon_step(self.table, self.n, float(lr), float(momentum), int(bool(nesterov)),
+        lib = _lib.load()
+        if self._extra is not None:
+            xe, xp, xn, nx = self._extra
+            rc = lib.muon_step_ema(self.table, self.n, float(lr), float(momentum), int(bool(nesterov)),
                                    float(weight_decay), int(bool(row_norm)), steps, carr if steps else None,
-                                   self.ns_precision, float(ema_decay), self._ws_ptr, self._ws_bytes,
-                                   _stream_handle(stream, self.device))
+                                   self.ns_precision, float(ema_decay), xe, xp, xn, nx, self._ws_ptr,
+                                   self._ws_bytes, _stream_handle(stream, self.device))
+        else:
+            rc = lib.muon_step(self.table, self.n, float(lr), float(momentum), int(bool(nesterov)),
+                               float(weight_decay), int(bool(row_norm)), steps, carr if steps else None,
+                               self.ns_precision, float(ema_decay), self._ws_ptr, self._ws_bytes,
+                               _stream_handle(stream, self.device))
         _lib.check(rc)
 
 

@@ -678,6 +678,74 @@ int static_scratch(void*& out) {
     return MUON_OK;
 }
 
+// ------------------------------------------------------------- EMA lists
+// Arguments of an EMA list (ema_update, muon_step_ema): non-NULL arrays,
+// 1 <= n <= MUON_MAX_TENSORS, element counts in [0, kMaxStreamElems], 4-byte
+// aligned non-NULL buffers for every non-empty tensor.  The byte spans of the
+// buffers are appended to `spans` (tensor ids 0 .. n-1) for the caller's
+// overlap check.
+int validate_ema_list(float* const* ema, const float* const* params, const int64_t* numel, int32_t n,
+                      std::vector<Span>& spans) {
+    if (!ema || !params || !numel) return fail(MUON_ERR_INVALID_ARG, "ema, params and numel must be non-NULL");
+    if (n <= 0 || n > MUON_MAX_TENSORS) return fail(MUON_ERR_INVALID_ARG, "n = %d outside [1, %d]", n, MUON_MAX_TENSORS);
+    for (int i = 0; i < n; ++i) {
+        if (numel[i] < 0) return fail(MUON_ERR_INVALID_ARG, "numel[%d] = %lld is negative", i, (long long)numel[i]);
+        if (numel[i] > kMaxStreamElems)
+            return fail(MUON_ERR_UNSUPPORTED, "numel[%d] = %lld beyond %lld", i, (long long)numel[i],
+                        (long long)kMaxStreamElems);
+        if (numel[i] == 0) continue;
+        if (!ema[i] || !params[i]) return fail(MUON_ERR_INVALID_ARG, "tensor %d: NULL pointer", i);
+        if (reinterpret_cast<uintptr_t>(ema[i]) % 4 || reinterpret_cast<uintptr_t>(params[i]) % 4)
+            return fail(MUON_ERR_INVALID_ARG, "tensor %d: pointer not 4-byte aligned", i);
+        const uintptr_t e = reinterpret_cast<uintptr_t>(ema[i]);
+        const uintptr_t q = reinterpret_cast<uintptr_t>(params[i]);
+        const size_t bytes = (size_t)numel[i] * sizeof(float);
+        spans.push_back({e, e + bytes, i});
+        spans.push_back({q, q + bytes, i});
+    }
+    return MUON_OK;
+}
+
+// The EMA kernels over a validated list: table entries of at most
+// kEmaEntryElems elements, kEmaChunk per launch.
+int enqueue_ema_list(float* const* ema, const float* const* params, const int64_t* numel, int32_t n, float decay,
+                     hipStream_t s) {
+    int i = 0;
+    int64_t off = 0;
+    while (i < n) {
+        EmaArgs a;
+        memset(&a, 0, sizeof(a));
+        a.decay = decay;
+        a.one_minus_decay = 1.0f - decay;
+        int64_t blocks = 0;
+        while (i < n && a.n < kEmaChunk) {
+            if (off >= numel[i]) { ++i; off = 0; continue; }
+            const int64_t len = std::min(numel[i] - off, kEmaEntryElems);
+            const int64_t nb = (len + kEmaElemsPerBlock - 1) / kEmaElemsPerBlock;
+            if (blocks + nb > (int64_t)1 << 30) break;
+            EmaTensor& T = a.t[a.n++];
+            T.ema = ema[i] + off;
+            T.param = params[i] + off;
+            T.numel = (int)len;
+            T.block_begin = (int)blocks;
+            blocks += nb;
+            off += len;
+        }
+        if (a.n == 0) continue;
+        hipError_t err = timed_launch("ema", s, [&] { return launch_ema(a, (int)blocks, s); });
+        if (err != hipSuccess) return fail(MUON_ERR_HIP, "ema launch failed: %s", hipGetErrorString(err));
+    }
+    return MUON_OK;
+}
+
+// The other parameters' weight EMA that muon_step_ema runs with the step.
+struct EmaList {
+    float* const* ema;
+    const float* const* params;
+    const int64_t* numel;
+    int32_t n;
+};
+
 }  // namespace
 }  // namespace muon
 
@@ -696,9 +764,13 @@ size_t muon_workspace_size(const muon_tensor_t* tensors, int32_t n, int32_t ns_p
     return p.bytes;
 }
 
-int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum, int32_t nesterov,
-              float weight_decay, int32_t row_norm, int32_t ns_steps, const float* ns_coeffs,
-              int32_t ns_precision, float ema_decay, void* workspace, size_t workspace_bytes, void* stream) {
+// muon_step, and with `extra` the weight EMA of further tensors enqueued on the
+// lightest lane once its matrices are done (muon_step_ema).  Every argument has
+// been or is validated before anything is enqueued.
+static int muon_step_impl(const muon_tensor_t* tensors, int32_t n, float lr, float momentum, int32_t nesterov,
+                          float weight_decay, int32_t row_norm, int32_t ns_steps, const float* ns_coeffs,
+                          int32_t ns_precision, float ema_decay, const EmaList* extra, void* workspace,
+                          size_t workspace_bytes, void* stream) {
     int rc = validate_tensors(tensors, n, ns_precision);
     if (rc) return rc;
     if (!std::isfinite(lr) || !std::isfinite(momentum) || !std::isfinite(weight_decay))
@@ -1018,6 +1090,12 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
         for (int lane = 0; lane < nlanes; ++lane)
             if ((rc = enqueue_apply(lane))) return rc;
     if (use_chain && (rc = enqueue_chain())) return rc;
+    // the other parameters' EMA: its tensors are disjoint from the matrices,
+    // so it runs on the lane with the least NS work, beside the others' last
+    // phases, instead of after the join
+    if (extra && (rc = enqueue_ema_list(extra->ema, extra->params, extra->numel, extra->n, ema_decay,
+                                        lane_stream[nlanes - 1])))
+        return rc;
 
     if (L) {
         for (int l = 1; l < nlanes && err == hipSuccess; ++l) {
@@ -1027,6 +1105,47 @@ int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum,
         if (err != hipSuccess) return fail(MUON_ERR_HIP, "lane join failed: %s", hipGetErrorString(err));
     }
     return MUON_OK;
+}
+
+int muon_step(const muon_tensor_t* tensors, int32_t n, float lr, float momentum, int32_t nesterov,
+              float weight_decay, int32_t row_norm, int32_t ns_steps, const float* ns_coeffs,
+              int32_t ns_precision, float ema_decay, void* workspace, size_t workspace_bytes, void* stream) {
+    return muon_step_impl(tensors, n, lr, momentum, nesterov, weight_decay, row_norm, ns_steps, ns_coeffs,
+                          ns_precision, ema_decay, nullptr, workspace, workspace_bytes, stream);
+}
+
+int muon_step_ema(const muon_tensor_t* tensors, int32_t n, float lr, float momentum, int32_t nesterov,
+                  float weight_decay, int32_t row_norm, int32_t ns_steps, const float* ns_coeffs,
+                  int32_t ns_precision, float ema_decay, float* const* extra_ema, const float* const* extra_params,
+                  const int64_t* extra_numel, int32_t n_extra, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+    int rc = validate_tensors(tensors, n, ns_precision);
+    if (rc) return rc;
+    if (n_extra == 0)
+        return muon_step_impl(tensors, n, lr, momentum, nesterov, weight_decay, row_norm, ns_steps, ns_coeffs,
+                              ns_precision, ema_decay, nullptr, workspace, workspace_bytes, stream);
+    // the extra list, and no overlap between its buffers, the matrices' buffers
+    // and the workspace (ids: extra tensors 0 .. n_extra-1, then the matrices)
+    std::vector<Span> spans;
+    if ((rc = validate_ema_list(extra_ema, extra_params, extra_numel, n_extra, spans))) return rc;
+    for (int i = 0; i < n; ++i) {
+        const muon_tensor_t& x = tensors[i];
+        const size_t bytes = (size_t)x.rows * x.cols * sizeof(float);
+        const void* ptrs[5] = {x.param, x.grad, x.momentum, x.update_out, x.ema};
+        for (int k = 0; k < 5; ++k) {
+            if (!ptrs[k]) continue;
+            const uintptr_t lo = reinterpret_cast<uintptr_t>(ptrs[k]);
+            spans.push_back({lo, lo + bytes, n_extra + i});
+        }
+    }
+    if (workspace && workspace_bytes) {
+        const uintptr_t w = reinterpret_cast<uintptr_t>(workspace);
+        spans.push_back({w, w + workspace_bytes, n_extra + n});
+    }
+    if ((rc = check_overlaps(spans, "muon_step_ema"))) return rc;
+    const EmaList extra{extra_ema, extra_params, extra_numel, n_extra};
+    return muon_step_impl(tensors, n, lr, momentum, nesterov, weight_decay, row_norm, ns_steps, ns_coeffs,
+                          ns_precision, ema_decay, &extra, workspace, workspace_bytes, stream);
 }
 
 int muon_step_static(const muon_tensor_t* tensors, int32_t n, float lr, float momentum, int32_t nesterov,
@@ -1062,57 +1181,14 @@ int muon_plan_cache_stats(int64_t* built, int64_t* hits) {
 
 int ema_update(float* const* ema, const float* const* params, const int64_t* numel, int32_t n, float decay,
                void* stream) {
-    if (!ema || !params || !numel) return fail(MUON_ERR_INVALID_ARG, "ema, params and numel must be non-NULL");
-    if (n <= 0 || n > MUON_MAX_TENSORS) return fail(MUON_ERR_INVALID_ARG, "n = %d outside [1, %d]", n, MUON_MAX_TENSORS);
     if (!std::isfinite(decay) || decay < 0.f || decay > 1.f)
         return fail(MUON_ERR_INVALID_ARG, "decay must be finite and in [0, 1]");
     std::vector<Span> spans;
-    for (int i = 0; i < n; ++i) {
-        if (numel[i] < 0) return fail(MUON_ERR_INVALID_ARG, "numel[%d] = %lld is negative", i, (long long)numel[i]);
-        if (numel[i] > kMaxStreamElems)
-            return fail(MUON_ERR_UNSUPPORTED, "numel[%d] = %lld beyond %lld", i, (long long)numel[i],
-                        (long long)kMaxStreamElems);
-        if (numel[i] == 0) continue;
-        if (!ema[i] || !params[i]) return fail(MUON_ERR_INVALID_ARG, "tensor %d: NULL pointer", i);
-        if (reinterpret_cast<uintptr_t>(ema[i]) % 4 || reinterpret_cast<uintptr_t>(params[i]) % 4)
-            return fail(MUON_ERR_INVALID_ARG, "tensor %d: pointer not 4-byte aligned", i);
-        const uintptr_t e = reinterpret_cast<uintptr_t>(ema[i]);
-        const uintptr_t q = reinterpret_cast<uintptr_t>(params[i]);
-        const size_t bytes = (size_t)numel[i] * sizeof(float);
-        spans.push_back({e, e + bytes, i});
-        spans.push_back({q, q + bytes, i});
-    }
-    // no two buffers of the call may overlap
-    int rc = check_overlaps(spans, "ema_update");
+    int rc = validate_ema_list(ema, params, numel, n, spans);
     if (rc) return rc;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    // table entries of at most kEmaEntryElems elements, kEmaChunk per launch
-    int i = 0;
-    int64_t off = 0;
-    while (i < n) {
-        EmaArgs a;
-        memset(&a, 0, sizeof(a));
-        a.decay = decay;
-        a.one_minus_decay = 1.0f - decay;
-        int64_t blocks = 0;
-        while (i < n && a.n < kEmaChunk) {
-            if (off >= numel[i]) { ++i; off = 0; continue; }
-            const int64_t len = std::min(numel[i] - off, kEmaEntryElems);
-            const int64_t nb = (len + kEmaElemsPerBlock - 1) / kEmaElemsPerBlock;
-            if (blocks + nb > (int64_t)1 << 30) break;
-            EmaTensor& T = a.t[a.n++];
-            T.ema = ema[i] + off;
-            T.param = params[i] + off;
-            T.numel = (int)len;
-            T.block_begin = (int)blocks;
-            blocks += nb;
-            off += len;
-        }
-        if (a.n == 0) continue;
-        hipError_t err = timed_launch("ema", s, [&] { return launch_ema(a, (int)blocks, s); });
-        if (err != hipSuccess) return fail(MUON_ERR_HIP, "ema launch failed: %s", hipGetErrorString(err));
-    }
-    return MUON_OK;
+    // no two buffers of the call may overlap
+    if ((rc = check_overlaps(spans, "ema_update"))) return rc;
+    return enqueue_ema_list(ema, params, numel, n, decay, static_cast<hipStream_t>(stream));
 }
 
 int ema_swap(float* const* ema, float* const* params, const int64_t* numel, int32_t n, void* stream) {

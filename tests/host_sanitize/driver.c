@@ -160,6 +160,19 @@ static void check_streaming_entry_points(void) {
     EXPECT(adamw_step(a, 2, 1e-3f, 1.5f, 0.999f, 1e-8f, 0.01f, 10, 0.0f, NULL) == MUON_ERR_INVALID_ARG);
     a[1].grad = a[0].param;
     EXPECT(adamw_step(a, 2, 1e-3f, 0.9f, 0.999f, 1e-8f, 0.01f, 10, 0.0f, NULL) == MUON_ERR_UNSUPPORTED);
+    /* the step with the other tensors' EMA: a valid call plans and fails at its first HIP call; an extra
+     * buffer inside a matrix's is refused before anything */
+    muon_tensor_t m2[2] = {tensor(800, 512, 512), tensor(801, 256, 512)};
+    const size_t ws2 = muon_workspace_size(m2, 2, MUON_NS_BF16);
+    void* wsp2 = (void*)(kBase - ((uintptr_t)1 << 42));
+    int rc = muon_step_ema(m2, 2, 0.02f, 0.95f, 1, 0.1f, 1, 5, coeffs, MUON_NS_BF16, 0.99f, e, p, ne, 3, wsp2, ws2,
+                           NULL);
+    EXPECT(rc == MUON_ERR_HIP || rc == MUON_OK);
+    float* e_bad[3] = {e[0], (float*)m2[1].grad + 8, e[2]};
+    EXPECT(muon_step_ema(m2, 2, 0.02f, 0.95f, 1, 0.1f, 1, 5, coeffs, MUON_NS_BF16, 0.99f, e_bad, p, ne, 3, wsp2,
+                         ws2, NULL) == MUON_ERR_UNSUPPORTED);
+    EXPECT(muon_step_ema(m2, 2, 0.02f, 0.95f, 1, 0.1f, 1, 5, coeffs, MUON_NS_BF16, 0.99f, e, p, ne, -2, wsp2, ws2,
+                         NULL) == MUON_ERR_INVALID_ARG);
     EXPECT(muon_profile_enable(0) == 0);
     EXPECT(muon_profile_read(NULL, NULL, NULL, 0, 1) == 0);
 }

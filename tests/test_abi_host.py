@@ -31,7 +31,7 @@ def test_header_declares_the_abi():
     names = _declared_functions()
     assert names == sorted(["muon_workspace_size", "muon_step", "ema_update", "ema_swap", "adamw_step",
                             "muon_last_error", "muon_version", "muon_profile_enable", "muon_profile_read",
-                            "muon_plan_cache_stats", "muon_set_ns_schedule", "muon_step_static"])
+                            "muon_plan_cache_stats", "muon_set_ns_schedule", "muon_step_static", "muon_step_ema"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -336,3 +336,68 @@ def test_static_entry_rejects_what_the_static_workspace_cannot_hold():
     assert rc == _lib.MUON_ERR_WORKSPACE
     assert "static workspace" in lib.muon_last_error().decode()
     assert lib.muon_step_static(table, 0, 0.02, 0.95, 1, 0.1, 1, k, carr, 0, 0.99, None) == _lib.MUON_ERR_INVALID_ARG
+
+
+def _call_ema(entries, extra, ws=BASE + (1 << 45), ws_bytes=1 << 40, n_extra=None, decay=0.9965, arrays=True):
+    """muon_step_ema with the standard table; extra: list of (ema, param, numel) fake pointers."""
+    lib = _lib.load()
+    table = _lib.tensor_table(entries)
+    carr, k = _lib.coeff_array([(3.4445, -4.775, 2.0315)] * 5)
+    m = len(extra)
+    e = (ctypes.c_void_p * max(1, m))(*[x[0] for x in extra])
+    p = (ctypes.c_void_p * max(1, m))(*[x[1] for x in extra])
+    ne = (ctypes.c_int64 * max(1, m))(*[x[2] for x in extra])
+    if not arrays:
+        e = p = ne = None
+    rc = lib.muon_step_ema(table, len(entries), 0.02, 0.95, 1, 0.1, 1, k, carr, 0, decay, e, p, ne,
+                           m if n_extra is None else n_extra, ctypes.c_void_p(ws), ws_bytes, None)
+    return rc, lib.muon_last_error().decode()
+
+
+EXTRA = BASE + (1 << 44)   # the other tensors' buffers, far from the matrices'
+
+
+def _x(i, numel):
+    return (EXTRA + 2 * i * (1 << 30), EXTRA + (2 * i + 1) * (1 << 30), numel)
+
+
+def test_muon_step_ema_validates_the_extra_list_before_anything():
+    mats = [_t(0, 64, 32, ema=True), _t(1, 16, 48)]
+    good = [_x(0, 4096), _x(1, 17)]
+    # a valid call reaches the GPU (or, without one, fails at its first HIP call): nothing here is rejected
+    rc, err = _call_ema(mats, good)
+    assert rc in (_lib.MUON_OK, _lib.MUON_ERR_HIP), err
+    assert _call_ema(mats, good, n_extra=-1)[0] == _lib.MUON_ERR_INVALID_ARG
+    assert _call_ema(mats, good, n_extra=_lib.MUON_MAX_TENSORS + 1)[0] == _lib.MUON_ERR_INVALID_ARG
+    assert _call_ema(mats, good, arrays=False)[0] == _lib.MUON_ERR_INVALID_ARG
+    assert _call_ema(mats, [_x(0, -1)])[0] == _lib.MUON_ERR_INVALID_ARG
+    assert _call_ema(mats, [_x(0, 1 << 41)])[0] == _lib.MUON_ERR_UNSUPPORTED
+    assert _call_ema(mats, [(0, EXTRA, 10)])[0] == _lib.MUON_ERR_INVALID_ARG          # NULL ema
+    assert _call_ema(mats, [(EXTRA + 2, EXTRA + (1 << 30), 10)])[0] == _lib.MUON_ERR_INVALID_ARG   # misaligned
+    rc, err = _call_ema(mats, [(EXTRA, EXTRA + 64, 1000)])                 # an ema overlapping its param
+    assert rc == _lib.MUON_ERR_UNSUPPORTED and "overlap" in err
+    rc, err = _call_ema(mats, [_x(0, 100), (_x(1, 100)[0], _x(0, 100)[1] + 16, 100)])   # two extras share a buffer
+    assert rc == _lib.MUON_ERR_UNSUPPORTED and "overlap" in err
+    p0, g0, m0, _, e0, r0, c0 = mats[0]
+    for buf in (p0, g0, m0, e0):                                            # an extra buffer inside a matrix's
+        rc, err = _call_ema(mats, [(EXTRA, buf + 128, 10)])
+        assert rc == _lib.MUON_ERR_UNSUPPORTED and "muon_step_ema" in err, (buf, err)
+    ws = BASE + (1 << 45)
+    rc, err = _call_ema(mats, [(EXTRA, ws + 4096, 10)], ws=ws)              # inside the workspace
+    assert rc == _lib.MUON_ERR_UNSUPPORTED and "overlap" in err
+    assert _call_ema(mats, good, decay=1.5)[0] == _lib.MUON_ERR_INVALID_ARG
+    # n_extra == 0 is muon_step itself, the arrays may be NULL
+    rc0, _ = _call_ema(mats, [], arrays=False)
+    rc1, _ = _call(mats)
+    assert rc0 == rc1
+
+
+def test_muon_step_ema_plans_like_muon_step():
+    """The extra list is not part of the schedule signature: the same matrices reuse the schedule."""
+    mats = [_t(60, 512, 512), _t(61, 256, 512)]
+    _call(mats)
+    built0, hits0, _ = _lib.plan_cache_stats()
+    rc, err = _call_ema(mats, [_x(5, 1 << 20)])
+    assert rc in (_lib.MUON_OK, _lib.MUON_ERR_HIP), err
+    built1, hits1, _ = _lib.plan_cache_stats()
+    assert (built1, hits1) == (built0, hits0 + 1)

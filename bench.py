@@ -562,7 +562,7 @@ def time_other_config(cfg, steps, warmup, seed):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: this benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU sharding is a design note, not a measured path", file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:

@@ -8,7 +8,7 @@ Source: "Record: L_ParallelResiduals_UNetSkips_DepthRecur_Muon_ 1.0901"
 (PR #1893), table "Architecture and training stack", row Optimizer: Muon runs
 on the matrix parameters and AdamW on the embeddings and scalars.  The page
 names the optimizer only; it gives neither its equations nor its
-hyperparameters.  Reading taken (R13, repeated in the design doc): AdamW as
+hyperparameters.  Reading taken (R13): AdamW as
 Loshchilov and Hutter define it, with decoupled weight decay applied to the
 pre-update parameter, bias-corrected moments at step t (t counts from 1) and
 eps added to the square root of the corrected second moment:

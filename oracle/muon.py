@@ -24,8 +24,7 @@ Sources (the pages are cited by title and section):
   code only, so the optimizer's arithmetic is the plain one written here.
 
 The pages name the method but do not print its equations.  This oracle takes
-the plainest reading of "Muon" (the readings are listed below and repeated in
-DESIGN.md):
+the plainest reading of "Muon" (the readings are listed below):
 
   R1 momentum (Nesterov, SGD form):   M' = mu*M + G;   U = G + mu*M'
      (without Nesterov: U = M').

@@ -1,11 +1,11 @@
 """The library's host code under AddressSanitizer and UndefinedBehaviorSanitizer.
 
 A copy of the library is built with the sanitizers on its host code only
-(device code as usual) and driven by tests/host_sanitize/driver.c without a
+(device code as usual) and driven by tests/host_sanitize/exercise_abi.c without a
 GPU: argument validation and overlap checks, workspace sizing, the shape-group
 plan, launch tables and schedule cache of valid calls (which then fail at their
 first HIP call), cache eviction, and the streaming entry points' checks.  Any
-sanitizer report ends the driver with a non-zero status.
+sanitizer report ends the test program with a non-zero status.
 """
 
 import os
@@ -22,7 +22,7 @@ CLANG = "/opt/rocm/llvm/bin/clang"
 
 @pytest.mark.skipif(not (os.path.exists(HIPCC) and os.path.exists(CLANG)), reason="ROCm compilers not installed")
 @pytest.mark.skipif(os.path.exists("/dev/kfd"),
-                    reason="the driver's valid calls carry fake device pointers: run only where no GPU is present")
+                    reason="the test program's valid calls carry fake device pointers: run only where no GPU is present")
 def test_host_code_is_clean_under_asan_and_ubsan(tmp_path):
     lib = tmp_path / "libmuonstep_san.so"
     sources = [os.path.join(CSRC, f) for f in ("api.hip", "elementwise.hip", "ns.hip", "chain.hip")]
@@ -33,10 +33,10 @@ def test_host_code_is_clean_under_asan_and_ubsan(tmp_path):
              "-I", os.path.join(ROOT, "include")] + sources + ["-o", str(lib)]
     r = subprocess.run(build, capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stderr[-3000:]
-    exe = tmp_path / "driver"
+    exe = tmp_path / "exercise_abi"
     link = [CLANG, "-std=c11", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
             "-fno-omit-frame-pointer", "-I", os.path.join(ROOT, "include"),
-            os.path.join(ROOT, "tests", "host_sanitize", "driver.c"),
+            os.path.join(ROOT, "tests", "host_sanitize", "exercise_abi.c"),
             f"-L{tmp_path}", "-lmuonstep_san", f"-Wl,-rpath,{tmp_path}", "-o", str(exe)]
     r = subprocess.run(link, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr[-3000:]

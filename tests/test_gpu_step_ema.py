@@ -99,3 +99,26 @@ def test_prepared_step_with_extra_ema_and_empty_list():
     torch.cuda.synchronize()
     for x, y in zip(c["P"] + c["E"], d["P"] + d["E"]):
         assert _bits_equal(gu.host(x), gu.host(y))
+
+
+def test_prepared_ema_equals_ema_update():
+    import torch
+    import muon_optimizer_step_amd as ms
+    rng = np.random.default_rng(21)
+    sizes = [1, 5, 4096, 4097, 123457, 300000]
+    p_h = [rng.standard_normal(n).astype(np.float32) for n in sizes]
+    e_h = [rng.standard_normal(n).astype(np.float32) for n in sizes]
+    P = [gu.dev(x) for x in p_h]
+    A = [gu.dev(x) for x in e_h]
+    B = [gu.dev(x) for x in e_h]
+    prepared = ms.PreparedEma(B, P)
+    for decay in (0.9965, 0.5):
+        ms.ema_update(A, P, decay)
+        prepared(decay)
+    torch.cuda.synchronize()
+    for i, (x, y) in enumerate(zip(A, B)):
+        assert _bits_equal(gu.host(x), gu.host(y)), i
+    # and against the oracle, two updates in a row
+    for i, (e0, p0) in enumerate(zip(e_h, p_h)):
+        want = om.ema_update(om.ema_update(e0, p0, gu.f32(0.9965)), p0, gu.f32(0.5))
+        assert gu.rel_max(gu.host(B[i]), want) <= gu.ELEM_TOL, i
